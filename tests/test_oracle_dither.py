@@ -1,0 +1,96 @@
+"""Pins of the oracle's dither generator (counter hash) against what the
+pages and the mathematics fix: xi must be U[-1/2, 1/2) draws, independent
+across channels of a token (Tier B's variance proxy sums d independent
+uniform residuals), regenerated bit-identically at read time."""
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import dither
+
+
+def test_pcg_is_a_bijection_on_a_range():
+    # The RXS-M-XS output permutation is invertible (shift >= 4, odd
+    # multiplier, xorshift), so distinct counters give distinct words.
+    x = np.arange(0, 1 << 20, dtype=np.uint64) * np.uint64(4099) + np.uint64(17)
+    h = dither.pcg(x)
+    assert len(np.unique(h)) == len(h)
+
+
+def test_pcg_scalar_matches_array():
+    xs = [0, 1, 2, 0xFFFFFFFF, 123456789]
+    arr = dither.pcg(np.array(xs, dtype=np.uint64))
+    for x, a in zip(xs, arr):
+        assert dither.pcg(x) == int(a)
+
+
+def test_pcg_hand_evaluation():
+    # One evaluation written out with python big ints, step by step.
+    v = 42
+    state = (v * 747796405 + 2891336453) % 2**32
+    word = (((state >> ((state >> 28) + 4)) ^ state) * 277803737) % 2**32
+    want = ((word >> 22) ^ word) % 2**32
+    assert dither.pcg(v) == want
+
+
+def test_xi_range_and_grid():
+    t = np.arange(512)[:, None]
+    c = np.arange(128)[None, :]
+    for stream in (0, 1):
+        xi = dither.dither_xi(99, 3, 1, stream, t, c).astype(np.float64)
+        assert xi.min() >= -0.5 and xi.max() < 0.5
+        k = (xi + 0.5) * 65536
+        assert np.all(k == np.round(k))
+
+
+def test_deterministic_regeneration():
+    a = dither.dither_rows(7, 2, 3, 0, np.arange(100, 164))
+    b = dither.dither_rows(7, 2, 3, 0, np.arange(100, 164))
+    assert np.array_equal(a, b)
+    c = dither.dither_rows(8, 2, 3, 0, np.arange(100, 164))
+    assert not np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("stream", [0, 1])
+def test_uniformity(stream):
+    t = np.arange(4096)[:, None]
+    c = np.arange(128)[None, :]
+    k = dither.dither_k16(2024, 5, 2, stream, t, c).astype(np.int64).ravel()
+    xi = k / 65536.0 - 0.5
+    ks = stats.kstest(xi + 0.5, "uniform")
+    assert ks.pvalue > 1e-3
+    for bits in (k >> 8, k & 0xFF):          # both bytes of each draw
+        cnt = np.bincount(bits, minlength=256)
+        chi = stats.chisquare(cnt)
+        assert chi.pvalue > 1e-3
+    n = xi.size
+    assert abs(xi.mean()) < 4 * np.sqrt(1 / 12 / n)
+    assert abs(xi.var() - 1 / 12) < 4 * np.sqrt((1 / 80 - 1 / 144) / n)
+
+
+@pytest.mark.parametrize("stream", [0, 1])
+def test_no_correlation_between_neighbours(stream):
+    t = np.arange(2048)[:, None]
+    c = np.arange(128)[None, :]
+    xi = dither.dither_xi(11, 0, 0, stream, t, c).astype(np.float64)
+    n = xi.size
+    lim = 5 / np.sqrt(n)
+    for a, b in [(xi[:, 0::2], xi[:, 1::2]),     # channel pairs (same word for keys)
+                 (xi[:, :-1], xi[:, 1:]),        # adjacent channels
+                 (xi[0::2], xi[1::2]),           # token pairs (same word for values)
+                 (xi[:-1], xi[1:])]:             # adjacent tokens
+        r = np.corrcoef(a.ravel(), b.ravel())[0, 1]
+        assert abs(r) < lim
+    # pairs of draws are jointly uniform on a 16 x 16 grid
+    cells = (np.floor((xi[:, 0::2] + 0.5) * 16) * 16 + np.floor((xi[:, 1::2] + 0.5) * 16)).astype(int)
+    cnt = np.bincount(cells.ravel(), minlength=256)
+    assert stats.chisquare(cnt).pvalue > 1e-3
+
+
+def test_streams_heads_layers_differ():
+    t = np.arange(64)[:, None]
+    c = np.arange(128)[None, :]
+    base = dither.dither_k16(5, 1, 1, 0, t, c)
+    for args in [(5, 1, 1, 1), (5, 1, 2, 0), (5, 2, 1, 0), (6, 1, 1, 0)]:
+        other = dither.dither_k16(*args, t, c)
+        assert np.mean(base == other) < 0.01

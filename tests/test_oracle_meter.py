@@ -1,0 +1,237 @@
+"""Pins of the oracle's meter: Theorem 2 (Tier A), the Tier B certificate,
+the TV aggregation, KV splits with LSE merge, and the budget arithmetic."""
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+from oracle import dither, meter, quant, rope
+from certified_kv_cache_amd import inputs
+
+SM = 1.0 / math.sqrt(128)
+
+
+def _cache(S, seed, d=128, scale=1.0):
+    rng = np.random.default_rng(seed)
+    k = (rng.standard_normal((S, d)) * scale).astype(np.float32)
+    v = rng.standard_normal((S, d)).astype(np.float32)
+    xi_k = dither.dither_rows(seed, 0, 0, 0, np.arange(S))
+    xi_v = dither.dither_rows(seed, 0, 0, 1, np.arange(S))
+    ck, sk, _ = quant.dither_int8(k, xi_k)
+    cv, sv, _ = quant.dither_int8(v, xi_v)
+    khat = quant.dequant_dither_int8(ck, sk, xi_k)
+    vhat = quant.dequant_dither_int8(cv, sv, xi_v)
+    w = quant.witness(k, khat)
+    return k, v, khat, vhat, w, sk
+
+
+# ----------------------------------------------------------------- Tier A
+def test_tier_a_sound_random_queries():
+    k, v, khat, vhat, w, sk = _cache(200, 1)
+    q = np.random.default_rng(2).standard_normal((3000, 128)) * np.random.default_rng(3).uniform(0.1, 10, (3000, 1))
+    eps = np.abs(SM * q @ (khat - k).T)
+    a = meter.tier_a(q, w, SM)
+    assert np.all(eps <= a * (1 + 1e-12))
+
+
+def test_tier_a_equality_case():
+    # Cauchy-Schwarz is tight when q_b is a nonnegative multiple of r_b in
+    # every band: then eps_t = a_t exactly.
+    k, v, khat, vhat, w, sk = _cache(20, 4)
+    r = khat - k
+    dims = rope.band_dims()
+    lam = np.random.default_rng(5).uniform(0.5, 3.0, 8)
+    for t in range(20):
+        q = np.zeros(128)
+        for b in range(8):
+            rb = r[t, dims[b]]
+            q[dims[b]] = lam[b] * rb / np.linalg.norm(rb)
+        eps = abs(SM * q @ r[t])
+        a = meter.tier_a(q[None], w[t:t + 1], SM)[0, 0]
+        assert abs(eps - a) <= 1e-12 * a
+
+
+def test_tier_a_one_band_and_refinement():
+    k, v, khat, vhat, w, sk = _cache(50, 6)
+    r = khat - k
+    q = np.random.default_rng(7).standard_normal((5, 128))
+    w1 = quant.witness(k, khat, num_bands=1)
+    a1 = meter.tier_a(q, w1, SM, num_bands=1)
+    assert np.allclose(a1, SM * np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(r, axis=1)[None], rtol=1e-13)
+    w4 = quant.witness(k, khat, num_bands=4)
+    a4 = meter.tier_a(q, w4, SM, num_bands=4)
+    a8 = meter.tier_a(q, w, SM)
+    assert np.all(a8 <= a4 * (1 + 1e-13)) and np.all(a4 <= a1 * (1 + 1e-13))
+
+
+def test_tier_a_witness_position_invariance_end_to_end():
+    # Theorem 2 with Lemma 1: the bound computed from the stored witness holds
+    # for the residual rotated to any position (RoPE is applied to both q, r).
+    k, v, khat, vhat, w, sk = _cache(30, 8)
+    r = khat - k
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        pos = rng.integers(0, 10 ** 6)
+        q = rng.standard_normal(128)
+        rr = rope.rope_rotate(r, np.full(30, pos))
+        eps = np.abs(SM * rr @ q)
+        assert np.all(eps <= meter.tier_a(q[None], w, SM)[0] * (1 + 1e-12))
+
+
+# ----------------------------------------------------------------- Tier B
+def test_tier_b_variance_proxy_is_exact_variance():
+    # For a fixed (non-adaptive) query the logit error is a sum of independent
+    # uniform residuals, so Var(eps_t) = varsigma_t^2 exactly.  Monte Carlo over
+    # dither seeds; a wrong 1/12, d or scale factor fails this.
+    rng = np.random.default_rng(10)
+    S, R = 8, 1500
+    k = rng.standard_normal((S, 128)).astype(np.float32)
+    q = rng.standard_normal((2, 128))
+    errs = []
+    sk = None
+    for seed in range(R):
+        xi = dither.dither_rows(10_000 + seed, 0, 0, 0, np.arange(S))
+        c, s, _ = quant.dither_int8(k, xi)
+        khat = quant.dequant_dither_int8(c, s, xi)
+        errs.append(SM * q @ (khat - k).T)
+        sk = s
+    errs = np.array(errs)                       # [R, 2, S]
+    var = meter.tier_b_sigma2(q, sk, SM)
+    ratio = errs.var(axis=0) / var
+    # Var estimate of a near-Gaussian: relative SE sqrt(2/R)
+    assert np.all(np.abs(ratio - 1) < 5 * math.sqrt(2 / R))
+    assert np.all(np.abs(errs.mean(0)) < 5 * np.sqrt(var / R))
+
+
+@pytest.mark.parametrize("delta", [0.5, 1e-2])
+def test_tier_b_violation_rate(delta):
+    rng = np.random.default_rng(11)
+    S, R = 64, 1000
+    k = rng.standard_normal((S, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 128))
+    log_term = math.log(2 * S / delta)
+    viol = 0
+    for seed in range(R):
+        xi = dither.dither_rows(50_000 + seed, 0, 0, 0, np.arange(S))
+        c, s, _ = quant.dither_int8(k, xi)
+        khat = quant.dequant_dither_int8(c, s, xi)
+        eps = np.abs(SM * q @ (khat - k).T)
+        u = meter.tier_b(q, s, SM, log_term)
+        viol += bool(np.any(eps > u))
+    rate = viol / R
+    assert rate <= delta + 3 * math.sqrt(delta * (1 - delta) / R)
+
+
+def test_delta_arithmetic():
+    d = meter.delta_loc(1e-2, 28, 28, 256)
+    assert abs(d - 1e-2 / 200704) < 1e-20
+    assert abs(math.log(2 * 4096 / d) - 25.8265) < 1e-3
+    assert abs(math.log(2 * 256 / 1e-2) - math.log(51200)) < 1e-12
+
+
+def test_cells_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "cells.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    req, L, H, T, n = map(int, rows[0])
+    assert meter.cells(req, L, H, T) == n
+
+
+# ----------------------------------------------------------------- TV aggregation
+def _sup_tv_vertices(lt, c):
+    S = len(lt)
+    pt = meter.softmax(lt)
+    best = 0.0
+    for mask in range(1 << S):
+        sgn = np.array([1.0 if (mask >> i) & 1 else -1.0 for i in range(S)])
+        best = max(best, meter.tv(meter.softmax(lt + sgn * c), pt))
+    return best
+
+
+def test_tv_bound_sound_on_vertices_and_interior():
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        S = rng.integers(1, 9)
+        lt = rng.standard_normal(S) * rng.uniform(0.1, 4)
+        c = rng.uniform(0, 1.5, S) * (rng.uniform() < 0.8)
+        pt = meter.softmax(lt)
+        _, R, bound = meter.meter_from(pt, c)
+        assert _sup_tv_vertices(lt, c) <= bound + 1e-12
+        for _ in range(20):
+            dl = rng.uniform(-1, 1, S) * c
+            assert meter.tv(meter.softmax(lt + dl), pt) <= bound + 1e-12
+
+
+def test_tv_bound_closed_forms():
+    pt = meter.softmax(np.random.default_rng(13).standard_normal(10))
+    assert meter.meter_from(pt, np.zeros(10))[1] == 0.0
+    c = 0.3
+    E, R, _ = meter.meter_from(pt, np.full(10, c))
+    assert abs(R - (math.exp(2 * c) - 1) / 2) < 1e-14
+    assert abs(E - math.expm1(c)) < 1e-15
+    # S = 1: the softmax is 1 whatever the logit error, TV = 0
+    assert meter.tv(meter.softmax(np.array([3.0])), meter.softmax(np.array([-7.0]))) == 0.0
+
+
+def test_tv_bound_mpmath_agreement():
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(14)
+    for _ in range(20):
+        lt = rng.standard_normal(6)
+        c = rng.uniform(0, 0.2, 6)
+        pt = meter.softmax(lt)
+        _, R, _ = meter.meter_from(pt, c)
+        Z = sum(mpmath.e ** mpmath.mpf(x) for x in lt)
+        A = sum(mpmath.e ** mpmath.mpf(x) / Z * mpmath.e ** mpmath.mpf(cc) for x, cc in zip(lt, c))
+        Rm = (A * A - 1) / 2
+        assert abs(float(Rm) - R) <= 1e-12 * float(Rm)
+
+
+def test_meter_sound_against_true_tv_on_quantized_cache():
+    k, v, khat, vhat, w, sk = _cache(256, 15)
+    q = np.random.default_rng(16).standard_normal((4, 128))
+    out = meter.decode_group(q, k, khat, v, vhat, w, SM, k_scale=sk, log_term=math.log(2 * 256 / 1e-2))
+    assert np.all(out["tv_true"] <= np.minimum(1, out["R_A"]))
+    assert np.all(out["eps"] <= out["a"] * (1 + 1e-12))
+    assert np.allclose(out["block_risk"].sum(-1), out["E_B"], rtol=1e-12)
+
+
+# ----------------------------------------------------------------- attention + splits
+def test_zero_residual_attention_equals_sdpa():
+    rng = np.random.default_rng(17)
+    k = rng.standard_normal((77, 128))
+    v = rng.standard_normal((77, 128))
+    q = rng.standard_normal((7, 128))
+    out = meter.decode_group(q, k, k, v, v, np.zeros((77, 8)), SM)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None, None].expand(1, 7, 77, 128),
+        torch.from_numpy(v)[None, None].expand(1, 7, 77, 128))[0, :, 0].numpy()
+    assert np.allclose(out["o_tilde"], ref, rtol=1e-12, atol=1e-14)
+    assert np.all(out["R_A"] == 0) and np.all(out["tv_true"] < 1e-15)
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 3, 16, 22, 40])
+def test_split_merge_invariance(n_split):
+    S = 341                                     # ragged: 22 pages, last holds 5 tokens
+    k, v, khat, vhat, w, sk = _cache(S, 18)
+    q = np.random.default_rng(19).standard_normal((7, 128))
+    lt = math.log(2 * S / 1e-6)
+    ref = meter.decode_group(q, k, khat, v, vhat, w, SM, k_scale=sk, log_term=lt)
+    parts = meter.split_partials(q, khat, vhat, ref["a"], ref["u"], SM, n_split)
+    m = meter.lse_merge(parts)
+    assert np.allclose(m["o"], ref["o_tilde"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(m["lse"], ref["lse"], rtol=1e-13)
+    assert np.allclose(m["R_A"], ref["R_A"], rtol=1e-12)
+    assert np.allclose(m["R_B"], ref["R_B"], rtol=1e-12)
+
+
+def test_repaired_tokens_carry_no_bound_and_full_repair_is_exact():
+    k, v, khat, vhat, w, sk = _cache(64, 20)
+    q = np.random.default_rng(21).standard_normal((7, 128))
+    rep = np.ones(64, dtype=bool)
+    out = meter.decode_group(q, k, khat, v, v, w, SM, k_scale=sk, log_term=10.0, repaired=rep)
+    assert np.all(out["R_A"] == 0) and np.all(out["R_B"] == 0)
+    assert np.allclose(out["o_tilde"], out["o_exact"], rtol=1e-13, atol=1e-15)
+    assert np.all(out["tv_true"] < 1e-15)

@@ -1,0 +1,162 @@
+"""Pins of the oracle's write path: dithered INT8, fp8 e4m3fn, 2-bit grouped,
+and the band-norm witness (Lemma 1)."""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+from oracle import dither, quant, rope
+from certified_kv_cache_amd import inputs
+
+
+def _rows(n, d=128, seed=0, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal((n, d)) * scale).astype(np.float32)
+
+
+def test_dither_error_bounded_by_half_step():
+    # Subtractive dither: x^ - x = s (round(y + xi) - (y + xi)) with y = x/s,
+    # so |x^ - x| <= s/2 up to the float32 rounding of y.
+    x = _rows(2000)
+    xi = dither.dither_rows(3, 0, 0, 0, np.arange(2000))
+    code, s, inv = quant.dither_int8(x, xi)
+    xhat = quant.dequant_dither_int8(code, s, xi)
+    err = np.abs(xhat - x)
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+
+
+def test_dither_residual_is_uniform_and_independent_of_input():
+    # Classical subtractive-dither theory: e = (x^ - x)/s ~ U[-1/2, 1/2],
+    # independent of x.  Tier B's proxy varsigma^2 uses its variance 1/12.
+    x = _rows(4000, seed=1)
+    xi = dither.dither_rows(4, 0, 0, 0, np.arange(4000))
+    code, s, _ = quant.dither_int8(x, xi)
+    e = ((quant.dequant_dither_int8(code, s, xi) - x) / s[:, None]).ravel()
+    n = e.size
+    assert abs(e.mean()) < 4 * np.sqrt(1 / 12 / n)
+    assert abs(e.var() - 1 / 12) < 4 * np.sqrt((1 / 80 - 1 / 144) / n)
+    assert stats.kstest(e + 0.5, "uniform").pvalue > 1e-3
+    assert abs(np.corrcoef(e, x.ravel())[0, 1]) < 5 / np.sqrt(n)
+
+
+def test_zero_dither_is_round_to_nearest():
+    x = _rows(300, seed=2)
+    code, s, inv = quant.dither_int8(x, np.zeros_like(x))
+    ref = np.clip(np.rint(x.astype(np.float64) * inv[:, None].astype(np.float64)), -128, 127)
+    # float32 product vs exact product can differ only at exact .5 boundaries
+    assert np.mean(code == ref) > 0.9999
+
+
+def test_scale_definition_and_zero_row():
+    x = _rows(8, seed=3)
+    x[2] = 0.0
+    xi = dither.dither_rows(1, 0, 0, 0, np.arange(8))
+    code, s, inv = quant.dither_int8(x, xi)
+    am = np.max(np.abs(x), axis=1)
+    assert np.all(s[am > 0] == (am[am > 0] / np.float32(127)).astype(np.float32))
+    assert s[2] == 0 and np.all(code[2] == 0)
+    assert np.all(np.abs(code.astype(int)) <= 128)
+
+
+def test_code_minus_xi_exact_in_float32():
+    code = np.arange(-128, 128, dtype=np.float64)[:, None]
+    k = np.array([0, 1, 32767, 32768, 65535], dtype=np.float64)[None, :]
+    xi = k / 65536 - 0.5
+    exact = code - xi
+    assert np.all(exact.astype(np.float32).astype(np.float64) == exact)
+
+
+def test_fp8_matches_torch_cast_in_range():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 10, rng.standard_normal(2000) * 1e-3,
+                        np.linspace(-447.9, 447.9, 5001)]).astype(np.float32)
+    code, val = quant.fp8_e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    assert np.array_equal(code, ref.view(torch.uint8).numpy())
+    assert np.array_equal(val, ref.to(torch.float64).numpy())
+
+
+def test_fp8_saturates_and_decodes():
+    code, val = quant.fp8_e4m3(np.array([448.0, 449.0, 1e6, -1e6, 0.0, -0.0, 2.0 ** -10]))
+    assert list(val[:4]) == [448.0, 448.0, 448.0, -448.0]
+    assert code[0] == 0x7E and code[3] == 0xFE
+    assert val[6] == 0.0       # 2**-10 is a tie between 0 and 2**-9 -> even (0)
+    every = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    v = quant.fp8_e4m3_decode(every)
+    c2, v2 = quant.fp8_e4m3(v)
+    assert np.array_equal(v2, v)
+    nz = v != 0
+    assert np.array_equal(c2[nz], every[nz])
+
+
+def test_two_bit_codes_are_nearest_level():
+    rng = np.random.default_rng(6)
+    g = (rng.standard_normal((500, 32)) * rng.uniform(0.1, 3, (500, 1))).astype(np.float32)
+    code, scale, mn, xhat = quant.quant2_groups(g)
+    levels = mn[:, None].astype(np.float64) + np.arange(4)[None, :] * scale[:, None].astype(np.float64)
+    dist = np.abs(g[..., None].astype(np.float64) - levels[:, None, :])
+    best = np.argmin(dist, axis=-1)
+    sorted_d = np.sort(dist, axis=-1)
+    tie = (sorted_d[..., 1] - sorted_d[..., 0]) < 1e-5 * scale[:, None]
+    assert np.all((best == code) | tie)
+    assert np.all(code <= 3)
+    assert np.all(np.abs(xhat - g) <= scale[:, None] * (0.5 + 1e-5))
+
+
+def test_two_bit_constant_group():
+    g = np.full((1, 32), 1.25, dtype=np.float32)
+    code, scale, mn, xhat = quant.quant2_groups(g)
+    assert scale[0] == 0 and np.all(code == 0) and np.all(xhat == g)
+
+
+def test_kivi_group_axes():
+    k = _rows(64, seed=7)
+    code, scale, mn, xhat = quant.kivi2_keys(k)
+    assert scale.shape == (2, 128)
+    assert np.all(mn[0] == k[:32].min(axis=0)) and np.all(mn[1] == k[32:].min(axis=0))
+    v = _rows(3, seed=8)
+    code, scale, mn, xhat = quant.kivi2_values(v)
+    assert scale.shape == (3, 4)
+    assert np.all(mn[:, 1] == v[:, 32:64].min(axis=1))
+
+
+def test_witness_lemma1_rope_invariance():
+    # Lemma 1: RoPE acts unitarily within a frequency band, so band norms of
+    # a residual do not depend on the position it is rotated to.
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((64, 128))
+    pos = rng.integers(0, 10 ** 6, size=64)
+    w0 = quant.witness(np.zeros_like(r), r)
+    w1 = quant.witness(np.zeros_like(r), rope.rope_rotate(r, pos))
+    assert np.max(np.abs(w1 - w0) / w0) < 1e-12
+    # the synthesis module's independent RoPE agrees
+    w2 = quant.witness(np.zeros_like(r), inputs.apply_rope_np(r[None], pos)[0])
+    assert np.max(np.abs(w2 - w0) / w0) < 1e-12
+
+
+def test_witness_lemma1_discriminates_wrong_bands():
+    # Contiguous-dimension bands are not RoPE-invariant under rotate-half
+    # pairing: the test above would catch that band definition.
+    rng = np.random.default_rng(10)
+    r = rng.standard_normal((64, 128))
+    r2 = rope.rope_rotate(r, rng.integers(1, 10 ** 6, size=64))
+    wrong0 = np.sqrt((r.reshape(64, 8, 16) ** 2).sum(-1))
+    wrong1 = np.sqrt((r2.reshape(64, 8, 16) ** 2).sum(-1))
+    assert np.max(np.abs(wrong1 - wrong0) / wrong0) > 0.05
+
+
+def test_witness_bands_partition_and_total_norm():
+    dims = rope.band_dims(128, 8)
+    assert sorted(dims.ravel().tolist()) == list(range(128))
+    r = np.random.default_rng(11).standard_normal((10, 128))
+    w = quant.witness(np.zeros_like(r), r)
+    assert np.allclose(np.sqrt((w ** 2).sum(1)), np.linalg.norm(r, axis=1), rtol=1e-14)
+
+
+def test_witness_size_golden():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "witness_size.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    bands, per, total = map(int, rows[0])
+    w = quant.witness(np.zeros((3, 128)), np.ones((3, 128)))
+    assert w.shape[1] == bands and np.dtype(np.float32).itemsize == per
+    assert w.shape[1] * np.dtype(np.float32).itemsize == total
