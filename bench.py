@@ -1,0 +1,236 @@
+"""Benchmark of the WitCert hot path on one MI355X.
+
+Workload (the headline configuration): decode batch 32, 32768 cached tokens
+per sequence, Qwen2.5-7B attention shape (28 query / 4 KV heads, d = 128),
+dithered INT8 cache paged at 16 tokens with a random page permutation,
+16 KV splits, Tier A + Tier B meter (delta_req 1e-2 over L = 28, H = 28,
+T = 256).  Inputs are synthetic and seeded (bf16 N(0,1), RoPE on K).
+
+One step = append one token per sequence (wc_write_kv), fused decode +
+meter with block risks (wc_decode_attn_meter), LSE merge (wc_lse_merge) and
+the gate at tau = 0.2 (wc_gate_pagein).  The cache is resident in HBM before
+the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HQ, HKV, D, NSPLIT = 28, 4, 128, 16
+DELTA = (1e-2, 28, 28, 256)
+TAU = 0.2
+PEAK_GBS = 8000.0
+METRIC = "fused INT8 decode attn+meter: achieved HBM GB/s (% peak), overhead vs no meter"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_int8_b32_s32k_counters.json")
+
+
+def decode_source_sha():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "wc_common.h"):
+        h.update(open(os.path.join(ROOT, "certified_kv_cache_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(B, S, meter):
+    """Algorithmic HBM bytes of one decode launch: cache, page table, query."""
+    per_tok = 128 + 128 + 4 + 4 + (32 if meter else 0)   # K, V codes, K, V scales, witness
+    P = -(-S // 16)
+    return B * S * HKV * per_tok + B * P * 4 + B * HQ * D * 2 + B * 4 + B * 8
+
+
+def step_bytes(B, S):
+    """Algorithmic bytes of one whole step (decode + append + merge + gate)."""
+    P = -(-S // 16)
+    write = B * HKV * (2 * D * 2 + 2 * D + 2 * 4 + 32) + B * (8 + 4 + 8)
+    merge_out = B * HQ * (D * 4 + 3 * 4)
+    risk = 2 * B * HQ * P * 4                         # block risks written by decode, read by the gate
+    return decode_bytes(B, S, True) + write + merge_out + risk
+
+
+def setup(B, S, seed=3):
+    import numpy as np
+    import torch
+
+    from certified_kv_cache_amd import _lib as L
+    from certified_kv_cache_amd import inputs
+
+    k, v = inputs.decode_kv_torch(seed, B, S, Hkv=HKV)
+    q = inputs.query_torch(seed, B, Hq=HQ)
+    ctx = np.full(B, S)
+    tab, npages = inputs.page_table(seed, ctx)
+    seeds = inputs.seeds(B, base=1000 + seed)
+    cache = L.KVCache(L.WC_DITHER_INT8, 1, npages, HKV, pool_capacity=4096)
+    dev = torch.device("cuda")
+    tab_d = torch.from_numpy(tab).to(dev)
+    t = torch.arange(S, device=dev)
+    slot = (tab_d[:, t // 16].long() * 16 + (t % 16)[None]).reshape(-1)
+    pos = t.int().repeat(B)
+    sd = torch.from_numpy(seeds.view(np.int64)).to(dev)
+    L.wc_write_kv(cache, k, v, slot, pos, sd.repeat_interleave(S))
+    last = torch.arange(B, device=dev) * S + (S - 1)
+    new = dict(k=k[last].contiguous(), v=v[last].contiguous(), slot=slot[last].contiguous(),
+               pos=pos[last].contiguous(), seed=sd.clone())
+    # exact backing store in pinned host memory, paged like the cache
+    store = torch.empty((1, npages, HKV, 16, D), dtype=torch.bfloat16, device=dev)
+    store[0, slot // 16, :, slot % 16, :] = k
+    host = torch.empty(store.shape, dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(store)
+    del store
+    torch.cuda.synchronize()
+    return dict(L=L, cache=cache, k=k, v=v, q=q, tab=tab_d, ctx=torch.full((B,), S, dtype=torch.int32, device=dev),
+                seed=sd, new=new, host=host, npages=npages, tab_np=tab, seeds=seeds)
+
+
+def make_step(w, B, S):
+    import torch
+    L = w["L"]
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    o = torch.empty((B, HQ, D), device="cuda")
+    lse = torch.empty((B, HQ), device="cuda")
+    ra = torch.empty((B, HQ), device="cuda")
+    rb = torch.empty((B, HQ), device="cuda")
+    gws = torch.empty(L.wc_gate_workspace_bytes(B, HKV, mp), dtype=torch.uint8, device="cuda")
+    pool_used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    paged = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sm = 1.0 / math.sqrt(D)
+    n = w["new"]
+
+    def decode(mask=3, with_risk=True):
+        L.wc_decode_attn_meter(w["cache"], 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    def step(ev=None):
+        L.wc_write_kv(w["cache"], n["k"], n["v"], n["slot"], n["pos"], n["seed"])
+        if ev is not None:
+            ev[0].record()
+        decode()
+        if ev is not None:
+            ev[1].record()
+        L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb)
+        L.wc_gate_pagein(w["cache"], 0, risk, lse, w["tab"], w["ctx"], TAU, w["host"], pool_used, paged, gws)
+
+    return step, decode, dict(o=o, lse=lse, ra=ra, rb=rb, paged=paged)
+
+
+def time_decode(decode, iters, **kw):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        decode(**kw)
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / iters * 1e3     # microseconds
+
+
+def cpu_baseline(w, B, S, pairs=6):
+    """The float64 oracle's read path (dither regeneration, dequantization,
+    attention, Tier A/B, TV meter) on `pairs` (sequence, KV head) pairs of the
+    same workload, one thread, scaled to GB/s of the same algorithmic bytes."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dither, meter, quant
+    sm = 1.0 / math.sqrt(D)
+    lt = math.log(2 * S / meter.delta_loc(*DELTA))
+    rng = np.random.default_rng(0)
+    picks = [(int(rng.integers(B)), int(g)) for g in rng.integers(0, HKV, pairs)]
+    total = 0.0
+    with threadpool_limits(limits=1):
+        for b, g in picks:
+            k32 = w["k"][b * S:(b + 1) * S, g].float().cpu().numpy()
+            v32 = w["v"][b * S:(b + 1) * S, g].float().cpu().numpy()
+            q = w["q"][b, g * 7:(g + 1) * 7].float().cpu().numpy().astype(np.float64)
+            seed = int(w["seeds"][b])
+            pos = np.arange(S)
+            ck, sk, _ = quant.dither_int8(k32, dither.dither_rows(seed, 0, g, 0, pos))
+            cv, sv, _ = quant.dither_int8(v32, dither.dither_rows(seed, 0, g, 1, pos))
+            wt = quant.witness(k32, quant.dequant_dither_int8(ck, sk, dither.dither_rows(seed, 0, g, 0, pos)))
+            t0 = time.perf_counter()
+            xk = dither.dither_rows(seed, 0, g, 0, pos)
+            xv = dither.dither_rows(seed, 0, g, 1, pos)
+            khat = quant.dequant_dither_int8(ck, sk, xk)
+            vhat = quant.dequant_dither_int8(cv, sv, xv)
+            meter.decode_group(q, k32, khat, v32, vhat, wt, sm, k_scale=sk, log_term=lt)
+            total += time.perf_counter() - t0
+    sample_bytes = pairs * decode_bytes(B, S, True) / (B * HKV)
+    return dict(value=round(sample_bytes / total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{pairs} of {B * HKV} (sequence, KV head) pairs, all {S} tokens, "
+                       f"{total:.1f} s single-threaded float64 numpy")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--ctx", type=int, default=32768)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU; the path shards without communication "
+              "(see the design notes), so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    B, S = args.batch, args.ctx
+    w = setup(B, S)
+    step, decode, outs = make_step(w, B, S)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    dec_step_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+    # meter overhead: the same kernel with the meter disabled
+    iters = max(args.steps, 10)
+    t_on = time_decode(decode, iters, mask=3, with_risk=False)
+    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    t_on2 = time_decode(decode, iters, mask=3, with_risk=False)
+    t_on = min(t_on, t_on2)
+    bytes_on = decode_bytes(B, S, True)
+    ach = bytes_on / (dec_step_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        cnt = json.load(open(COUNTERS))
+        if cnt.get("source_sha") == decode_source_sha() and cnt.get("batch") == B and cnt.get("ctx") == S:
+            traffic = cnt.get("hbm_bytes_per_launch")
+    value = step_bytes(B, S) / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"decode B={B} S={S} Hq={HQ} Hkv={HKV} d={D} dithered-int8 Tier A+B, "
+                               f"{NSPLIT} KV splits, 16-token pages (random permutation), append+decode+merge+gate",
+                   "batch": B, "ctx": S, "n_split": NSPLIT, "tau": TAU},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_GBS, 4), "traffic": traffic},
+        "decode_us": round(dec_step_us, 2), "decode_meter_on_us": round(t_on, 2),
+        "decode_meter_off_us": round(t_off, 2), "meter_overhead": round(t_on / t_off - 1, 4),
+        "pct_peak": round(100 * ach / PEAK_GBS, 2),
+        "kv_tokens_per_s": round(B * S / (dec_step_us * 1e-6), 1),
+        "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),
+        "pages_paged_in": int(outs["paged"].item()) // 4096,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, B, S)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

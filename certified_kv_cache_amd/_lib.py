@@ -1,0 +1,191 @@
+"""ctypes binding of libwitcert.so: argument marshalling only.
+
+Every step of the hot path runs in the HIP library; this module turns torch
+tensors into pointers and streams and raises on error codes.  It never falls
+back to anything: if the library is missing, importing fails loudly.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwitcert.so")
+
+WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
+WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2 = 0, 1, 2
+WC_F32, WC_BF16 = 0, 1
+WC_METER_A, WC_METER_B = 1, 2
+PARTIAL = 132
+
+_c_void_p = ctypes.c_void_p
+_i32, _i64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+
+
+class WcCache(ctypes.Structure):
+    _fields_ = [("scheme", _i32), ("head_dim", _i32), ("num_kv_heads", _i32), ("num_bands", _i32),
+                ("page_size", _i32), ("num_layers", _i32), ("num_pages", _i64),
+                ("k_codes", _c_void_p), ("v_codes", _c_void_p), ("k_scale", _c_void_p),
+                ("v_scale", _c_void_p), ("k_aux", _c_void_p), ("v_aux", _c_void_p),
+                ("witness", _c_void_p), ("exact_slot", _c_void_p), ("exact_pool", _c_void_p),
+                ("exact_scale", _c_void_p), ("pool_capacity", _i64)]
+
+
+class WitcertError(RuntimeError):
+    def __init__(self, fn, code, text):
+        super().__init__(f"{fn} returned {code}: {text}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m certified_kv_cache_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = _c_void_p
+    sig = {
+        "wc_write_kv": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, P, P, P],
+        "wc_decode_attn_meter": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
+                                 P, P, ctypes.c_float, ctypes.c_uint, ctypes.c_double, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P, P],
+        "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P],
+        "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
+                           ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
+        "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.wc_decode_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    lib.wc_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.wc_gate_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    lib.wc_gate_workspace_bytes.restype = ctypes.c_size_t
+    lib.wc_last_error.restype = ctypes.c_char_p
+    lib.wc_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
+           "wc_gate_pagein", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_last_error", "wc_version"]
+
+
+def _check(fn, code):
+    if code != WC_OK:
+        raise WitcertError(fn, code, lib.wc_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return WC_F32
+    if t.dtype == torch.bfloat16:
+        return WC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- cache allocation
+class KVCache:
+    """Device tensors of one paged cache (all layers) plus its C descriptor."""
+
+    def __init__(self, scheme, num_layers, num_pages, num_kv_heads, device="cuda", pool_capacity=0,
+                 page_size=None):
+        self.scheme = scheme
+        self.L, self.P, self.H = num_layers, num_pages, num_kv_heads
+        ps = page_size or (32 if scheme == WC_KIVI2 else 16)
+        self.page_size = ps
+        u8 = dict(dtype=torch.uint8, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        shp = (num_layers, num_pages, num_kv_heads)
+        if scheme == WC_KIVI2:
+            self.k_codes = torch.zeros(shp + (128, 8), **u8)
+            self.v_codes = torch.zeros(shp + (32, 32), **u8)
+            self.k_aux = torch.zeros(shp + (128, 2), **f32)
+            self.v_aux = torch.zeros(shp + (32, 4, 2), **f32)
+            self.k_scale = self.v_scale = None
+        else:
+            self.k_codes = torch.zeros(shp + (16, 128), **u8)
+            self.v_codes = torch.zeros(shp + (4, 128, 4), **u8)
+            self.k_aux = self.v_aux = None
+            if scheme == WC_DITHER_INT8:
+                self.k_scale = torch.zeros(shp + (16,), **f32)
+                self.v_scale = torch.zeros(shp + (16,), **f32)
+            else:
+                self.k_scale = self.v_scale = None
+        self.witness = torch.zeros(shp + (ps, 8), **f32)
+        self.pool_capacity = pool_capacity
+        if pool_capacity > 0:
+            self.exact_slot = torch.full(shp, -1, dtype=torch.int32, device=device)
+            self.exact_pool = torch.zeros((pool_capacity, 16, 128), dtype=torch.float16, device=device)
+            self.exact_scale = torch.zeros((pool_capacity, 16), **f32)
+        else:
+            self.exact_slot = self.exact_pool = self.exact_scale = None
+        self.desc = WcCache(scheme, 128, num_kv_heads, 8, ps, num_layers, num_pages,
+                            *[t.data_ptr() if t is not None else None for t in
+                              (self.k_codes, self.v_codes, self.k_scale, self.v_scale, self.k_aux,
+                               self.v_aux, self.witness, self.exact_slot, self.exact_pool, self.exact_scale)],
+                            pool_capacity)
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+# ---------------------------------------------------------------- entry points
+def wc_write_kv(cache, k, v, slot, pos, seed, layer0=0, stream=None):
+    """k, v: [n_layers, n_tok, Hkv, 128] or [n_tok, Hkv, 128] (bf16 or fp32, contiguous)."""
+    if k.dim() == 3:
+        k, v = k[None], v[None]
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+    n_layers, n_tok = k.shape[0], k.shape[1]
+    _check("wc_write_kv", lib.wc_write_kv(cache.ref(), layer0, n_layers, _ptr(k), _ptr(v), _dtype_code(k), n_tok,
+                                          n_tok * k.shape[2] * k.shape[3], _ptr(slot), _ptr(pos), _ptr(seed),
+                                          _stream(stream)))
+
+
+def wc_decode_workspace_bytes(B, Hq, n_split):
+    return lib.wc_decode_workspace_bytes(B, Hq, n_split)
+
+
+def wc_decode_attn_meter(cache, layer, q, page_table, ctx_len, seed, partials, sm_scale, meter_mask,
+                         delta_req, L, H, T, n_split, block_logrisk=None, stream=None):
+    assert q.is_contiguous() and page_table.is_contiguous()
+    B, Hq = q.shape[0], q.shape[1]
+    _check("wc_decode_attn_meter", lib.wc_decode_attn_meter(
+        cache.ref(), layer, _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[1],
+        _ptr(ctx_len), _ptr(seed), float(sm_scale), int(meter_mask), float(delta_req), L, H, T, n_split,
+        _ptr(partials), partials.numel() * partials.element_size(), _ptr(block_logrisk), _stream(stream)))
+
+
+def wc_lse_merge(partials, B, Hq, n_split, o, lse, meter_a=None, meter_b=None, stream=None):
+    _check("wc_lse_merge", lib.wc_lse_merge(_ptr(partials), B, Hq, n_split, _ptr(o), _ptr(lse), _ptr(meter_a),
+                                            _ptr(meter_b), _stream(stream)))
+
+
+def wc_gate_workspace_bytes(B, Hkv, max_pages):
+    return lib.wc_gate_workspace_bytes(B, Hkv, max_pages)
+
+
+def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, host_exact_k, pool_used,
+                   bytes_paged, workspace, budget_blocks=-1, selected=None, rho_fx=None, stream=None):
+    B, Hq, max_pages = block_logrisk.shape
+    _check("wc_gate_pagein", lib.wc_gate_pagein(
+        cache.ref(), layer, _ptr(block_logrisk), _ptr(lse), B, Hq, _ptr(page_table), max_pages, _ptr(ctx_len),
+        float(tau), int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged), _ptr(selected),
+        _ptr(rho_fx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def wc_dither_fill(seed, layer, kv_head, stream_kv, pos0, n_pos, out, stream=None):
+    _check("wc_dither_fill", lib.wc_dither_fill(int(seed), layer, kv_head, stream_kv, pos0, n_pos, _ptr(out),
+                                                _stream(stream)))

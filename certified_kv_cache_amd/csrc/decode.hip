@@ -1,0 +1,611 @@
+// Fused split-KV decode attention + WitCert meter, and the LSE merge.
+//
+// WitCert summary: Theorem 2 (Tier A) eps_t <= (1/sqrt d) sum_b ||q_b|| w_{t,b};
+// Tier B paragraph: u_t = sqrt(2 varsigma_t^2 log(2S/delta_loc)),
+// varsigma_t^2 = (1/d) sum_c q_c^2 s_{c,t}^2 / 12, delta_loc = delta_req/(L H T);
+// improvements list: TV <= min(1, (A^2 - 1)/2), A = sum_t p~_t e^{c_t};
+// implementation paragraph and the paperswithlean Figure 2 caption: output and
+// meter in one data pass, LSE-merged across KV splits.
+//
+// Work decomposition: one workgroup of 4 waves per (sequence b, KV head g,
+// split); the waves take the split's 16-token pages round robin and combine
+// through LDS at the end.  Inside a wave, lane l is (n = l % 16, k = l / 16):
+//
+//   QK   S^T[token][head] = Khat[token][:] . Q'[head][:]   (MFMA 16x16x32 f16)
+//        A = key codes of token n, channels 32k..32k+31 (one 32 B load);
+//        B = the scaled query of head n, same channels.  The dequantized key
+//        is s_t (code - xi) with xi = h 2^-8 + l 2^-16 (h in [-128,127],
+//        l in [0,255] the two bytes of the 16-bit draw): three MFMAs on exact
+//        fp16 integers (code, h, l) against one fp16 query, so the products
+//        are exact and only the fp32 accumulation rounds.
+//   D    lane (n, k) holds tokens 4k..4k+3 of head n: softmax, both meter
+//        tiers and the block risk stay lane-local up to 4-lane reductions.
+//   PV   O^T[channel][head] += Vhat^T[channel][token] . P^T[token][head]
+//        (MFMA 16x16x16 f16, 8 channel tiles); B = P^T is exactly the D layout
+//        above (lane (n, k): tokens 4k..4k+3 of head n), so no shuffles; A = the
+//        value codes of channel 8n + tile, tokens 4k..4k+3, one 32-bit word of
+//        the value page layout.  Lane (n, k) ends with channels 32k..32k+31 of
+//        head n.
+//   Tier A  a^T[token][head] = W[token][band] . beta[head][band] as one MFMA
+//        16x16x32 with hi/lo fp16 splits (w_hi b_hi + w_lo b_hi + w_hi b_lo).
+#include <math.h>
+
+#include "wc_common.h"
+
+namespace wc {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNW = 4;            // waves per workgroup
+constexpr int kPartial = 132;     // floats per (b, h, split) partial
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// fp16 bit pattern 0x64XX is 1024 + XX exactly.
+constexpr uint32_t kMagic = 0x64646464u;
+
+// Four int8 codes (two's complement, one word) -> two fp16 pairs of the exact
+// integers: bias to unsigned, splice under the 1024 exponent, subtract 1152.
+__device__ __forceinline__ void codes_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = as_u32(as_h2(perm(kMagic, u, 0x04010400u)) - bias);
+  hi = as_u32(as_h2(perm(kMagic, u, 0x04030402u)) - bias);
+}
+
+// One hash word (two 16-bit draws k0 = low half, k1 = high half) -> fp16 pair
+// of the high bytes minus 128 (h) and of the low bytes (l): k - 32768 = 256 h + l.
+__device__ __forceinline__ void draw_to_h(uint32_t w, uint32_t& hh, uint32_t& ll) {
+  const h2 b1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const h2 b1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  hh = as_u32(as_h2(perm(kMagic, w, 0x04030401u)) - b1152);
+  ll = as_u32(as_h2(perm(kMagic, w, 0x04020400u)) - b1024);
+}
+
+// Two e4m3fn bytes (byte 0 and 1 of v after the caller's permute) -> fp16
+// pair of the exact values: (magnitude << 7 | sign << 8) times 2^8.
+__device__ __forceinline__ uint32_t fp8x2_to_h(uint32_t b01) {
+  // b01 holds the two bytes in bits 8..15 and 24..31
+  const uint32_t mag = (b01 >> 1) & 0x3F803F80u;
+  const uint32_t sgn = b01 & 0x80008000u;
+  const h2 k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return as_u32(as_h2(mag | sgn) * k256);
+}
+__device__ __forceinline__ void fp8_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = fp8x2_to_h(perm(0u, w, 0x010C000Cu));  // bytes: 0, w0, 0, w1
+  hi = fp8x2_to_h(perm(0u, w, 0x030C020Cu));  // bytes: 0, w2, 0, w3
+}
+
+__device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8, u);
+}
+__device__ __forceinline__ h4 make_h4(uint32_t a, uint32_t b) {
+  uint2 u = make_uint2(a, b);
+  return __builtin_bit_cast(h4, u);
+}
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// expm1 accurate to a few ulp relative on [0, 88]; +inf above (saturated bound).
+__device__ __forceinline__ float expm1_pos(float c) {
+  if (c < 0.03125f) {
+    float c2 = c * c;
+    return fmaf(c2, fmaf(c, fmaf(c, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), c);
+  }
+  return expm1f(c);
+}
+
+struct DecodeArgs {
+  const void* q;
+  const int32_t* page_table;
+  const int32_t* ctx_len;
+  const uint64_t* seed;
+  float* partials;
+  float* block_logrisk;
+  int B, Hq, G, max_pages, n_split, layer;
+  unsigned mask;
+  float sm_scale;
+  float neg_log_dloc;   // -log(delta_loc)
+};
+
+template <int SCHEME, bool QF32>
+__global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int G = a.G;
+  const int hkv = c.num_kv_heads;
+  const int h = g * G + n;                     // query head of lane column n
+  const bool hv = n < G;
+  const int S = a.ctx_len[b];
+  const int P = (S + 15) >> 4;
+  const int p0 = (int)((int64_t)split * P / a.n_split), p1 = (int)((int64_t)(split + 1) * P / a.n_split);
+  const bool meterA = (a.mask & WC_METER_A) != 0;
+  const bool meterB = SCHEME == WC_DITHER_INT8 && (a.mask & WC_METER_B) != 0;
+  const bool risk = a.block_logrisk != nullptr;
+  const bool gateB = meterB;
+
+  // ---------------------------------------------------------------- query prep
+  float qf[32];
+  if (hv) {
+    if (QF32) {
+      const float* qp = reinterpret_cast<const float*>(a.q) + ((int64_t)b * a.Hq + h) * 128 + 32 * kq;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        float4 v = *reinterpret_cast<const float4*>(qp + i);
+        qf[i] = v.x; qf[i + 1] = v.y; qf[i + 2] = v.z; qf[i + 3] = v.w;
+      }
+    } else {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h) * 128 + 32 * kq;
+#pragma unroll
+      for (int i = 0; i < 32; i += 8) {
+        uint4 v = *reinterpret_cast<const uint4*>(qp + i);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[i + 2 * e] = __uint_as_float(w[e] << 16);
+          qf[i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
+  }
+  float qmax = 0.0f, bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    qmax = fmaxf(qmax, fabsf(qf[i]));
+    bsum[i >> 3] = fmaf(qf[i], qf[i], bsum[i >> 3]);
+  }
+  qmax = fmaxf(qmax, shfl_xor(qmax, 16));
+  qmax = fmaxf(qmax, shfl_xor(qmax, 32));
+  int qe = 0;
+  if (qmax > 0.0f) {
+    int ex;
+    frexpf(qmax, &ex);                        // qmax in [2^(ex-1), 2^ex)
+    qe = 15 - ex;                              // scaled max in [2^14, 2^15)
+  }
+  h8 Qhi[4], Qlo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = ldexpf(qf[8 * j + 2 * e], qe), x1 = ldexpf(qf[8 * j + 2 * e + 1], qe);
+      _Float16 a0 = (_Float16)x0, a1 = (_Float16)x1;
+      h2 hv2 = {a0, a1};
+      hw[e] = as_u32(hv2);
+      if (QF32) {
+        h2 lv2 = {(_Float16)(x0 - (float)a0), (_Float16)(x1 - (float)a1)};
+        lw[e] = as_u32(lv2);
+      }
+    }
+    Qhi[j] = make_h8(hw[0], hw[1], hw[2], hw[3]);
+    if (QF32) Qlo[j] = make_h8(lw[0], lw[1], lw[2], lw[3]);
+  }
+  // band norms: lane k holds bands (4k + jj) mod 8, half (k >> 1)
+  float bfull[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) bfull[jj] = bsum[jj] + shfl_xor(bsum[jj], 32);
+  float qn2 = bfull[0] + bfull[1] + bfull[2] + bfull[3];
+  qn2 += shfl_xor(qn2, 16);                    // ||q_h||^2 over all 8 bands
+  float beta[8];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float mine = a.sm_scale * sqrtf(bfull[jj]);
+    float other = shfl_xor(mine, 16);
+    // lanes with k even hold bands 0..3, odd hold 4..7
+    beta[jj] = (kq & 1) ? other : mine;
+    beta[4 + jj] = (kq & 1) ? mine : other;
+  }
+  // beta scaled by a power of two into [2^14, 2^15) so its fp16 hi/lo split is exact
+  int be = 0;
+  {
+    float bmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, beta[e]);
+    if (bmax > 0.0f && bmax < INFINITY) {
+      int ex;
+      frexpf(bmax, &ex);
+      be = 15 - ex;
+    }
+  }
+  const float bunscale = ldexpf(1.0f, -be);
+  h8 Bbeta;
+  {
+    uint32_t bw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = ldexpf(beta[2 * e], be), x1 = ldexpf(beta[2 * e + 1], be);
+      _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      h2 hi2 = {h0, h1};
+      h2 lo2 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+      uint32_t v = kq == 2 ? as_u32(lo2) : as_u32(hi2);
+      bw[e] = (kq == 3 || !hv) ? 0u : v;
+    }
+    Bbeta = make_h8(bw[0], bw[1], bw[2], bw[3]);
+  }
+  const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // logit (log2 units) per raw unit
+  const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
+  const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
+
+  uint32_t keyK = 0, keyV = 0;
+  if (SCHEME == WC_DITHER_INT8) {
+    const uint64_t sd = a.seed[b];
+    keyK = stream_key(sd, (uint32_t)a.layer, (uint32_t)g, 0u);
+    keyV = stream_key(sd, (uint32_t)a.layer, (uint32_t)g, 1u);
+  }
+
+  // ---------------------------------------------------------------- state
+  float m_run = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
+  f4 O[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) O[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(c.k_codes);
+  const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(c.v_codes);
+
+  for (int jj = p0 + wave; jj < p1; jj += kNW) {
+    const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
+    const int tok0 = jj * 16;
+    const int64_t pg = ((int64_t)a.layer * c.num_pages + phys) * hkv + g;
+    const int slot = c.exact_slot ? c.exact_slot[pg] : -1;
+    const bool exact = slot >= 0;
+
+    // ---------------- QK^T
+    f4 Dc = {0.f, 0.f, 0.f, 0.f}, Dh = Dc, Dl = Dc;
+    float st[4];
+    if (!exact) {
+      const uint4* kp = reinterpret_cast<const uint4*>(kcodes + pg * 2048 + n * 128 + 32 * kq);
+      const uint4 k0 = kp[0], k1 = kp[1];
+      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const uint32_t base = keyK + (uint32_t)(64 * (tok0 + n) + 16 * kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t c0, c1, c2, c3;
+        if (SCHEME == WC_DITHER_INT8) {
+          codes_to_h(kw[2 * j], c0, c1);
+          codes_to_h(kw[2 * j + 1], c2, c3);
+        } else {
+          fp8_to_h(kw[2 * j], c0, c1);
+          fp8_to_h(kw[2 * j + 1], c2, c3);
+        }
+        const h8 Ac = make_h8(c0, c1, c2, c3);
+        Dc = mfma32(Ac, Qhi[j], Dc);
+        if (QF32) Dc = mfma32(Ac, Qlo[j], Dc);
+        if (SCHEME == WC_DITHER_INT8) {
+          uint32_t hh[4], ll[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) draw_to_h(pcg(base + (uint32_t)(4 * j + e)), hh[e], ll[e]);
+          const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
+          const h8 Al = make_h8(ll[0], ll[1], ll[2], ll[3]);
+          Dh = mfma32(Ah, Qhi[j], Dh);
+          Dl = mfma32(Al, Qhi[j], Dl);
+          if (QF32) {
+            Dh = mfma32(Ah, Qlo[j], Dh);
+            Dl = mfma32(Al, Qlo[j], Dl);
+          }
+        }
+      }
+      if (SCHEME == WC_DITHER_INT8) {
+        const float4 s4 = *reinterpret_cast<const float4*>(c.k_scale + pg * 16 + 4 * kq);
+        st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+      } else {
+        st[0] = st[1] = st[2] = st[3] = 1.0f;
+      }
+    } else {
+      const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)slot * 16 + n) * 128 + 32 * kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = xp[j];
+        const h8 Ax = make_h8(v.x, v.y, v.z, v.w);
+        Dc = mfma32(Ax, Qhi[j], Dc);
+        if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
+      }
+      const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)slot * 16 + 4 * kq);
+      st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+    }
+    float l2[4];
+    bool valid[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float raw = Dc[r];
+      if (SCHEME == WC_DITHER_INT8 && !exact) raw = raw - Dh[r] * 0.00390625f - Dl[r] * 1.52587890625e-05f;
+      valid[r] = tok0 + 4 * kq + r < S;
+      l2[r] = valid[r] ? qs2 * st[r] * raw : -INFINITY;
+    }
+
+    // ---------------- per-token bounds (Tier A by MFMA, Tier B by one multiply)
+    float cA[4] = {0.f, 0.f, 0.f, 0.f}, cB[4] = {0.f, 0.f, 0.f, 0.f};
+    if (meterA && !exact) {
+      const float4* wp = reinterpret_cast<const float4*>(c.witness + (pg * 16 + n) * 8);
+      const float4 w0 = wp[0], w1 = wp[1];
+      float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float wmax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wmax = fmaxf(wmax, wv[e]);
+      int we = 0;
+      if (wmax > 0.0f && wmax < INFINITY) {
+        int ex;
+        frexpf(wmax, &ex);
+        we = 15 - ex;
+      }
+      uint32_t aw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0 = ldexpf(wv[2 * e], we), x1 = ldexpf(wv[2 * e + 1], we);
+        _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+        h2 hi2 = {h0, h1};
+        h2 lo2 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+        aw[e] = kq == 3 ? 0u : (kq == 1 ? as_u32(lo2) : as_u32(hi2));
+      }
+      const f4 Da = mfma32(make_h8(aw[0], aw[1], aw[2], aw[3]), Bbeta, f4{0.f, 0.f, 0.f, 0.f});
+      const float wunscale = ldexpf(1.0f, -we);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = __shfl(wunscale, 4 * kq + r, 64) * bunscale;
+        cA[r] = valid[r] ? Da[r] * f : 0.0f;
+      }
+    }
+    if (meterB && !exact) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cB[r] = valid[r] ? kappa * st[r] : 0.0f;
+    }
+
+    // ---------------- online softmax and meter accumulators
+    float tmax = fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3]));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+    float p[4], psum = 0.0f, ea = 0.0f, eb = 0.0f, er = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = valid[r] ? exp2f(l2[r] - m_new) : 0.0f;
+      psum += p[r];
+      if (meterA) ea += cA[r] >= 88.0f ? INFINITY : p[r] * expm1_pos(cA[r]);
+      if (meterB) eb += cB[r] >= 88.0f ? INFINITY : p[r] * expm1_pos(cB[r]);
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    if (meterA) na = fmaf(na, alpha, ea);
+    if (meterB) nb = fmaf(nb, alpha, eb);
+    m_run = m_new;
+    if (risk) {
+      er = gateB ? eb : ea;
+      er += shfl_xor(er, 16);
+      er += shfl_xor(er, 32);
+      if (kq == 0 && hv)
+        a.block_logrisk[((int64_t)b * a.Hq + h) * a.max_pages + jj] =
+            er > 0.0f ? logf(er) + m_new * kLn2 : -INFINITY;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) O[t] *= alpha;
+
+    // ---------------- PV: O^T += Vhat^T P^T
+    float sv[4];
+    if (SCHEME == WC_DITHER_INT8) {
+      const float4 s4 = *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq);
+      sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
+    } else {
+      sv[0] = sv[1] = sv[2] = sv[3] = 1.0f;
+    }
+    _Float16 pb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pb[r] = valid[r] ? (_Float16)(p[r] * sv[r]) : (_Float16)0.0f;
+    const h4 Bc = {pb[0], pb[1], pb[2], pb[3]};
+    const h4 Bh = Bc * (_Float16)(-0.00390625f);
+    const h4 Bl = Bc * (_Float16)(-1.52587890625e-05f);
+    const uint4* vp = reinterpret_cast<const uint4*>(vcodes + pg * 2048 + kq * 512 + 32 * n);
+    const uint4 v0 = vp[0], v1 = vp[1];
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t vbase = keyV + (uint32_t)(128 * ((tok0 + 4 * kq) >> 1) + 8 * n);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t c0, c1;
+      if (SCHEME == WC_DITHER_INT8)
+        codes_to_h(vw[t], c0, c1);
+      else
+        fp8_to_h(vw[t], c0, c1);
+      O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
+      if (SCHEME == WC_DITHER_INT8) {
+        uint32_t hh0, ll0, hh1, ll1;
+        draw_to_h(pcg(vbase + (uint32_t)t), hh0, ll0);
+        draw_to_h(pcg(vbase + 128u + (uint32_t)t), hh1, ll1);
+        O[t] = mfma16(make_h4(hh0, hh1), Bh, O[t]);
+        O[t] = mfma16(make_h4(ll0, ll1), Bl, O[t]);
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- combine waves
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  na += shfl_xor(na, 16);
+  na += shfl_xor(na, 32);
+  nb += shfl_xor(nb, 16);
+  nb += shfl_xor(nb, 32);
+  __shared__ float sO[kNW][16][128];
+  __shared__ float sM[kNW][16][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sO[wave][n][32 * kq + 8 * r + t] = O[t][r];
+  if (kq == 0) {
+    sM[wave][n][0] = m_run;
+    sM[wave][n][1] = l_run;
+    sM[wave][n][2] = na;
+    sM[wave][n][3] = nb;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * kPartial; e += 256) {
+    const int hn = e / kPartial, f = e % kPartial;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sM[w][hn][0]);
+    float val = 0.0f;
+    if (f == 0) {
+      val = M;
+    } else if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const float mw = sM[w][hn][0];
+        const float sc = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+        const float x = f < 4 ? sM[w][hn][f] : sO[w][hn][f - 4];
+        val = fmaf(sc, x, val);
+      }
+    }
+    a.partials[(((int64_t)b * a.Hq + g * G + hn) * a.n_split + split) * kPartial + f] = val;
+  }
+}
+
+// ---------------------------------------------------------------- LSE merge
+// One wave per (b, h): lanes take two output channels each.
+__global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ part, int n_split, float* o,
+                                                   float* lse, float* meter_a, float* meter_b) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const float* pp = part + (int64_t)bh * n_split * kPartial;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[s * kPartial]);
+  float L = 0.f, NA = 0.f, NB = 0.f, o0 = 0.f, o1 = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float* q = pp + s * kPartial;
+      const float ms = q[0];
+      const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+      L = fmaf(w, q[1], L);
+      NA = fmaf(w, q[2], NA);
+      NB = fmaf(w, q[3], NB);
+      o0 = fmaf(w, q[4 + 2 * lane], o0);
+      o1 = fmaf(w, q[5 + 2 * lane], o1);
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  o[(int64_t)bh * 128 + 2 * lane] = o0 * inv;
+  o[(int64_t)bh * 128 + 2 * lane + 1] = o1 * inv;
+  if (lane == 0) {
+    lse[bh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    const float ea = NA * inv, eb = NB * inv;
+    if (meter_a) meter_a[bh] = ea * (1.0f + 0.5f * ea);
+    if (meter_b) meter_b[bh] = eb * (1.0f + 0.5f * eb);
+  }
+}
+
+}  // namespace wc
+
+using namespace wc;
+
+extern "C" size_t wc_decode_workspace_bytes(int B, int Hq, int n_split) {
+  if (B < 0 || Hq < 0 || n_split < 0) return 0;
+  return (size_t)B * Hq * n_split * kPartial * sizeof(float);
+}
+
+extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_dtype, int B, int Hq,
+                                    const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                                    const uint64_t* seed, float sm_scale, unsigned meter_mask, double delta_req,
+                                    int L, int H, int T, int n_split, float* partials, size_t ws_bytes,
+                                    float* block_logrisk, void* stream) {
+  if (!cache || !q || !page_table || !ctx_len || !partials) {
+    set_error("wc_decode_attn_meter: null pointer");
+    return WC_EINVAL;
+  }
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1) {
+    set_error("wc_decode_attn_meter: need head_dim 128, 8 bands, 16-token pages");
+    return WC_EUNSUPPORTED;
+  }
+  if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3) {
+    set_error("wc_decode_attn_meter: scheme %d has no decode path", c.scheme);
+    return WC_EUNSUPPORTED;
+  }
+  if (q_dtype != WC_F32 && q_dtype != WC_BF16) {
+    set_error("wc_decode_attn_meter: q_dtype must be WC_F32 or WC_BF16");
+    return WC_EUNSUPPORTED;
+  }
+  if (B < 0 || Hq < 1 || Hq % c.num_kv_heads != 0 || Hq / c.num_kv_heads > 16 || max_pages < 1 ||
+      n_split < 1 || n_split > 1024 || layer < 0 || layer >= c.num_layers) {
+    set_error("wc_decode_attn_meter: bad B/Hq/max_pages/n_split/layer");
+    return WC_EINVAL;
+  }
+  if (meter_mask & ~(WC_METER_A | WC_METER_B)) {
+    set_error("wc_decode_attn_meter: unknown meter_mask bits");
+    return WC_EINVAL;
+  }
+  if ((meter_mask & WC_METER_B) && (c.scheme != WC_DITHER_INT8 || !(meter_mask & WC_METER_A))) {
+    set_error("wc_decode_attn_meter: Tier B needs the dithered INT8 scheme and Tier A");
+    return WC_EINVAL;
+  }
+  if ((meter_mask & WC_METER_A) && !c.witness) {
+    set_error("wc_decode_attn_meter: Tier A needs the witness");
+    return WC_EINVAL;
+  }
+  if (block_logrisk && !(meter_mask & WC_METER_A)) {
+    set_error("wc_decode_attn_meter: block risks need the meter on");
+    return WC_EINVAL;
+  }
+  if (c.scheme == WC_DITHER_INT8 && (!seed || !c.k_scale || !c.v_scale)) {
+    set_error("wc_decode_attn_meter: INT8 cache needs seeds and scales");
+    return WC_EINVAL;
+  }
+  if (!c.k_codes || !c.v_codes) {
+    set_error("wc_decode_attn_meter: cache codes not set");
+    return WC_EINVAL;
+  }
+  if (c.exact_slot && (!c.exact_pool || !c.exact_scale)) {
+    set_error("wc_decode_attn_meter: exact_slot set without exact_pool/exact_scale");
+    return WC_EINVAL;
+  }
+  if (!(sm_scale > 0.0f) || !(delta_req > 0.0 && delta_req < 1.0) || L < 1 || H < 1 || T < 1) {
+    set_error("wc_decode_attn_meter: need sm_scale > 0, 0 < delta_req < 1, L, H, T >= 1");
+    return WC_EINVAL;
+  }
+  if (ws_bytes < wc_decode_workspace_bytes(B, Hq, n_split)) {
+    set_error("wc_decode_attn_meter: workspace %zu < %zu bytes", ws_bytes, wc_decode_workspace_bytes(B, Hq, n_split));
+    return WC_EWORKSPACE;
+  }
+  if (B == 0) return WC_OK;
+  const double dloc = delta_req / ((double)L * (double)H * (double)T);
+  DecodeArgs a{q, page_table, ctx_len, seed, partials, block_logrisk, B, Hq, Hq / c.num_kv_heads, max_pages,
+               n_split, layer, meter_mask, sm_scale, (float)(-log(dloc))};
+  dim3 grid((unsigned)n_split, (unsigned)c.num_kv_heads, (unsigned)B);
+  hipStream_t st = (hipStream_t)stream;
+  if (c.scheme == WC_DITHER_INT8) {
+    if (q_dtype == WC_BF16)
+      hipLaunchKernelGGL((decode_kernel<WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<WC_DITHER_INT8, true>), grid, dim3(256), 0, st, c, a);
+  } else {
+    if (q_dtype == WC_BF16)
+      hipLaunchKernelGGL((decode_kernel<WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<WC_FP8_E4M3, true>), grid, dim3(256), 0, st, c, a);
+  }
+  return check_launch("wc_decode_attn_meter");
+}
+
+extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
+                            float* meter_a, float* meter_b, void* stream) {
+  if (!partials || !o || !lse || B < 0 || Hq < 1 || n_split < 1 || n_split > 1024) {
+    set_error("wc_lse_merge: bad arguments");
+    return WC_EINVAL;
+  }
+  if (B == 0) return WC_OK;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split, o,
+                     lse, meter_a, meter_b);
+  return check_launch("wc_lse_merge");
+}

@@ -1,0 +1,82 @@
+// Shared device helpers and host glue of the WitCert HIP library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/witcert.h"
+
+namespace wc {
+
+// ---------------------------------------------------------------- host glue
+void set_error(const char* fmt, ...);
+int check_launch(const char* what);
+
+// ---------------------------------------------------------------- dither
+// pcg hash of Jarzynski and Olano, "Hash Functions for GPU Rendering",
+// JCGT 9(3), 2020: one LCG step followed by the RXS-M-XS output permutation.
+__host__ __device__ __forceinline__ uint32_t pcg(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+// 32-bit key of one dither stream (stream 0 = keys, 1 = values), chained
+// from the 64-bit sequence seed, the layer and the KV head.
+__host__ __device__ __forceinline__ uint32_t stream_key(uint64_t seed, uint32_t layer,
+                                                        uint32_t kv_head, uint32_t stream) {
+  uint32_t k = pcg((uint32_t)(seed >> 32));
+  k = pcg(k ^ (uint32_t)seed);
+  k = pcg(k ^ layer);
+  return pcg(k ^ (2u * kv_head + stream));
+}
+
+// Key words: j = 64 t + c/2 (low half = even channel).
+// Value words: j = 128 (t/2) + c (low half = even token).
+// xi = k * 2^-16 - 1/2 with k the 16-bit half of pcg(key + j).
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Exact-rounding fp32 ops (the write path must agree bit for bit with a
+// float32 replay; the library is built with -ffp-contract=off as well).
+__device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
+__device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
+__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
+
+// Witness rounding guard: the float32 band norm is within ~2^-20 of the
+// exact norm; scaling by 1 + 2^-17 keeps the stored value above it.
+constexpr float kWitnessGuard = 1.0f + 7.62939453125e-06f;
+
+// OCP fp8 e4m3fn, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t code;
+  if (!(a <= 448.0f)) {
+    code = 0x7Eu;                              // saturate (also NaN input)
+  } else if (a < 0.015625f) {                  // below 2^-6: subnormal grid 2^-9
+    code = (uint32_t)rintf(a * 512.0f);        // 8 -> smallest normal, coded 0x08
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // a in [2^e, 2^(e+1))
+    float m = ldexpf(a, 3 - e);                // in [8, 16)
+    uint32_t q = (uint32_t)rintf(m);
+    if (q == 16u) { q = 8u; e += 1; }
+    code = ((uint32_t)(e + 7) << 3) | (q - 8u);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  float v = e == 0 ? (float)m * 0.001953125f : ldexpf((float)(8 + m), (int)e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace wc

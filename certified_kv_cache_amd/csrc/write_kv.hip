@@ -1,0 +1,412 @@
+// Write path: quantize K/V rows and store the key witness.
+//
+// WitCert summary (Tier B paragraph): subtractive dither
+// x^ = s(round(x/s + xi) - xi), xi regenerated at read time; (witness-theorem
+// paragraph) w_{t,b} = ||r_{t,b}|| stored once at write time; black-box
+// schemes (fp8 raw cast, kivi-2bit) measured through the same witness.
+//
+// INT8 / fp8: one row = one (layer, token, KV head) of 128 channels, handled
+// by 16 lanes with 8 channels each (one 16 B bf16 load), 4 rows per wave.
+// The row absmax and the band sums are 16-lane xor-shuffle reductions; band
+// b = dims 8b..8b+7 (lane b) and 64+8b..64+8b+7 (lane b+8).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "wc_common.h"
+
+namespace wc {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return WC_EHIP;
+  }
+  return WC_OK;
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
+  uint4 a = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+struct RowArgs {
+  int64_t n_tok;
+  int64_t layer_stride;
+  int64_t num_pages;
+  int hkv;
+  int layer0;
+  int n_layers;
+  const int64_t* slot;
+  const int32_t* pos;
+  const uint64_t* seed;
+};
+
+// Quantize the 8 channels of one lane; returns codes packed little-endian
+// in two words and the residual r = x^ - x.
+template <int SCHEME, bool IS_V>
+__device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, uint32_t key,
+                                       int32_t p, int lane16, uint32_t (&packed)[2], float (&r)[8]) {
+  packed[0] = packed[1] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int c = 8 * lane16 + i;
+    uint32_t code;
+    float xr;
+    if (SCHEME == WC_DITHER_INT8) {
+      uint32_t word, k16;
+      if (!IS_V) {
+        word = pcg(key + (uint32_t)(64 * p + (c >> 1)));
+        k16 = (c & 1) ? (word >> 16) : (word & 0xFFFFu);
+      } else {
+        word = pcg(key + (uint32_t)(128 * (p >> 1) + c));
+        k16 = (p & 1) ? (word >> 16) : (word & 0xFFFFu);
+      }
+      float xi = (float)k16 * 1.52587890625e-05f - 0.5f;   // exact
+      float q;
+      if (s == 0.0f) {
+        q = 0.0f;
+      } else {
+        float y = add_rn(mul_rn(x[i], inv), xi);
+        q = fminf(fmaxf(rintf(y), -128.0f), 127.0f);
+      }
+      code = (uint32_t)(int32_t)q & 0xFFu;
+      xr = fmaf(s, q - xi, -x[i]);           // q - xi exact; one rounding
+      if (s == 0.0f) xr = -x[i];
+    } else {
+      code = f32_to_e4m3(x[i]);
+      xr = e4m3_to_f32(code) - x[i];
+    }
+    packed[i >> 2] |= code << (8 * (i & 3));
+    r[i] = xr;
+  }
+}
+
+template <typename T, int SCHEME>
+__global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
+                                                         const T* __restrict__ vin, RowArgs a) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
+  const bool live = row < rows;
+  const int64_t rr = live ? row : 0;
+  const int g = (int)(rr % a.hkv);
+  const int64_t i = (rr / a.hkv) % a.n_tok;
+  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
+  const int layer = a.layer0 + l;
+  const int64_t slot = a.slot[i];
+  const int64_t page = slot / 16, off = slot % 16;
+  const int32_t p = a.pos[i];
+  const uint64_t seed = a.seed[i];
+  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
+  const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
+
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const bool isv = which == 1;
+    float x[8];
+    load8<T>((isv ? vin : kin) + in_off, x);
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, shfl_xor(am, m));
+    float s = 0.0f, inv = 0.0f;
+    if (SCHEME == WC_DITHER_INT8 && am > 0.0f) {
+      s = div_rn(am, 127.0f);
+      inv = div_rn(127.0f, am);
+    }
+    uint32_t packed[2];
+    float r[8];
+    uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(seed, (uint32_t)layer, (uint32_t)g, isv ? 1u : 0u) : 0u;
+    if (isv)
+      quant8<SCHEME, true>(x, s, inv, key, p, lane16, packed, r);
+    else
+      quant8<SCHEME, false>(x, s, inv, key, p, lane16, packed, r);
+    if (!isv) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
+      float tot = ss + shfl_xor(ss, 8);
+      float w = sqrtf(tot) * kWitnessGuard;
+      if (live) {
+        uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + (pg * 16 + off) * 128 + 8 * lane16;
+        *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
+        if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = w;
+        if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.k_scale[pg * 16 + off] = s;
+      }
+    } else if (live) {
+      uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 512 + (off & 3);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vc[(8 * lane16 + k) * 4] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
+      if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.v_scale[pg * 16 + off] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 2-bit (KIVI-style)
+// One workgroup per (layer, 32-token page, KV head).  Keys are grouped over
+// the 32 tokens of each channel, values over 32 channels of each token.
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p);
+template <>
+__device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ void quant2(float x, float mn, float scale, float inv, uint32_t& code, float& xhat) {
+  float q = 0.0f;
+  if (scale != 0.0f) q = fminf(fmaxf(rintf(mul_rn(x - mn, inv)), 0.0f), 3.0f);
+  code = (uint32_t)q;
+  xhat = add_rn(mn, mul_rn(q, scale));
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* __restrict__ kin,
+                                                          const T* __restrict__ vin, RowArgs a) {
+  __shared__ float xs[32][129];
+  __shared__ float red[2][2][128];
+  const int t = threadIdx.x;
+  const int64_t ngrp = a.n_tok / 32;
+  const int64_t blk = blockIdx.x;
+  const int g = (int)(blk % a.hkv);
+  const int64_t grp = (blk / a.hkv) % ngrp;
+  const int l = (int)(blk / ((int64_t)a.hkv * ngrp));
+  const int layer = a.layer0 + l;
+  const int64_t i0 = grp * 32;
+  const int64_t page = a.slot[i0] / 32;
+  const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;
+  const T* kb = kin + (int64_t)l * a.layer_stride;
+  const T* vb = vin + (int64_t)l * a.layer_stride;
+
+  // keys: stage the 32 x 128 tile, per-channel min/max over the 32 tokens
+  for (int e = t; e < 32 * 128; e += 256) {
+    int tok = e >> 7, ch = e & 127;
+    xs[tok][ch] = ldf<T>(kb + ((i0 + tok) * a.hkv + g) * 128 + ch);
+  }
+  __syncthreads();
+  const int ch = t & 127, h = t >> 7;
+  float mn = xs[16 * h][ch], mx = mn;
+  for (int k = 1; k < 16; ++k) {
+    mn = fminf(mn, xs[16 * h + k][ch]);
+    mx = fmaxf(mx, xs[16 * h + k][ch]);
+  }
+  red[0][h][ch] = mn;
+  red[1][h][ch] = mx;
+  __syncthreads();
+  mn = fminf(red[0][0][ch], red[0][1][ch]);
+  mx = fmaxf(red[1][0][ch], red[1][1][ch]);
+  const float scale = div_rn(mx - mn, 3.0f);
+  const float inv = scale != 0.0f ? div_rn(1.0f, scale) : 0.0f;
+  uint32_t packed = 0;
+  float res[16];
+  for (int k = 0; k < 16; ++k) {
+    uint32_t code;
+    float xh;
+    float x = xs[16 * h + k][ch];
+    quant2(x, mn, scale, inv, code, xh);
+    packed |= code << (2 * k);
+    res[k] = xh - x;
+  }
+  uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 1024 + ch * 8 + 4 * h;
+  *reinterpret_cast<uint32_t*>(kc) = packed;
+  if (h == 0) {
+    c.k_aux[(pg * 128 + ch) * 2 + 0] = scale;
+    c.k_aux[(pg * 128 + ch) * 2 + 1] = mn;
+  }
+  __syncthreads();
+  for (int k = 0; k < 16; ++k) xs[16 * h + k][ch] = res[k];
+  __syncthreads();
+  {
+    const int tok = t >> 3, b = t & 7;
+    float ss = 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      float r0 = xs[tok][8 * b + k];
+      ss = fmaf(r0, r0, ss);
+    }
+    float s2 = 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      float r1 = xs[tok][64 + 8 * b + k];
+      s2 = fmaf(r1, r1, s2);
+    }
+    c.witness[(pg * 32 + tok) * 8 + b] = sqrtf(ss + s2) * kWitnessGuard;
+  }
+  // values: groups of 32 channels of one token; thread = (token, 16-channel half-group)
+  {
+    const int tok = t >> 3, part = t & 7;
+    float x[16];
+    const T* src = vb + ((i0 + tok) * a.hkv + g) * 128 + 16 * part;
+    float vmn = ldf<T>(src), vmx = vmn;
+    for (int k = 0; k < 16; ++k) {
+      x[k] = ldf<T>(src + k);
+      vmn = fminf(vmn, x[k]);
+      vmx = fmaxf(vmx, x[k]);
+    }
+    vmn = fminf(vmn, __shfl_xor(vmn, 1, 64));
+    vmx = fmaxf(vmx, __shfl_xor(vmx, 1, 64));
+    const float vs = div_rn(vmx - vmn, 3.0f);
+    const float vinv = vs != 0.0f ? div_rn(1.0f, vs) : 0.0f;
+    uint32_t pk = 0;
+    for (int k = 0; k < 16; ++k) {
+      uint32_t code;
+      float xh;
+      quant2(x[k], vmn, vs, vinv, code, xh);
+      pk |= code << (2 * k);
+    }
+    uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 1024 + tok * 32 + 4 * part;
+    *reinterpret_cast<uint32_t*>(vc) = pk;
+    if ((part & 1) == 0) {
+      c.v_aux[((pg * 32 + tok) * 4 + part / 2) * 2 + 0] = vs;
+      c.v_aux[((pg * 32 + tok) * 4 + part / 2) * 2 + 1] = vmn;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dither fill (test hook)
+__global__ void dither_fill_kernel(uint32_t key, int stream_kv, int64_t pos0, int64_t n_pos, uint16_t* out) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_pos * 128) return;
+  int64_t t = pos0 + e / 128;
+  int c = (int)(e % 128);
+  uint32_t word, k16;
+  if (stream_kv == 0) {
+    word = pcg(key + (uint32_t)(64 * t + (c >> 1)));
+    k16 = (c & 1) ? word >> 16 : word & 0xFFFFu;
+  } else {
+    word = pcg(key + (uint32_t)(128 * (t >> 1) + c));
+    k16 = (t & 1) ? word >> 16 : word & 0xFFFFu;
+  }
+  out[e] = (uint16_t)k16;
+}
+
+}  // namespace wc
+
+using namespace wc;
+
+extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
+                           int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
+                           const int32_t* pos, const uint64_t* seed, void* stream) {
+  if (!cache || !k || !v || !slot || !pos || !seed) {
+    set_error("wc_write_kv: null pointer");
+    return WC_EINVAL;
+  }
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.num_bands != 8 || c.num_kv_heads < 1 || c.num_layers < 1 || c.num_pages < 1) {
+    set_error("wc_write_kv: need head_dim 128, 8 bands, >= 1 KV head, layer and page");
+    return WC_EUNSUPPORTED;
+  }
+  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_tok < 0) {
+    set_error("wc_write_kv: layer range or token count out of range");
+    return WC_EINVAL;
+  }
+  if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
+    set_error("wc_write_kv: in_dtype must be WC_F32 or WC_BF16");
+    return WC_EUNSUPPORTED;
+  }
+  if (n_layers > 1 && layer_stride < n_tok * c.num_kv_heads * 128) {
+    set_error("wc_write_kv: layer_stride smaller than one layer");
+    return WC_EINVAL;
+  }
+  if (!c.k_codes || !c.v_codes || !c.witness) {
+    set_error("wc_write_kv: cache codes and witness must be set");
+    return WC_EINVAL;
+  }
+  if (n_tok > (int64_t(1) << 26)) {
+    set_error("wc_write_kv: at most 2^26 tokens per call");
+    return WC_EINVAL;
+  }
+  RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, pos, seed};
+  hipStream_t st = (hipStream_t)stream;
+  if (n_tok == 0) return WC_OK;
+  if (c.scheme == WC_DITHER_INT8 || c.scheme == WC_FP8_E4M3) {
+    if (c.page_size != 16) {
+      set_error("wc_write_kv: INT8 and fp8 caches use 16-token pages");
+      return WC_EUNSUPPORTED;
+    }
+    if (c.scheme == WC_DITHER_INT8 && (!c.k_scale || !c.v_scale)) {
+      set_error("wc_write_kv: INT8 cache needs k_scale and v_scale");
+      return WC_EINVAL;
+    }
+    const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
+    dim3 grid((unsigned)((rows + 15) / 16));
+    if (c.scheme == WC_DITHER_INT8) {
+      if (in_dtype == WC_BF16)
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8>), grid, dim3(256), 0, st, c,
+                           (const uint16_t*)k, (const uint16_t*)v, a);
+      else
+        hipLaunchKernelGGL((write_rows_kernel<float, WC_DITHER_INT8>), grid, dim3(256), 0, st, c,
+                           (const float*)k, (const float*)v, a);
+    } else {
+      if (in_dtype == WC_BF16)
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_FP8_E4M3>), grid, dim3(256), 0, st, c,
+                           (const uint16_t*)k, (const uint16_t*)v, a);
+      else
+        hipLaunchKernelGGL((write_rows_kernel<float, WC_FP8_E4M3>), grid, dim3(256), 0, st, c,
+                           (const float*)k, (const float*)v, a);
+    }
+    return check_launch("wc_write_kv");
+  }
+  if (c.scheme == WC_KIVI2) {
+    if (c.page_size != 32 || (n_tok % 32) != 0) {
+      set_error("wc_write_kv: 2-bit cache needs 32-token pages and whole pages of tokens");
+      return WC_EUNSUPPORTED;
+    }
+    if (!c.k_aux || !c.v_aux) {
+      set_error("wc_write_kv: 2-bit cache needs k_aux and v_aux");
+      return WC_EINVAL;
+    }
+    dim3 grid((unsigned)((int64_t)n_layers * (n_tok / 32) * c.num_kv_heads));
+    if (in_dtype == WC_BF16)
+      hipLaunchKernelGGL((write_kivi2_kernel<uint16_t>), grid, dim3(256), 0, st, c, (const uint16_t*)k,
+                         (const uint16_t*)v, a);
+    else
+      hipLaunchKernelGGL((write_kivi2_kernel<float>), grid, dim3(256), 0, st, c, (const float*)k,
+                         (const float*)v, a);
+    return check_launch("wc_write_kv");
+  }
+  set_error("wc_write_kv: unknown scheme %d", c.scheme);
+  return WC_EUNSUPPORTED;
+}
+
+extern "C" int wc_dither_fill(uint64_t seed, int layer, int kv_head, int stream_kv, int64_t pos0, int64_t n_pos,
+                              uint16_t* out, void* stream) {
+  if (!out || n_pos < 0 || pos0 < 0 || (stream_kv != 0 && stream_kv != 1) || pos0 + n_pos > (int64_t(1) << 26)) {
+    set_error("wc_dither_fill: bad arguments");
+    return WC_EINVAL;
+  }
+  if (n_pos == 0) return WC_OK;
+  uint32_t key = stream_key(seed, (uint32_t)layer, (uint32_t)kv_head, (uint32_t)stream_kv);
+  int64_t n = n_pos * 128;
+  hipLaunchKernelGGL(dither_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, key,
+                     stream_kv, pos0, n_pos, out);
+  return check_launch("wc_dither_fill");
+}
+
+extern "C" const char* wc_last_error(void) { return g_err; }
+extern "C" const char* wc_version(void) { return "witcert-mi355x 0.1"; }

@@ -1,0 +1,226 @@
+/*
+ * witcert.h -- C ABI of the MI355X (gfx950) WitCert hot path.
+ *
+ * WitCert ("WitCert: Sound Runtime Risk Observability and Gating for
+ * KV-Cache Quantization", arXiv 2607.28699) stores, at write time, a
+ * per-band residual-norm witness beside a quantized KV cache and computes,
+ * in the same pass as decode attention, a per-(layer, head, step) upper
+ * bound on the total variation between exact and compressed attention.
+ * The implementation paragraph of the m.montaan.com summary lists the four
+ * pieces exported here: a write path storing witnesses, a fused decode
+ * attention kernel computing output and meter in one data pass, LSE-merged
+ * certificate accumulation across KV splits, and a gate that pages in exact
+ * blocks from a CPU backing store when the meter exceeds a threshold.
+ *
+ * Conventions
+ *  - The caller owns every buffer.  Device buffers come from any allocator
+ *    (PyTorch here); the exact backing store is pinned host memory that the
+ *    device can read (hipHostMalloc / torch pin_memory).  The library never
+ *    allocates or frees, and keeps no state beyond a thread-local error text.
+ *  - Every call is asynchronous on the HIP stream passed as `stream`
+ *    (a hipStream_t; NULL = the default stream) and never synchronizes.
+ *  - Shapes are validated on the host before any launch.  Return codes:
+ *      WC_OK 0, WC_EINVAL -1 (null pointer, bad shape or argument),
+ *      WC_EUNSUPPORTED -2 (scheme/dtype/shape not built),
+ *      WC_EWORKSPACE -3 (workspace too small), WC_EHIP -4 (launch error).
+ *    wc_last_error() returns a text for the last failure on this thread.
+ *  - Device-resident index arrays (slots, positions, page tables, lengths)
+ *    cannot be checked on the host: out-of-range values are undefined
+ *    behaviour, as for any kernel argument.
+ *
+ * Cache layout (one layer = `num_pages` physical pages; arrays carry a
+ * leading layer dimension of `num_layers`; P = num_pages, Hkv = num_kv_heads,
+ * d = 128, page = 16 tokens for INT8/fp8, 32 for 2-bit):
+ *  k_codes   INT8/fp8: [L][P][Hkv][16][128] bytes, token-major.
+ *            2-bit:    [L][P][Hkv][128][8] bytes (32 tokens of one channel,
+ *                      4 codes per byte, token i in bits 2(i%4)).
+ *  v_codes   INT8/fp8: [L][P][Hkv][4][128][4] bytes: token t of the page at
+ *                      ((t/4)*128 + c)*4 + t%4 (four tokens of one channel
+ *                      are one 32-bit word).
+ *            2-bit:    [L][P][Hkv][32][32] bytes (token-major, 4 codes/byte).
+ *  k_scale,
+ *  v_scale   INT8: fp32 [L][P][Hkv][16], s = absmax/127 of the row.
+ *  k_aux     2-bit: fp32 [L][P][Hkv][128][2] (scale, min) per channel group.
+ *  v_aux     2-bit: fp32 [L][P][Hkv][32][4][2] (scale, min) per token group.
+ *  witness   fp32 [L][P][Hkv][page][8]: w_{t,b} = ||r_{t,b}||, keys only.
+ *  exact_slot int32 [L][P][Hkv]: -1 = quantized, else the slot of the
+ *            repaired block in the exact pool.
+ *  exact_pool fp16 [capacity][16][128] and exact_scale fp32 [capacity][16]:
+ *            a repaired block's exact keys as fp16(k * 2^e_t) with the
+ *            per-token power of two 2^-e_t in exact_scale.
+ */
+#ifndef WITCERT_H
+#define WITCERT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WC_OK 0
+#define WC_EINVAL (-1)
+#define WC_EUNSUPPORTED (-2)
+#define WC_EWORKSPACE (-3)
+#define WC_EHIP (-4)
+
+/* Quantization schemes. */
+#define WC_DITHER_INT8 0 /* subtractively-dithered INT8 (Tier A + Tier B) */
+#define WC_FP8_E4M3 1    /* fp8 e4m3fn raw cast, black box (Tier A)       */
+#define WC_KIVI2 2       /* 2-bit asymmetric, group 32 (write path only)  */
+
+/* Input dtypes. */
+#define WC_F32 0
+#define WC_BF16 1
+
+/* meter_mask bits. */
+#define WC_METER_A 1u
+#define WC_METER_B 2u
+
+typedef struct {
+  int32_t scheme;       /* WC_DITHER_INT8 | WC_FP8_E4M3 | WC_KIVI2          */
+  int32_t head_dim;     /* must be 128                                       */
+  int32_t num_kv_heads; /* Hkv >= 1                                          */
+  int32_t num_bands;    /* must be 8: band b = frequency pairs [8b, 8b+8)    */
+  int32_t page_size;    /* 16 (INT8, fp8) or 32 (2-bit)                      */
+  int32_t num_layers;   /* leading dimension of every cache array            */
+  int64_t num_pages;    /* physical pages per layer                          */
+  void* k_codes;
+  void* v_codes;
+  float* k_scale;
+  float* v_scale;
+  float* k_aux;
+  float* v_aux;
+  float* witness;
+  int32_t* exact_slot;  /* may be NULL when no block is ever repaired        */
+  uint16_t* exact_pool;
+  float* exact_scale;
+  int64_t pool_capacity;
+} wc_cache;
+
+/*
+ * wc_write_kv -- quantize keys and values and store their witnesses.
+ *
+ * Defined by the WitCert summary: subtractive dither x^ = s(round(x/s + xi)
+ * - xi) with xi regenerated at read time (Tier B paragraph), the witness
+ * w_{t,b} = ||r_{t,b}|| stored once per token at write time (witness-theorem
+ * paragraph), and black-box schemes measured through the same witness
+ * (implementation paragraph; fp8 raw and kivi-2bit in the RULER paragraph).
+ *
+ *  k, v       device, dtype in_dtype (WC_F32 | WC_BF16), post-RoPE,
+ *             [n_layers][n_tok][Hkv][128]; layer l starts at
+ *             l * layer_stride elements.
+ *  layer0     first cache layer written; layers layer0 .. layer0+n_layers-1.
+ *  slot       device int64 [n_tok]: page * page_size + offset of each token
+ *             (the same slots in every layer).  For 2-bit the tokens must
+ *             come in whole pages: slot[32g + i] = page_g * 32 + i.
+ *  pos        device int32 [n_tok]: the token's 0-based position in its
+ *             sequence (dither counter).
+ *  seed       device uint64 [n_tok]: dither seed of the token's sequence.
+ * Writes k_codes, v_codes, scales (or aux) and the key witness.
+ */
+int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
+                int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
+                const int32_t* pos, const uint64_t* seed, void* stream);
+
+/*
+ * wc_decode_attn_meter -- fused split-KV decode attention and meter.
+ *
+ * One data pass over the paged cache computes, per query head h, the
+ * compressed attention sum_t p~_t v^_t and the meter accumulators of the
+ * WitCert summary: Tier A (Theorem 2) c_t = sm_scale * sum_b ||q_b|| w_{t,b};
+ * Tier B (dithered INT8 only) c_t = sqrt(2 varsigma_t^2 log(2S/delta_loc)),
+ * varsigma_t^2 = sm_scale^2 s_t^2 ||q||^2 / 12, delta_loc = delta_req/(L*H*T);
+ * aggregated by E = sum_t p~_t expm1(c_t) (improvements list: TV <=
+ * min(1, (A^2-1)/2), A = 1 + E).  Repaired blocks use exact keys and c = 0.
+ *
+ *  q          device [B][Hq][128], q_dtype WC_F32 | WC_BF16; Hq multiple of Hkv,
+ *             Hq/Hkv <= 16.
+ *  page_table device int32 [B][max_pages] physical page of each logical block.
+ *  ctx_len    device int32 [B]: tokens cached per sequence (<= max_pages*16).
+ *  seed       device uint64 [B]: dither seed of each sequence.
+ *  meter_mask 0, WC_METER_A or WC_METER_A|WC_METER_B (B needs dithered INT8).
+ *             With 0 the witness is not read; output and LSE bits are the same
+ *             as with the meter on.
+ *  n_split    1..1024 KV splits per (sequence, KV head): split i covers blocks
+ *             [i*P_b/n_split, (i+1)*P_b/n_split) of the sequence's P_b blocks.
+ *  partials   device fp32 workspace [B][Hq][n_split][132]: per split
+ *             (m, l, N_A, N_B, o[128]) with m the running max of the logits in
+ *             log2 units, l = sum 2^(l2 - m), N_X = sum 2^(l2 - m) expm1(c_X),
+ *             o = sum 2^(l2 - m) v^.  ws_bytes >= wc_decode_workspace_bytes().
+ *  block_logrisk  nullable device fp32 [B][Hq][max_pages]: natural log of
+ *             sum_{t in block} exp(l_t) expm1(c_t) for the gate's tier (B if
+ *             requested, else A); -inf for blocks without risk.
+ */
+int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_dtype, int B, int Hq,
+                         const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                         const uint64_t* seed, float sm_scale, unsigned meter_mask, double delta_req,
+                         int L, int H, int T, int n_split, float* partials, size_t ws_bytes,
+                         float* block_logrisk, void* stream);
+
+/* Bytes of the decode workspace: B * Hq * n_split * 132 * 4. */
+size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
+
+/*
+ * wc_lse_merge -- merge KV-split partials by log-sum-exp (output and
+ * certificate together; summary implementation paragraph and paperswithlean
+ * Figure 2 caption).
+ *
+ *  o        device fp32 [B][Hq][128]: sum_t p~_t v^_t.
+ *  lse      device fp32 [B][Hq]: natural-log LSE of the logits (-inf if empty).
+ *  meter_a, meter_b  nullable device fp32 [B][Hq]: R = E (1 + E/2), unclamped;
+ *           the TV bound is min(1, R).  meter_b is 0 when Tier B is off.
+ */
+int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
+                 float* meter_a, float* meter_b, void* stream);
+
+/*
+ * wc_gate_pagein -- meter-driven repair from the exact backing store.
+ *
+ * WitCert summary (implementation paragraph) and paperswithlean
+ * (Problem/Approach, Figure 2 and Figure 5 captions): when the meter exceeds
+ * tau, exact blocks are paged in from the CPU store, ranked by risk, the
+ * repaired witnesses are zeroed and the repair persists.  Per (sequence b,
+ * KV head g): rho_fx[h][j] = min(ceil(exp(logrisk - lse_h) * 2^40), 2^47);
+ * X_h = sum_j rho_fx; trigger when max_h X_h > T = floor((sqrt(1+2 tau)-1) 2^40);
+ * repair the shortest prefix of the unrepaired blocks ranked by
+ * max_h rho_fx[h][j] (ties to the lower index) that leaves every
+ * X_h - sum rho_fx <= T, capped by budget_blocks (-1 = no cap).  Pool slots
+ * are handed out in (b, g, rank) order from *pool_used; selection stops when
+ * the pool is full.
+ *
+ *  host_exact_k  pinned host bf16 [L][P][Hkv][16][128], device-readable.
+ *  pool_used     device int64 [1], in/out.
+ *  bytes_paged   device int64 [1], incremented by 4096 per repaired block.
+ *  selected      nullable device int32 [B][Hkv][max_pages + 1]: count, then
+ *                the chosen blocks in rank order (those that got a slot).
+ *  rho_fx        nullable device uint64 [B][Hq][max_pages] test export.
+ *  workspace     device scratch, ws_bytes >= wc_gate_workspace_bytes().
+ * Requires cache->exact_slot, exact_pool, exact_scale; 0 <= tau, E_tau < 64.
+ */
+int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                   int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                   double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
+                   int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the gate workspace for B sequences, Hkv heads and max_pages blocks. */
+size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages);
+
+/*
+ * wc_dither_fill -- test hook: the 16-bit dither draws k (xi = k/65536 - 1/2)
+ * the kernels regenerate, for positions pos0 .. pos0+n_pos-1 of one stream
+ * (stream 0 = keys, 1 = values), into device uint16 out[n_pos][128].
+ */
+int wc_dither_fill(uint64_t seed, int layer, int kv_head, int stream_kv, int64_t pos0, int64_t n_pos,
+                   uint16_t* out, void* stream);
+
+const char* wc_last_error(void);
+const char* wc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WITCERT_H */

@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/witcert.h declares, and rejects bad arguments on the host before
+any launch (these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from certified_kv_cache_amd import _lib
+    return _lib
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "witcert.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wc_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for fn in ["wc_write_kv", "wc_decode_attn_meter", "wc_lse_merge", "wc_gate_pagein"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(L.EXPORTS)
+
+
+def test_version_and_workspace_sizes():
+    L = _lib()
+    assert L.lib.wc_version().startswith(b"witcert")
+    assert L.wc_decode_workspace_bytes(32, 28, 16) == 32 * 28 * 16 * 132 * 4
+    assert L.wc_decode_workspace_bytes(-1, 28, 16) == 0
+    assert L.wc_gate_workspace_bytes(2, 4, 10) > 0
+
+
+def _cache(L, **kw):
+    c = L.WcCache(L.WC_DITHER_INT8, 128, 4, 8, 16, 2, 10, *([1] * 10), 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_write_rejects_bad_arguments():
+    L = _lib()
+    f = L.lib.wc_write_kv
+    p = ctypes.c_void_p(16)
+    ok = _cache(L)
+    assert f(None, 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
+    assert f(ctypes.byref(_cache(L, head_dim=64)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(ok), 1, 2, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL      # layer range
+    assert f(ctypes.byref(ok), 0, 1, p, p, 7, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED  # dtype
+    assert f(ctypes.byref(ok), 0, 2, p, p, 1, 4, 10, p, p, p, None) == L.WC_EINVAL     # layer stride
+    assert f(ctypes.byref(_cache(L, page_size=32)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, scheme=2)), 0, 1, p, p, 1, 31, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, scheme=9)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, k_scale=None)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
+    assert f(ctypes.byref(ok), 0, 1, p, p, 1, 0, 0, p, p, p, None) == L.WC_OK         # nothing to do
+    assert b"wc_write_kv" in L.lib.wc_last_error()
+
+
+def test_decode_rejects_bad_arguments():
+    L = _lib()
+    f = L.lib.wc_decode_attn_meter
+    p = ctypes.c_void_p(16)
+    c = ctypes.byref(_cache(L))
+    ws = L.wc_decode_workspace_bytes(2, 28, 4)
+
+    def call(cache=c, layer=0, qd=1, B=2, Hq=28, mp=8, mask=3, dr=1e-2, ns=4, wsb=ws, br=None, seed=p):
+        return f(cache, layer, p, qd, B, Hq, p, mp, p, seed, 0.088, mask, dr, 28, 28, 256, ns, p, wsb, br, None)
+
+    assert call(wsb=ws - 1) == L.WC_EWORKSPACE
+    assert call(Hq=30) == L.WC_EINVAL                 # not a multiple of Hkv
+    assert call(Hq=4 * 17) == L.WC_EINVAL             # group larger than 16
+    assert call(ns=0) == L.WC_EINVAL
+    assert call(layer=2) == L.WC_EINVAL
+    assert call(qd=5) == L.WC_EUNSUPPORTED
+    assert call(mask=2) == L.WC_EINVAL                # Tier B without Tier A
+    assert call(mask=8) == L.WC_EINVAL
+    assert call(mask=0, br=p) == L.WC_EINVAL          # block risk needs the meter
+    assert call(dr=0.0) == L.WC_EINVAL
+    assert call(seed=None) == L.WC_EINVAL
+    assert call(cache=ctypes.byref(_cache(L, scheme=1)), mask=3) == L.WC_EINVAL   # Tier B needs INT8
+    assert call(cache=ctypes.byref(_cache(L, scheme=2))) == L.WC_EUNSUPPORTED
+    assert call(B=0) == L.WC_OK
+
+
+def test_merge_and_gate_reject_bad_arguments():
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None) == L.WC_EINVAL
+    assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None) == L.WC_EINVAL
+    g = L.lib.wc_gate_pagein
+    c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
+    wsb = L.wc_gate_workspace_bytes(2, 4, 8)
+
+    def call(cache=c, tau=0.2, mp=8, wsb=wsb, host=p):
+        return g(cache, 0, p, p, 2, 28, p, mp, p, tau, -1, host, p, p, None, None, p, wsb, None)
+
+    assert call(host=None) == L.WC_EINVAL
+    assert call(tau=-1.0) == L.WC_EINVAL
+    assert call(tau=1e6) == L.WC_EINVAL
+    assert call(mp=5000) == L.WC_EINVAL
+    assert call(wsb=1) == L.WC_EWORKSPACE
+    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
+    assert L.lib.wc_dither_fill(1, 0, 0, 2, 0, 4, p, None) == L.WC_EINVAL
