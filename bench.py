@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; the path shards without communication "
@@ -229,6 +231,13 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
+    if args.copy_ref:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_ref_bytes"] = 2 * src.numel() * 4
     print(json.dumps(out), flush=True)
 
 
