@@ -101,15 +101,6 @@ __device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// expm1 accurate to a few ulp relative on [0, 88]; +inf above (saturated bound).
-__device__ __forceinline__ float expm1_pos(float c) {
-  if (c < 0.03125f) {
-    float c2 = c * c;
-    return fmaf(c2, fmaf(c, fmaf(c, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), c);
-  }
-  return expm1f(c);
-}
-
 struct DecodeArgs {
   const void* q;
   const int32_t* page_table;
@@ -123,13 +114,60 @@ struct DecodeArgs {
   float neg_log_dloc;   // -log(delta_loc)
 };
 
+// One page of one wave: the 16 tokens' codes, scales and witness for the
+// lane's share, loaded one page ahead of its use.
+struct PageLoad {
+  uint4 k0, k1, v0, v1;   // key codes (token n, 32 channels); value codes (8 channels x 4 tokens)
+  float4 ks, vs;          // key / value scales of tokens 4k..4k+3
+  float2 w;               // witness bands 2k, 2k+1 of token n
+  int slot;               // exact-pool slot (-1 = quantized)
+  int64_t pg;             // page-head block index
+};
+
+template <int SCHEME>
+__device__ __forceinline__ void load_page(const wc_cache& c, const DecodeArgs& a, int b, int g, int jj, int n, int kq,
+                                          bool meterA, PageLoad& d) {
+  const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
+  d.pg = ((int64_t)a.layer * c.num_pages + phys) * c.num_kv_heads + g;
+  d.slot = c.exact_slot ? c.exact_slot[d.pg] : -1;
+  const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.k_codes) + d.pg * 2048 +
+                                                   n * 128 + 32 * kq);
+  d.k0 = kp[0];
+  d.k1 = kp[1];
+  const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.v_codes) + d.pg * 2048 +
+                                                   kq * 512 + 32 * n);
+  d.v0 = vp[0];
+  d.v1 = vp[1];
+  if (SCHEME == WC_DITHER_INT8) {
+    d.ks = *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq);
+    d.vs = *reinterpret_cast<const float4*>(c.v_scale + d.pg * 16 + 4 * kq);
+  } else {
+    d.ks = d.vs = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+  d.w = meterA ? *reinterpret_cast<const float2*>(c.witness + (d.pg * 16 + n) * 8 + 2 * kq) : make_float2(0.f, 0.f);
+}
+
+// expm1 for c >= 0: series below 2^-5, else 2^(c log2 e) - 1 on v_exp_f32.
+__device__ __forceinline__ float expm1_fast(float c) {
+  const float e = __builtin_amdgcn_exp2f(c * kLog2e) - 1.0f;
+  const float p = fmaf(c * c, fmaf(c, fmaf(c, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), c);
+  return c < 0.03125f ? p : e;
+}
+
+__device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Lazy rescale: the running max of a head only moves when a page's max
+// exceeds it by more than 8 (log2 units), so exp2 weights stay <= 256.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int SCHEME, bool QF32>
 __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kq = lane >> 4;
   const int G = a.G;
-  const int hkv = c.num_kv_heads;
   const int h = g * G + n;                     // query head of lane column n
   const bool hv = n < G;
   const int S = a.ctx_len[b];
@@ -138,9 +176,9 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   const bool meterA = (a.mask & WC_METER_A) != 0;
   const bool meterB = SCHEME == WC_DITHER_INT8 && (a.mask & WC_METER_B) != 0;
   const bool risk = a.block_logrisk != nullptr;
-  const bool gateB = meterB;
 
   // ---------------------------------------------------------------- query prep
+  // lane (n, k) holds channels 32k..32k+31 of head n.
   float qf[32];
   if (hv) {
     if (QF32) {
@@ -179,9 +217,10 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   if (qmax > 0.0f) {
     int ex;
     frexpf(qmax, &ex);                        // qmax in [2^(ex-1), 2^ex)
-    qe = 15 - ex;                              // scaled max in [2^14, 2^15)
+    qe = 15 - ex;                              // scaled max in [2^14, 2^15): exact in fp16 for bf16 q
   }
   h8 Qhi[4], Qlo[4];
+  float qsum = 0.0f;                           // sum of the fp16 query operand (dither bias)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t hw[4], lw[4];
@@ -191,15 +230,20 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
       _Float16 a0 = (_Float16)x0, a1 = (_Float16)x1;
       h2 hv2 = {a0, a1};
       hw[e] = as_u32(hv2);
+      qsum += (float)a0 + (float)a1;
       if (QF32) {
-        h2 lv2 = {(_Float16)(x0 - (float)a0), (_Float16)(x1 - (float)a1)};
+        _Float16 b0 = (_Float16)(x0 - (float)a0), b1 = (_Float16)(x1 - (float)a1);
+        h2 lv2 = {b0, b1};
         lw[e] = as_u32(lv2);
+        qsum += (float)b0 + (float)b1;
       }
     }
     Qhi[j] = make_h8(hw[0], hw[1], hw[2], hw[3]);
     if (QF32) Qlo[j] = make_h8(lw[0], lw[1], lw[2], lw[3]);
   }
-  // band norms: lane k holds bands (4k + jj) mod 8, half (k >> 1)
+  qsum += shfl_xor(qsum, 16);
+  qsum += shfl_xor(qsum, 32);
+  // band norms: lane k holds bands (4k + jj) mod 8 of one half; halves are k, k^2
   float bfull[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) bfull[jj] = bsum[jj] + shfl_xor(bsum[jj], 32);
@@ -210,38 +254,15 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   for (int jj = 0; jj < 4; ++jj) {
     float mine = a.sm_scale * sqrtf(bfull[jj]);
     float other = shfl_xor(mine, 16);
-    // lanes with k even hold bands 0..3, odd hold 4..7
-    beta[jj] = (kq & 1) ? other : mine;
+    beta[jj] = (kq & 1) ? other : mine;        // k even holds bands 0..3, odd 4..7
     beta[4 + jj] = (kq & 1) ? mine : other;
   }
-  // beta scaled by a power of two into [2^14, 2^15) so its fp16 hi/lo split is exact
-  int be = 0;
-  {
-    float bmax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bmax = fmaxf(bmax, beta[e]);
-    if (bmax > 0.0f && bmax < INFINITY) {
-      int ex;
-      frexpf(bmax, &ex);
-      be = 15 - ex;
-    }
-  }
-  const float bunscale = ldexpf(1.0f, -be);
-  h8 Bbeta;
-  {
-    uint32_t bw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x0 = ldexpf(beta[2 * e], be), x1 = ldexpf(beta[2 * e + 1], be);
-      _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      h2 hi2 = {h0, h1};
-      h2 lo2 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
-      uint32_t v = kq == 2 ? as_u32(lo2) : as_u32(hi2);
-      bw[e] = (kq == 3 || !hv) ? 0u : v;
-    }
-    Bbeta = make_h8(bw[0], bw[1], bw[2], bw[3]);
-  }
-  const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // logit (log2 units) per raw unit
+  // Tier A operands of the two fp32 MFMAs: K slot k <-> bands 2k and 2k+1
+  const float bA0 = hv ? beta[2 * kq] : 0.0f, bA1 = hv ? beta[2 * kq + 1] : 0.0f;
+  const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // log2-unit logit per raw unit
+  // raw = Dc - 2^-8 (Dh - 1152 sum q') - 2^-16 (Dl - 1024 sum q'): K-side dither
+  // bytes enter the MFMA as 1024 + byte, the bias is removed here.
+  const float qbias = qsum * (1152.0f * 0.00390625f + 1024.0f * 1.52587890625e-05f);
   const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
   const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
@@ -253,28 +274,24 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   }
 
   // ---------------------------------------------------------------- state
-  float m_run = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
   f4 O[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) O[t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(c.k_codes);
-  const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(c.v_codes);
-
-  for (int jj = p0 + wave; jj < p1; jj += kNW) {
-    const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
+  PageLoad cur, nxt;
+  int jj = p0 + wave;
+  if (jj < p1) load_page<SCHEME>(c, a, b, g, jj, n, kq, meterA, cur);
+  for (; jj < p1; jj += kNW) {
+    if (jj + kNW < p1) load_page<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt);
     const int tok0 = jj * 16;
-    const int64_t pg = ((int64_t)a.layer * c.num_pages + phys) * hkv + g;
-    const int slot = c.exact_slot ? c.exact_slot[pg] : -1;
-    const bool exact = slot >= 0;
+    const bool exact = cur.slot >= 0;
 
     // ---------------- QK^T
     f4 Dc = {0.f, 0.f, 0.f, 0.f}, Dh = Dc, Dl = Dc;
-    float st[4];
+    float st[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
     if (!exact) {
-      const uint4* kp = reinterpret_cast<const uint4*>(kcodes + pg * 2048 + n * 128 + 32 * kq);
-      const uint4 k0 = kp[0], k1 = kp[1];
-      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
       const uint32_t base = keyK + (uint32_t)(64 * (tok0 + n) + 16 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -292,7 +309,11 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
         if (SCHEME == WC_DITHER_INT8) {
           uint32_t hh[4], ll[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) draw_to_h(pcg(base + (uint32_t)(4 * j + e)), hh[e], ll[e]);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
+            hh[e] = perm(kMagic, wd, 0x04030401u);   // 1024 + high bytes
+            ll[e] = perm(kMagic, wd, 0x04020400u);   // 1024 + low bytes
+          }
           const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
           const h8 Al = make_h8(ll[0], ll[1], ll[2], ll[3]);
           Dh = mfma32(Ah, Qhi[j], Dh);
@@ -303,14 +324,8 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
           }
         }
       }
-      if (SCHEME == WC_DITHER_INT8) {
-        const float4 s4 = *reinterpret_cast<const float4*>(c.k_scale + pg * 16 + 4 * kq);
-        st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
-      } else {
-        st[0] = st[1] = st[2] = st[3] = 1.0f;
-      }
     } else {
-      const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)slot * 16 + n) * 128 + 32 * kq);
+      const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 v = xp[j];
@@ -318,102 +333,80 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
         Dc = mfma32(Ax, Qhi[j], Dc);
         if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
       }
-      const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)slot * 16 + 4 * kq);
+      const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
       st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+    }
+    // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs
+    f4 Da = {0.f, 0.f, 0.f, 0.f};
+    if (meterA && !exact) {
+      Da = mfma_f32(cur.w.x, bA0, Da);
+      Da = mfma_f32(cur.w.y, bA1, Da);
     }
     float l2[4];
     bool valid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float raw = Dc[r];
-      if (SCHEME == WC_DITHER_INT8 && !exact) raw = raw - Dh[r] * 0.00390625f - Dl[r] * 1.52587890625e-05f;
+      if (SCHEME == WC_DITHER_INT8 && !exact)
+        raw = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw + qbias));
       valid[r] = tok0 + 4 * kq + r < S;
       l2[r] = valid[r] ? qs2 * st[r] * raw : -INFINITY;
     }
 
-    // ---------------- per-token bounds (Tier A by MFMA, Tier B by one multiply)
-    float cA[4] = {0.f, 0.f, 0.f, 0.f}, cB[4] = {0.f, 0.f, 0.f, 0.f};
-    if (meterA && !exact) {
-      const float4* wp = reinterpret_cast<const float4*>(c.witness + (pg * 16 + n) * 8);
-      const float4 w0 = wp[0], w1 = wp[1];
-      float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      float wmax = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wmax = fmaxf(wmax, wv[e]);
-      int we = 0;
-      if (wmax > 0.0f && wmax < INFINITY) {
-        int ex;
-        frexpf(wmax, &ex);
-        we = 15 - ex;
-      }
-      uint32_t aw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x0 = ldexpf(wv[2 * e], we), x1 = ldexpf(wv[2 * e + 1], we);
-        _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-        h2 hi2 = {h0, h1};
-        h2 lo2 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
-        aw[e] = kq == 3 ? 0u : (kq == 1 ? as_u32(lo2) : as_u32(hi2));
-      }
-      const f4 Da = mfma32(make_h8(aw[0], aw[1], aw[2], aw[3]), Bbeta, f4{0.f, 0.f, 0.f, 0.f});
-      const float wunscale = ldexpf(1.0f, -we);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = __shfl(wunscale, 4 * kq + r, 64) * bunscale;
-        cA[r] = valid[r] ? Da[r] * f : 0.0f;
-      }
-    }
-    if (meterB && !exact) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cB[r] = valid[r] ? kappa * st[r] : 0.0f;
-    }
-
-    // ---------------- online softmax and meter accumulators
+    // ---------------- online softmax with lazy rescale
     float tmax = fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3]));
     tmax = fmaxf(tmax, shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
-    float p[4], psum = 0.0f, ea = 0.0f, eb = 0.0f, er = 0.0f;
+    const float svmax = fmaxf(fmaxf(cur.vs.x, cur.vs.y), fmaxf(cur.vs.z, cur.vs.w));
+    const bool move = tmax > m_ref + kRescaleSlack || (svmax > 128.0f && tmax > m_ref);
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float m_new = move ? tmax : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+      na *= alpha;
+      nb *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) O[t] *= alpha;
+      m_ref = m_new;
+    }
+    float p[4];
+    float psum = 0.0f, ea = 0.0f, eb = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = valid[r] ? exp2f(l2[r] - m_new) : 0.0f;
+      p[r] = valid[r] ? __builtin_amdgcn_exp2f(l2[r] - m_ref) : 0.0f;
       psum += p[r];
-      if (meterA) ea += cA[r] >= 88.0f ? INFINITY : p[r] * expm1_pos(cA[r]);
-      if (meterB) eb += cB[r] >= 88.0f ? INFINITY : p[r] * expm1_pos(cB[r]);
+      // a bound of 88 or more saturates the meter (+inf); the IEEE max also
+      // absorbs the 0 * inf of an underflowed weight
+      if (meterA) {
+        const float ca = (valid[r] && !exact) ? Da[r] : 0.0f;
+        ea += fmaxf(p[r] * expm1_fast(ca), ca >= 88.0f ? INFINITY : 0.0f);
+      }
+      if (meterB) {
+        const float cb = (valid[r] && !exact) ? kappa * st[r] : 0.0f;
+        eb += fmaxf(p[r] * expm1_fast(cb), cb >= 88.0f ? INFINITY : 0.0f);
+      }
     }
-    l_run = fmaf(l_run, alpha, psum);
-    if (meterA) na = fmaf(na, alpha, ea);
-    if (meterB) nb = fmaf(nb, alpha, eb);
-    m_run = m_new;
+    l_run += psum;
+    na += ea;
+    nb += eb;
     if (risk) {
-      er = gateB ? eb : ea;
+      float er = meterB ? eb : ea;
       er += shfl_xor(er, 16);
       er += shfl_xor(er, 32);
       if (kq == 0 && hv)
         a.block_logrisk[((int64_t)b * a.Hq + h) * a.max_pages + jj] =
-            er > 0.0f ? logf(er) + m_new * kLn2 : -INFINITY;
+            er > 0.0f ? logf(er) + m_ref * kLn2 : -INFINITY;
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) O[t] *= alpha;
 
     // ---------------- PV: O^T += Vhat^T P^T
-    float sv[4];
-    if (SCHEME == WC_DITHER_INT8) {
-      const float4 s4 = *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq);
-      sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
-    } else {
-      sv[0] = sv[1] = sv[2] = sv[3] = 1.0f;
-    }
+    const float sv[4] = {cur.vs.x, cur.vs.y, cur.vs.z, cur.vs.w};
     _Float16 pb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pb[r] = valid[r] ? (_Float16)(p[r] * sv[r]) : (_Float16)0.0f;
     const h4 Bc = {pb[0], pb[1], pb[2], pb[3]};
     const h4 Bh = Bc * (_Float16)(-0.00390625f);
     const h4 Bl = Bc * (_Float16)(-1.52587890625e-05f);
-    const uint4* vp = reinterpret_cast<const uint4*>(vcodes + pg * 2048 + kq * 512 + 32 * n);
-    const uint4 v0 = vp[0], v1 = vp[1];
-    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t vw[8] = {cur.v0.x, cur.v0.y, cur.v0.z, cur.v0.w, cur.v1.x, cur.v1.y, cur.v1.z, cur.v1.w};
     const uint32_t vbase = keyV + (uint32_t)(128 * ((tok0 + 4 * kq) >> 1) + 8 * n);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -431,7 +424,9 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
         O[t] = mfma16(make_h4(ll0, ll1), Bl, O[t]);
       }
     }
+    cur = nxt;
   }
+  const float m_run = m_ref;
 
   // ---------------------------------------------------------------- combine waves
   l_run += shfl_xor(l_run, 16);
