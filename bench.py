@@ -153,14 +153,13 @@ def cpu_baseline(w, B, S, pairs=6):
             q = w["q"][b, g * 7:(g + 1) * 7].float().cpu().numpy().astype(np.float64)
             seed = int(w["seeds"][b])
             pos = np.arange(S)
-            ck, sk, _ = quant.dither_int8(k32, dither.dither_rows(seed, 0, g, 0, pos))
-            cv, sv, _ = quant.dither_int8(v32, dither.dither_rows(seed, 0, g, 1, pos))
-            wt = quant.witness(k32, quant.dequant_dither_int8(ck, sk, dither.dither_rows(seed, 0, g, 0, pos)))
+            ck, sk, _ = quant.dither_int8(k32, dither.dither_rows(seed, 0, g, pos))
+            cv, sv, _ = quant.dither_int8(v32, dither.dither_rows(seed, 0, g, pos))
+            wt = quant.witness(k32, quant.dequant_dither_int8(ck, sk, dither.dither_rows(seed, 0, g, pos)))
             t0 = time.perf_counter()
-            xk = dither.dither_rows(seed, 0, g, 0, pos)
-            xv = dither.dither_rows(seed, 0, g, 1, pos)
-            khat = quant.dequant_dither_int8(ck, sk, xk)
-            vhat = quant.dequant_dither_int8(cv, sv, xv)
+            xi = dither.dither_rows(seed, 0, g, pos)
+            khat = quant.dequant_dither_int8(ck, sk, xi)
+            vhat = quant.dequant_dither_int8(cv, sv, xi)
             meter.decode_group(q, k32, khat, v32, vhat, wt, sm, k_scale=sk, log_term=lt)
             total += time.perf_counter() - t0
     sample_bytes = pairs * decode_bytes(B, S, True) / (B * HKV)

@@ -2,29 +2,31 @@
 
 WitCert (m.montaan.com summary, Tier B paragraph) quantizes with subtractive
 dither x^ = s(round(x/s + xi) - xi), xi ~ U[-1/2, 1/2), and regenerates xi
-deterministically when the cache is read instead of storing it.  The pages
-do not fix the generator.  Reading used here (stated in the design doc):
+deterministically when the cache is read instead of storing it; the draw is
+a counter hash of (seed, layer, head, token, channel).  The pages do not fix
+the generator.  Reading used here (stated in the design doc):
 
 * The generator is the ``pcg`` hash published by Jarzynski and Olano,
   "Hash Functions for GPU Rendering", JCGT 9(3), 2020 (an RXS-M-XS output
   permutation applied to one LCG step of the input).
-* A 32-bit stream key is chained from the sequence seed (64 bit), the layer,
-  the KV head and the stream bit (0 = keys, 1 = values)::
+* A 32-bit key is chained from the sequence seed (64 bit), the layer and the
+  KV head::
 
-      key = pcg(pcg(pcg(pcg(seed_hi) ^ seed_lo) ^ layer) ^ (2*kv_head + stream))
+      key = pcg(pcg(pcg(seed_hi) ^ seed_lo) ^ layer) ^ kv_head)
 
-* Each 32-bit hash word yields two 16-bit draws k (low half first).  Keys use
-  one word per (token, channel pair), values one word per (token pair,
-  channel)::
+* Each 32-bit hash word yields two 16-bit draws (low half = even channel),
+  one word per (token, channel pair)::
 
-      keys:   j = 64*t + c//2,   half = c % 2
-      values: j = 128*(t//2) + c, half = t % 2
-      word = pcg((key + j) mod 2**32),  k = (word >> 16*half) & 0xffff
+      word = pcg((key + 64*t + c//2) mod 2**32),  k = (word >> 16*(c % 2)) & 0xffff
 
 * xi = k * 2**-16 - 1/2, which lies in [-1/2, 1/2) and is exact in float32.
+* The counter names (token, channel) only, as the pages' definition does:
+  the key and the value at the same (token, channel) are quantized with the
+  same draw.  Each tensor's residual keeps the subtractive-dither properties
+  (uniform, independent of that tensor's input); Tier B concerns keys only.
 
 t is the token's 0-based logical position in its sequence, c the channel
-(0..127).  Positions up to 2**26 keep j inside 32 bits.
+(0..127).  Positions up to 2**26 keep the counter inside 32 bits.
 
 Pins (tests/test_oracle_dither.py): the hash is a bijection on 32-bit words
 (checked on a sampled range), the draws are uniform (KS and chi-square),
@@ -53,40 +55,34 @@ def pcg(v):
     return int(out) if scalar else out.astype(np.uint32)
 
 
-def stream_key(seed, layer, kv_head, stream):
-    """32-bit key of one dither stream (stream 0 = keys, 1 = values)."""
+def stream_key(seed, layer, kv_head):
+    """32-bit key of the dither of one (sequence, layer, KV head)."""
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     k = pcg(seed >> 32)
     k = pcg(k ^ (seed & 0xFFFFFFFF))
     k = pcg(k ^ (int(layer) & 0xFFFFFFFF))
-    k = pcg(k ^ ((2 * int(kv_head) + int(stream)) & 0xFFFFFFFF))
-    return k
+    return pcg(k ^ (int(kv_head) & 0xFFFFFFFF))
 
 
-def dither_k16(seed, layer, kv_head, stream, t, c):
+def dither_k16(seed, layer, kv_head, t, c):
     """16-bit draw k for positions t and channels c (broadcast arrays)."""
-    key = stream_key(seed, layer, kv_head, stream)
+    key = stream_key(seed, layer, kv_head)
     t = np.asarray(t, dtype=np.int64)
     c = np.asarray(c, dtype=np.int64)
-    if stream == 0:
-        j = 64 * t + (c >> 1)
-        half = c & 1
-    else:
-        j = 128 * (t >> 1) + c
-        half = t & 1
-    j = (np.int64(key) + j) & 0xFFFFFFFF
+    j = (np.int64(key) + 64 * t + (c >> 1)) & 0xFFFFFFFF
     word = pcg(j.astype(np.uint64)).astype(np.uint64)
-    return ((word >> (np.uint64(16) * half.astype(np.uint64))) & np.uint64(0xFFFF)).astype(np.uint16)
+    half = (c & 1).astype(np.uint64)
+    return ((word >> (np.uint64(16) * half)) & np.uint64(0xFFFF)).astype(np.uint16)
 
 
-def dither_xi(seed, layer, kv_head, stream, t, c):
+def dither_xi(seed, layer, kv_head, t, c):
     """Dither xi = k * 2**-16 - 1/2 as float32 (exact) for positions t, channels c."""
-    k = dither_k16(seed, layer, kv_head, stream, t, c).astype(np.float64)
+    k = dither_k16(seed, layer, kv_head, t, c).astype(np.float64)
     return (k * 2.0 ** -16 - 0.5).astype(np.float32)
 
 
-def dither_rows(seed, layer, kv_head, stream, positions, d=128):
+def dither_rows(seed, layer, kv_head, positions, d=128):
     """xi for every channel of the given token positions: float32 [n, d]."""
     t = np.asarray(positions, dtype=np.int64)[:, None]
     c = np.arange(d, dtype=np.int64)[None, :]
-    return dither_xi(seed, layer, kv_head, stream, t, c)
+    return dither_xi(seed, layer, kv_head, t, c)

@@ -66,8 +66,7 @@ def gather_rows(arr, layer, pt_row, S, g):
 def oracle_int8_cache(k32, v32, seed, layer, g, S):
     """Oracle write of one (sequence, KV head): codes, scales, dequantized, witness."""
     pos = np.arange(S)
-    xk = dither.dither_rows(seed, layer, g, 0, pos)
-    xv = dither.dither_rows(seed, layer, g, 1, pos)
+    xk = xv = dither.dither_rows(seed, layer, g, pos)
     ck, sk, _ = quant.dither_int8(k32, xk)
     cv, sv, _ = quant.dither_int8(v32, xv)
     khat = quant.dequant_dither_int8(ck, sk, xk)

@@ -36,26 +36,25 @@ def test_pcg_hand_evaluation():
 def test_xi_range_and_grid():
     t = np.arange(512)[:, None]
     c = np.arange(128)[None, :]
-    for stream in (0, 1):
-        xi = dither.dither_xi(99, 3, 1, stream, t, c).astype(np.float64)
-        assert xi.min() >= -0.5 and xi.max() < 0.5
-        k = (xi + 0.5) * 65536
-        assert np.all(k == np.round(k))
+    xi = dither.dither_xi(99, 3, 1, t, c).astype(np.float64)
+    assert xi.min() >= -0.5 and xi.max() < 0.5
+    k = (xi + 0.5) * 65536
+    assert np.all(k == np.round(k))
 
 
 def test_deterministic_regeneration():
-    a = dither.dither_rows(7, 2, 3, 0, np.arange(100, 164))
-    b = dither.dither_rows(7, 2, 3, 0, np.arange(100, 164))
+    a = dither.dither_rows(7, 2, 3, np.arange(100, 164))
+    b = dither.dither_rows(7, 2, 3, np.arange(100, 164))
     assert np.array_equal(a, b)
-    c = dither.dither_rows(8, 2, 3, 0, np.arange(100, 164))
+    c = dither.dither_rows(8, 2, 3, np.arange(100, 164))
     assert not np.array_equal(a, c)
 
 
-@pytest.mark.parametrize("stream", [0, 1])
-def test_uniformity(stream):
+@pytest.mark.parametrize("seed", [2024, 2 ** 63 + 5])
+def test_uniformity(seed):
     t = np.arange(4096)[:, None]
     c = np.arange(128)[None, :]
-    k = dither.dither_k16(2024, 5, 2, stream, t, c).astype(np.int64).ravel()
+    k = dither.dither_k16(seed, 5, 2, t, c).astype(np.int64).ravel()
     xi = k / 65536.0 - 0.5
     ks = stats.kstest(xi + 0.5, "uniform")
     assert ks.pvalue > 1e-3
@@ -68,16 +67,16 @@ def test_uniformity(stream):
     assert abs(xi.var() - 1 / 12) < 4 * np.sqrt((1 / 80 - 1 / 144) / n)
 
 
-@pytest.mark.parametrize("stream", [0, 1])
-def test_no_correlation_between_neighbours(stream):
+@pytest.mark.parametrize("layer", [0, 17])
+def test_no_correlation_between_neighbours(layer):
     t = np.arange(2048)[:, None]
     c = np.arange(128)[None, :]
-    xi = dither.dither_xi(11, 0, 0, stream, t, c).astype(np.float64)
+    xi = dither.dither_xi(11, layer, 0, t, c).astype(np.float64)
     n = xi.size
     lim = 5 / np.sqrt(n)
-    for a, b in [(xi[:, 0::2], xi[:, 1::2]),     # channel pairs (same word for keys)
+    for a, b in [(xi[:, 0::2], xi[:, 1::2]),     # channel pairs (same hash word)
                  (xi[:, :-1], xi[:, 1:]),        # adjacent channels
-                 (xi[0::2], xi[1::2]),           # token pairs (same word for values)
+                 (xi[0::2], xi[1::2]),           # token pairs
                  (xi[:-1], xi[1:])]:             # adjacent tokens
         r = np.corrcoef(a.ravel(), b.ravel())[0, 1]
         assert abs(r) < lim
@@ -87,10 +86,10 @@ def test_no_correlation_between_neighbours(stream):
     assert stats.chisquare(cnt).pvalue > 1e-3
 
 
-def test_streams_heads_layers_differ():
+def test_seeds_heads_layers_differ():
     t = np.arange(64)[:, None]
     c = np.arange(128)[None, :]
-    base = dither.dither_k16(5, 1, 1, 0, t, c)
-    for args in [(5, 1, 1, 1), (5, 1, 2, 0), (5, 2, 1, 0), (6, 1, 1, 0)]:
+    base = dither.dither_k16(5, 1, 1, t, c)
+    for args in [(5, 1, 2), (5, 2, 1), (6, 1, 1), (5 + 2 ** 32, 1, 1)]:
         other = dither.dither_k16(*args, t, c)
         assert np.mean(base == other) < 0.01

@@ -18,8 +18,7 @@ def _cache(S, seed, d=128, scale=1.0):
     rng = np.random.default_rng(seed)
     k = (rng.standard_normal((S, d)) * scale).astype(np.float32)
     v = rng.standard_normal((S, d)).astype(np.float32)
-    xi_k = dither.dither_rows(seed, 0, 0, 0, np.arange(S))
-    xi_v = dither.dither_rows(seed, 0, 0, 1, np.arange(S))
+    xi_k = xi_v = dither.dither_rows(seed, 0, 0, np.arange(S))
     ck, sk, _ = quant.dither_int8(k, xi_k)
     cv, sv, _ = quant.dither_int8(v, xi_v)
     khat = quant.dequant_dither_int8(ck, sk, xi_k)
@@ -93,7 +92,7 @@ def test_tier_b_variance_proxy_is_exact_variance():
     errs = []
     sk = None
     for seed in range(R):
-        xi = dither.dither_rows(10_000 + seed, 0, 0, 0, np.arange(S))
+        xi = dither.dither_rows(10_000 + seed, 0, 0, np.arange(S))
         c, s, _ = quant.dither_int8(k, xi)
         khat = quant.dequant_dither_int8(c, s, xi)
         errs.append(SM * q @ (khat - k).T)
@@ -115,7 +114,7 @@ def test_tier_b_violation_rate(delta):
     log_term = math.log(2 * S / delta)
     viol = 0
     for seed in range(R):
-        xi = dither.dither_rows(50_000 + seed, 0, 0, 0, np.arange(S))
+        xi = dither.dither_rows(50_000 + seed, 0, 0, np.arange(S))
         c, s, _ = quant.dither_int8(k, xi)
         khat = quant.dequant_dither_int8(c, s, xi)
         eps = np.abs(SM * q @ (khat - k).T)

@@ -17,7 +17,7 @@ def test_dither_error_bounded_by_half_step():
     # Subtractive dither: x^ - x = s (round(y + xi) - (y + xi)) with y = x/s,
     # so |x^ - x| <= s/2 up to the float32 rounding of y.
     x = _rows(2000)
-    xi = dither.dither_rows(3, 0, 0, 0, np.arange(2000))
+    xi = dither.dither_rows(3, 0, 0, np.arange(2000))
     code, s, inv = quant.dither_int8(x, xi)
     xhat = quant.dequant_dither_int8(code, s, xi)
     err = np.abs(xhat - x)
@@ -28,7 +28,7 @@ def test_dither_residual_is_uniform_and_independent_of_input():
     # Classical subtractive-dither theory: e = (x^ - x)/s ~ U[-1/2, 1/2],
     # independent of x.  Tier B's proxy varsigma^2 uses its variance 1/12.
     x = _rows(4000, seed=1)
-    xi = dither.dither_rows(4, 0, 0, 0, np.arange(4000))
+    xi = dither.dither_rows(4, 0, 0, np.arange(4000))
     code, s, _ = quant.dither_int8(x, xi)
     e = ((quant.dequant_dither_int8(code, s, xi) - x) / s[:, None]).ravel()
     n = e.size
@@ -49,7 +49,7 @@ def test_zero_dither_is_round_to_nearest():
 def test_scale_definition_and_zero_row():
     x = _rows(8, seed=3)
     x[2] = 0.0
-    xi = dither.dither_rows(1, 0, 0, 0, np.arange(8))
+    xi = dither.dither_rows(1, 0, 0, np.arange(8))
     code, s, inv = quant.dither_int8(x, xi)
     am = np.max(np.abs(x), axis=1)
     assert np.all(s[am > 0] == (am[am > 0] / np.float32(127)).astype(np.float32))
