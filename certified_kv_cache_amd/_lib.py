@@ -10,7 +10,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwitcert.so")
+# WITCERT_LIB may name another build of the same library (A/B timing runs)
+LIB_PATH = os.environ.get("WITCERT_LIB") or os.path.join(_HERE, "libwitcert.so")
 
 WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
 WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2 = 0, 1, 2
@@ -50,7 +51,7 @@ def _load():
         "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P],
         "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
-        "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
+        "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -186,6 +187,5 @@ def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, h
         _ptr(rho_fx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def wc_dither_fill(seed, layer, kv_head, stream_kv, pos0, n_pos, out, stream=None):
-    _check("wc_dither_fill", lib.wc_dither_fill(int(seed), layer, kv_head, stream_kv, pos0, n_pos, _ptr(out),
-                                                _stream(stream)))
+def wc_dither_fill(seed, layer, kv_head, pos0, n_pos, out, stream=None):
+    _check("wc_dither_fill", lib.wc_dither_fill(int(seed), layer, kv_head, pos0, n_pos, _ptr(out), _stream(stream)))

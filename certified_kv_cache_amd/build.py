@@ -4,7 +4,9 @@
 
 The library is compiled with -ffp-contract=off (the write path must agree bit
 for bit with a float32 replay; every intended fused multiply-add is an
-explicit fmaf) and with packed fp32 VALU instructions disabled.
+explicit fmaf), with packed fp32 VALU instructions disabled, and with MFMA
+accumulators in ordinary VGPRs (the decode's output accumulators are also
+rescaled by VALU code; the AGPR form copied them on every page).
 """
 import os
 import shutil
@@ -29,12 +31,13 @@ def command(out=LIB, extra=()):
     srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), *extra, "-o", out, *srcs]
 
 
-def build(verbose=False):
-    cmd = command()
-    tmp = LIB + ".tmp"
+def build(verbose=False, out=LIB, extra=()):
+    cmd = command(out, extra)
+    tmp = out + ".tmp"
     cmd[cmd.index("-o") + 1] = tmp
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,8 +45,8 @@ def build(verbose=False):
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

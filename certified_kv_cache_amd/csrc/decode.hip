@@ -53,10 +53,9 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // fp16 bit pattern 0x64XX is 1024 + XX exactly.
 constexpr uint32_t kMagic = 0x64646464u;
 
-// Four int8 codes (two's complement, one word) -> two fp16 pairs of the exact
-// integers: bias to unsigned, splice under the 1024 exponent, subtract 1152.
-__device__ __forceinline__ void codes_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const uint32_t u = w ^ 0x80808080u;
+// Four INT8 codes stored as offset binary (code + 128, one word) -> two fp16
+// pairs of the exact integers: splice under the 1024 exponent, subtract 1152.
+__device__ __forceinline__ void codes_to_h(uint32_t u, uint32_t& lo, uint32_t& hi) {
   const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   lo = as_u32(as_h2(perm(kMagic, u, 0x04010400u)) - bias);
   hi = as_u32(as_h2(perm(kMagic, u, 0x04030402u)) - bias);
@@ -83,6 +82,22 @@ __device__ __forceinline__ uint32_t fp8x2_to_h(uint32_t b01) {
 __device__ __forceinline__ void fp8_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
   lo = fp8x2_to_h(perm(0u, w, 0x010C000Cu));  // bytes: 0, w0, 0, w1
   hi = fp8x2_to_h(perm(0u, w, 0x030C020Cu));  // bytes: 0, w2, 0, w3
+}
+
+// Reductions over the four lanes n, n^16, n^32, n^48 (one head's k groups)
+// with the gfx950 row-swap permutes: VALU only, no LDS round trip.  Each swap
+// returns the lane's own value and its partner's, in some order.
+__device__ __forceinline__ float max4k(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum4k(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 __device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -114,19 +129,25 @@ struct DecodeArgs {
   float neg_log_dloc;   // -log(delta_loc)
 };
 
-// One page of one wave: the 16 tokens' codes, scales and witness for the
-// lane's share, loaded one page ahead of its use.
-struct PageLoad {
-  uint4 k0, k1, v0, v1;   // key codes (token n, 32 channels); value codes (8 channels x 4 tokens)
-  float4 ks, vs;          // key / value scales of tokens 4k..4k+3
-  float2 w;               // witness bands 2k, 2k+1 of token n
+// One page of one wave, keys: the lane's 32 key codes of token n, the key
+// scales of tokens 4k..4k+3, the witness bands 2k, 2k+1 of token n.
+struct KLoad {
+  uint4 k0, k1;
+  float4 ks;
+  float2 w;
   int slot;               // exact-pool slot (-1 = quantized)
   int64_t pg;             // page-head block index
 };
+// Values: 8 channels x 4 tokens of codes and the value scales of tokens
+// 4k..4k+3.  Both are loaded one page ahead of their use.
+struct VLoad {
+  uint4 v0, v1;
+  float4 vs;
+};
 
 template <int SCHEME>
-__device__ __forceinline__ void load_page(const wc_cache& c, const DecodeArgs& a, int b, int g, int jj, int n, int kq,
-                                          bool meterA, PageLoad& d) {
+__device__ __forceinline__ void load_k(const wc_cache& c, const DecodeArgs& a, int b, int g, int jj, int n, int kq,
+                                       bool meterA, KLoad& d) {
   const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
   d.pg = ((int64_t)a.layer * c.num_pages + phys) * c.num_kv_heads + g;
   d.slot = c.exact_slot ? c.exact_slot[d.pg] : -1;
@@ -134,17 +155,21 @@ __device__ __forceinline__ void load_page(const wc_cache& c, const DecodeArgs& a
                                                    n * 128 + 32 * kq);
   d.k0 = kp[0];
   d.k1 = kp[1];
-  const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.v_codes) + d.pg * 2048 +
+  d.ks = SCHEME == WC_DITHER_INT8 ? *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq)
+                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+  d.w = meterA ? *reinterpret_cast<const float2*>(c.witness + (d.pg * 16 + n) * 8 + 2 * kq) : make_float2(0.f, 0.f);
+}
+
+template <int SCHEME>
+__device__ __forceinline__ VLoad load_v(const wc_cache& c, int64_t pg, int n, int kq) {
+  VLoad d;
+  const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.v_codes) + pg * 2048 +
                                                    kq * 512 + 32 * n);
   d.v0 = vp[0];
   d.v1 = vp[1];
-  if (SCHEME == WC_DITHER_INT8) {
-    d.ks = *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq);
-    d.vs = *reinterpret_cast<const float4*>(c.v_scale + d.pg * 16 + 4 * kq);
-  } else {
-    d.ks = d.vs = make_float4(1.f, 1.f, 1.f, 1.f);
-  }
-  d.w = meterA ? *reinterpret_cast<const float2*>(c.witness + (d.pg * 16 + n) * 8 + 2 * kq) : make_float2(0.f, 0.f);
+  d.vs = SCHEME == WC_DITHER_INT8 ? *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq)
+                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+  return d;
 }
 
 // expm1 for c >= 0: series below 2^-5, else 2^(c log2 e) - 1 on v_exp_f32.
@@ -162,8 +187,14 @@ __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
 // exceeds it by more than 8 (log2 units), so exp2 weights stay <= 256.
 constexpr float kRescaleSlack = 8.0f;
 
+// Minimum workgroups per CU the register allocation must allow (4 waves
+// each): 2 keeps the decode free of spills.
+#ifndef WC_DECODE_MIN_BLOCKS
+#define WC_DECODE_MIN_BLOCKS 2
+#endif
+
 template <int SCHEME, bool QF32>
-__global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
+__global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kq = lane >> 4;
@@ -260,18 +291,20 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
   // Tier A operands of the two fp32 MFMAs: K slot k <-> bands 2k and 2k+1
   const float bA0 = hv ? beta[2 * kq] : 0.0f, bA1 = hv ? beta[2 * kq + 1] : 0.0f;
   const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // log2-unit logit per raw unit
-  // raw = Dc - 2^-8 (Dh - 1152 sum q') - 2^-16 (Dl - 1024 sum q'): K-side dither
-  // bytes enter the MFMA as 1024 + byte, the bias is removed here.
-  const float qbias = qsum * (1152.0f * 0.00390625f + 1024.0f * 1.52587890625e-05f);
+  // the high and low dither bytes enter the key MFMAs as 1152 + h and
+  // 1024 + l; scaled by -2^-8 and -2^-16 their bias is -qsum (4.5 + 2^-6)
+  const float qbias = qsum * 4.515625f;
   const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
   const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
-  uint32_t keyK = 0, keyV = 0;
-  if (SCHEME == WC_DITHER_INT8) {
-    const uint64_t sd = a.seed[b];
-    keyK = stream_key(sd, (uint32_t)a.layer, (uint32_t)g, 0u);
-    keyV = stream_key(sd, (uint32_t)a.layer, (uint32_t)g, 1u);
-  }
+  const uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(a.seed[b], (uint32_t)a.layer, (uint32_t)g) : 0u;
+  // Per-wave LDS tile of the page's dither bytes as fp16 operands: the key
+  // side (lane = token) hashes each draw once and stores [token][8-channel
+  // group]; the value side (lane = channel group) reads four tokens back.
+  // The same bytes alias the end-of-split combine buffer.
+  __shared__ __align__(16) uint4 smem[kNW * 2 * 16 * 16];
+  uint4 (*sH)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 2 * 256);
+  uint4 (*sL)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 2 * 256 + 256);
 
   // ---------------------------------------------------------------- state
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
@@ -279,22 +312,40 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) O[t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  PageLoad cur, nxt;
-  int jj = p0 + wave;
-  if (jj < p1) load_page<SCHEME>(c, a, b, g, jj, n, kq, meterA, cur);
-  for (; jj < p1; jj += kNW) {
-    if (jj + kNW < p1) load_page<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt);
+  // one page of this wave; the loop below alternates two prefetch buffers
+  const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  float vbias = 0.0f;                          // 1024 * sum of the value low-byte weights fed to the MFMA
+  auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int jj) {
+    if (jj + kNW < p1) {                       // next page, one page ahead of its use
+      load_k<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt);
+      vnxt = load_v<SCHEME>(c, nxt.pg, n, kq);
+    }
     const int tok0 = jj * 16;
     const bool exact = cur.slot >= 0;
+    const bool full = tok0 + 16 <= S;          // wave-uniform: only the last page is ragged
 
-    // ---------------- QK^T
-    f4 Dc = {0.f, 0.f, 0.f, 0.f}, Dh = Dc, Dl = Dc;
+    // ---------------- QK^T: three MFMA chains over 128 channels
+    f4 Dc = zero4, Dh = zero4, Dl = zero4;
     float st[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
-    if (!exact) {
-      const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
-      const uint32_t base = keyK + (uint32_t)(64 * (tok0 + n) + 16 * kq);
+    float kbias = 0.0f;
+    const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
+    const uint32_t base = key + (uint32_t)(64 * (tok0 + n) + 16 * kq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      uint32_t hh[4], ll[4];
+      if (SCHEME == WC_DITHER_INT8) {
+        // draws of token n, channels 32k + 8j .. +7: 1024 + high byte (= 1152 + h)
+        // and 1024 + low byte, as fp16 pairs; the values reuse them from LDS
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
+          hh[e] = perm(kMagic, wd, 0x04030401u);
+          ll[e] = perm(kMagic, wd, 0x04020400u);
+        }
+        sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+        sL[n][4 * kq + j] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+      }
+      if (!exact) {
         uint32_t c0, c1, c2, c3;
         if (SCHEME == WC_DITHER_INT8) {
           codes_to_h(kw[2 * j], c0, c1);
@@ -304,60 +355,66 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
           fp8_to_h(kw[2 * j + 1], c2, c3);
         }
         const h8 Ac = make_h8(c0, c1, c2, c3);
-        Dc = mfma32(Ac, Qhi[j], Dc);
+        const h8 Qh = Qhi[j];
+        Dc = mfma32(Ac, Qh, j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ac, Qlo[j], Dc);
         if (SCHEME == WC_DITHER_INT8) {
-          uint32_t hh[4], ll[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
-            hh[e] = perm(kMagic, wd, 0x04030401u);   // 1024 + high bytes
-            ll[e] = perm(kMagic, wd, 0x04020400u);   // 1024 + low bytes
-          }
           const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
           const h8 Al = make_h8(ll[0], ll[1], ll[2], ll[3]);
-          Dh = mfma32(Ah, Qhi[j], Dh);
-          Dl = mfma32(Al, Qhi[j], Dl);
+          Dh = mfma32(Ah, Qh, j == 0 ? zero4 : Dh);
+          Dl = mfma32(Al, Qh, j == 0 ? zero4 : Dl);
           if (QF32) {
-            Dh = mfma32(Ah, Qlo[j], Dh);
-            Dl = mfma32(Al, Qlo[j], Dl);
+            const h8 Ql = Qlo[j];
+            Dh = mfma32(Ah, Ql, Dh);
+            Dl = mfma32(Al, Ql, Dl);
           }
         }
       }
+    }
+    if (!exact) {
+      if (SCHEME == WC_DITHER_INT8) kbias = qbias;
     } else {
       const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 v = xp[j];
         const h8 Ax = make_h8(v.x, v.y, v.z, v.w);
-        Dc = mfma32(Ax, Qhi[j], Dc);
+        Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
       }
       const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
       st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
     }
     // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs
-    f4 Da = {0.f, 0.f, 0.f, 0.f};
-    if (meterA && !exact) {
-      Da = mfma_f32(cur.w.x, bA0, Da);
-      Da = mfma_f32(cur.w.y, bA1, Da);
-    }
+    f4 Da = zero4;
+    if (meterA && !exact) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
+    // raw = sum q' (code - h 2^-8 - l 2^-16); kbias cancels the byte biases
     float l2[4];
-    bool valid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float raw = Dc[r];
-      if (SCHEME == WC_DITHER_INT8 && !exact)
-        raw = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw + qbias));
-      valid[r] = tok0 + 4 * kq + r < S;
-      l2[r] = valid[r] ? qs2 * st[r] * raw : -INFINITY;
+      if (SCHEME == WC_DITHER_INT8 && !exact) raw = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw + kbias));
+      l2[r] = qs2 * st[r] * raw;
+    }
+    float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
+    float cB[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cB[r] = (meterB && !exact) ? kappa * st[r] : 0.0f;
+    float sv[4] = {vl.vs.x, vl.vs.y, vl.vs.z, vl.vs.w};
+    if (!full) {                               // tokens past the end: no weight, no bound, finite scales
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = tok0 + 4 * kq + r < S;
+        l2[r] = ok ? l2[r] : -INFINITY;
+        cA[r] = ok ? cA[r] : 0.0f;
+        cB[r] = ok ? cB[r] : 0.0f;
+        sv[r] = ok ? sv[r] : 0.0f;
+      }
     }
 
     // ---------------- online softmax with lazy rescale
-    float tmax = fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3]));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float svmax = fmaxf(fmaxf(cur.vs.x, cur.vs.y), fmaxf(cur.vs.z, cur.vs.w));
+    float tmax = max4k(fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3])));
+    const float svmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     const bool move = tmax > m_ref + kRescaleSlack || (svmax > 128.0f && tmax > m_ref);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       const float m_new = move ? tmax : m_ref;
@@ -365,77 +422,120 @@ __global__ void __launch_bounds__(256) decode_kernel(wc_cache c, DecodeArgs a) {
       l_run *= alpha;
       na *= alpha;
       nb *= alpha;
+      vbias *= alpha;
 #pragma unroll
       for (int t = 0; t < 8; ++t) O[t] *= alpha;
       m_ref = m_new;
     }
-    float p[4];
-    float psum = 0.0f, ea = 0.0f, eb = 0.0f;
+    float p[4], dl[4], psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = valid[r] ? __builtin_amdgcn_exp2f(l2[r] - m_ref) : 0.0f;
+      dl[r] = l2[r] - m_ref;
+      p[r] = __builtin_amdgcn_exp2f(dl[r]);
       psum += p[r];
-      // a bound of 88 or more saturates the meter (+inf); the IEEE max also
-      // absorbs the 0 * inf of an underflowed weight
-      if (meterA) {
-        const float ca = (valid[r] && !exact) ? Da[r] : 0.0f;
-        ea += fmaxf(p[r] * expm1_fast(ca), ca >= 88.0f ? INFINITY : 0.0f);
-      }
-      if (meterB) {
-        const float cb = (valid[r] && !exact) ? kappa * st[r] : 0.0f;
-        eb += fmaxf(p[r] * expm1_fast(cb), cb >= 88.0f ? INFINITY : 0.0f);
-      }
     }
     l_run += psum;
-    na += ea;
-    nb += eb;
+    // meter terms p (e^c - 1) = 2^(l2 - m + c log2 e) - p: one exp per token, and
+    // a bound large enough to overflow saturates the meter at +inf.  A bound in
+    // (0, 2^-6) would lose relative precision to the subtraction: then the
+    // page takes the series path (wave-uniform).
+    float ea = 0.0f, eb = 0.0f;
+    if (meterA && !exact) {
+      bool tiny = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tiny |= (cA[r] > 0.0f && cA[r] < 0.015625f) || (cB[r] > 0.0f && cB[r] < 0.015625f);
+      if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ea += __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
+          if (meterB) eb += __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ea += fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
+          if (meterB) eb += fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f);
+        }
+      }
+      na += ea;
+      nb += eb;
+    }
     if (risk) {
-      float er = meterB ? eb : ea;
-      er += shfl_xor(er, 16);
-      er += shfl_xor(er, 32);
+      const float er = sum4k(meterB ? eb : ea);
       if (kq == 0 && hv)
         a.block_logrisk[((int64_t)b * a.Hq + h) * a.max_pages + jj] =
-            er > 0.0f ? logf(er) + m_ref * kLn2 : -INFINITY;
+            er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
     }
 
     // ---------------- PV: O^T += Vhat^T P^T
-    const float sv[4] = {cur.vs.x, cur.vs.y, cur.vs.z, cur.vs.w};
     _Float16 pb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pb[r] = valid[r] ? (_Float16)(p[r] * sv[r]) : (_Float16)0.0f;
+    for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(p[r] * sv[r]);
     const h4 Bc = {pb[0], pb[1], pb[2], pb[3]};
-    const h4 Bh = Bc * (_Float16)(-0.00390625f);
-    const h4 Bl = Bc * (_Float16)(-1.52587890625e-05f);
-    const uint32_t vw[8] = {cur.v0.x, cur.v0.y, cur.v0.z, cur.v0.w, cur.v1.x, cur.v1.y, cur.v1.z, cur.v1.w};
-    const uint32_t vbase = keyV + (uint32_t)(128 * ((tok0 + 4 * kq) >> 1) + 8 * n);
+    const uint32_t vw[8] = {vl.v0.x, vl.v0.y, vl.v0.z, vl.v0.w, vl.v1.x, vl.v1.y, vl.v1.z, vl.v1.w};
+    if (SCHEME == WC_DITHER_INT8) {
+      const h4 Bh = Bc * (_Float16)(-0.00390625f);
+      const h4 Bl = Bc * (_Float16)(-1.52587890625e-05f);
+      vbias += 1024.0f * (((float)Bl[0] + (float)Bl[1]) + ((float)Bl[2] + (float)Bl[3]));
+      // the draws of tokens 4k..4k+3, channels 8n..8n+7 written by the key side
+      __builtin_amdgcn_wave_barrier();
+      const uint4 H0 = sH[4 * kq][n], H1 = sH[4 * kq + 1][n], H2 = sH[4 * kq + 2][n], H3 = sH[4 * kq + 3][n];
+      const uint4 L0 = sL[4 * kq][n], L1 = sL[4 * kq + 1][n], L2 = sL[4 * kq + 2][n], L3 = sL[4 * kq + 3][n];
+      const uint32_t h0w[4] = {H0.x, H0.y, H0.z, H0.w}, h1w[4] = {H1.x, H1.y, H1.z, H1.w};
+      const uint32_t h2w[4] = {H2.x, H2.y, H2.z, H2.w}, h3w[4] = {H3.x, H3.y, H3.z, H3.w};
+      const uint32_t l0w[4] = {L0.x, L0.y, L0.z, L0.w}, l1w[4] = {L1.x, L1.y, L1.z, L1.w};
+      const uint32_t l2w[4] = {L2.x, L2.y, L2.z, L2.w}, l3w[4] = {L3.x, L3.y, L3.z, L3.w};
+      const h2 b1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint32_t c0, c1;
-      if (SCHEME == WC_DITHER_INT8)
+      for (int t = 0; t < 8; ++t) {
+        // channel 8n + t: half (t % 2) of word t / 2 of each token's group
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        const int w = t >> 1;
+        uint32_t c0, c1;
         codes_to_h(vw[t], c0, c1);
-      else
+        const uint32_t ha = as_u32(as_h2(perm(h1w[w], h0w[w], sel)) - b1152);
+        const uint32_t hb = as_u32(as_h2(perm(h3w[w], h2w[w], sel)) - b1152);
+        const uint32_t la = perm(l1w[w], l0w[w], sel), lb = perm(l3w[w], l2w[w], sel);   // 1024 + l
+        O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
+        O[t] = mfma16(make_h4(ha, hb), Bh, O[t]);
+        O[t] = mfma16(make_h4(la, lb), Bl, O[t]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        uint32_t c0, c1;
         fp8_to_h(vw[t], c0, c1);
-      O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
-      if (SCHEME == WC_DITHER_INT8) {
-        uint32_t hh0, ll0, hh1, ll1;
-        draw_to_h(pcg(vbase + (uint32_t)t), hh0, ll0);
-        draw_to_h(pcg(vbase + 128u + (uint32_t)t), hh1, ll1);
-        O[t] = mfma16(make_h4(hh0, hh1), Bh, O[t]);
-        O[t] = mfma16(make_h4(ll0, ll1), Bl, O[t]);
+        O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
       }
     }
-    cur = nxt;
+  };
+  KLoad kA, kB;
+  VLoad vA, vB;
+  int jj = p0 + wave;
+  if (jj < p1) {
+    load_k<SCHEME>(c, a, b, g, jj, n, kq, meterA, kA);
+    vA = load_v<SCHEME>(c, kA.pg, n, kq);
+  }
+  while (jj < p1) {
+    page(kA, vA, kB, vB, jj);
+    jj += kNW;
+    if (jj >= p1) break;
+    page(kB, vB, kA, vA, jj);
+    jj += kNW;
   }
   const float m_run = m_ref;
+  if (SCHEME == WC_DITHER_INT8) {
+    const float vb = sum4k(vbias);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) O[t] -= vb;
+  }
 
   // ---------------------------------------------------------------- combine waves
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
-  na += shfl_xor(na, 16);
-  na += shfl_xor(na, 32);
-  nb += shfl_xor(nb, 16);
-  nb += shfl_xor(nb, 32);
-  __shared__ float sO[kNW][16][128];
+  l_run = sum4k(l_run);
+  na = sum4k(na);
+  nb = sum4k(nb);
+  __syncthreads();                             // the dither tiles are reused below
+  float (*sO)[16][128] = reinterpret_cast<float (*)[16][128]>(smem);
   __shared__ float sM[kNW][16][4];
 #pragma unroll
   for (int t = 0; t < 8; ++t)

@@ -21,19 +21,19 @@ __host__ __device__ __forceinline__ uint32_t pcg(uint32_t v) {
   return (word >> 22u) ^ word;
 }
 
-// 32-bit key of one dither stream (stream 0 = keys, 1 = values), chained
-// from the 64-bit sequence seed, the layer and the KV head.
-__host__ __device__ __forceinline__ uint32_t stream_key(uint64_t seed, uint32_t layer,
-                                                        uint32_t kv_head, uint32_t stream) {
+// 32-bit key of the dither of one (sequence, layer, KV head), chained from
+// the 64-bit sequence seed, the layer and the KV head.
+__host__ __device__ __forceinline__ uint32_t stream_key(uint64_t seed, uint32_t layer, uint32_t kv_head) {
   uint32_t k = pcg((uint32_t)(seed >> 32));
   k = pcg(k ^ (uint32_t)seed);
   k = pcg(k ^ layer);
-  return pcg(k ^ (2u * kv_head + stream));
+  return pcg(k ^ kv_head);
 }
 
-// Key words: j = 64 t + c/2 (low half = even channel).
-// Value words: j = 128 (t/2) + c (low half = even token).
-// xi = k * 2^-16 - 1/2 with k the 16-bit half of pcg(key + j).
+// One draw per (token t, channel c), shared by the key and the value there:
+// word j = 64 t + c/2 (low half = even channel), k = 16-bit half of
+// pcg(key + j), xi = k * 2^-16 - 1/2.  INT8 codes are stored as offset binary
+// (code + 128).
 
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -69,36 +69,28 @@ struct RowArgs {
 };
 
 // Quantize the 8 channels of one lane; returns codes packed little-endian
-// in two words and the residual r = x^ - x.
-template <int SCHEME, bool IS_V>
-__device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, uint32_t key,
-                                       int32_t p, int lane16, uint32_t (&packed)[2], float (&r)[8]) {
+// in two words (INT8: offset binary code + 128) and the residual r = x^ - x.
+// words[w] holds the draws of channels 8 lane16 + 2w (low half) and + 1.
+template <int SCHEME>
+__device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, const uint32_t (&words)[4],
+                                       uint32_t (&packed)[2], float (&r)[8]) {
   packed[0] = packed[1] = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int c = 8 * lane16 + i;
     uint32_t code;
     float xr;
     if (SCHEME == WC_DITHER_INT8) {
-      uint32_t word, k16;
-      if (!IS_V) {
-        word = pcg(key + (uint32_t)(64 * p + (c >> 1)));
-        k16 = (c & 1) ? (word >> 16) : (word & 0xFFFFu);
-      } else {
-        word = pcg(key + (uint32_t)(128 * (p >> 1) + c));
-        k16 = (p & 1) ? (word >> 16) : (word & 0xFFFFu);
-      }
-      float xi = (float)k16 * 1.52587890625e-05f - 0.5f;   // exact
+      const uint32_t k16 = (i & 1) ? (words[i >> 1] >> 16) : (words[i >> 1] & 0xFFFFu);
+      const float xi = (float)k16 * 1.52587890625e-05f - 0.5f;   // exact
       float q;
       if (s == 0.0f) {
         q = 0.0f;
       } else {
-        float y = add_rn(mul_rn(x[i], inv), xi);
+        const float y = add_rn(mul_rn(x[i], inv), xi);
         q = fminf(fmaxf(rintf(y), -128.0f), 127.0f);
       }
-      code = (uint32_t)(int32_t)q & 0xFFu;
-      xr = fmaf(s, q - xi, -x[i]);           // q - xi exact; one rounding
-      if (s == 0.0f) xr = -x[i];
+      code = (uint32_t)((int32_t)q + 128);
+      xr = s == 0.0f ? -x[i] : fmaf(s, q - xi, -x[i]);   // q - xi exact; one rounding
     } else {
       code = f32_to_e4m3(x[i]);
       xr = e4m3_to_f32(code) - x[i];
@@ -123,10 +115,15 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
   const int64_t slot = a.slot[i];
   const int64_t page = slot / 16, off = slot % 16;
   const int32_t p = a.pos[i];
-  const uint64_t seed = a.seed[i];
   const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
   const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
 
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  if (SCHEME == WC_DITHER_INT8) {
+    const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
+  }
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const bool isv = which == 1;
@@ -144,17 +141,13 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
     }
     uint32_t packed[2];
     float r[8];
-    uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(seed, (uint32_t)layer, (uint32_t)g, isv ? 1u : 0u) : 0u;
-    if (isv)
-      quant8<SCHEME, true>(x, s, inv, key, p, lane16, packed, r);
-    else
-      quant8<SCHEME, false>(x, s, inv, key, p, lane16, packed, r);
+    quant8<SCHEME>(x, s, inv, words, packed, r);
     if (!isv) {
       float ss = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
-      float tot = ss + shfl_xor(ss, 8);
-      float w = sqrtf(tot) * kWitnessGuard;
+      const float tot = ss + shfl_xor(ss, 8);
+      const float w = sqrtf(tot) * kWitnessGuard;
       if (live) {
         uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + (pg * 16 + off) * 128 + 8 * lane16;
         *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
@@ -289,20 +282,13 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
 }
 
 // ---------------------------------------------------------------- dither fill (test hook)
-__global__ void dither_fill_kernel(uint32_t key, int stream_kv, int64_t pos0, int64_t n_pos, uint16_t* out) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void dither_fill_kernel(uint32_t key, int64_t pos0, int64_t n_pos, uint16_t* out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n_pos * 128) return;
-  int64_t t = pos0 + e / 128;
-  int c = (int)(e % 128);
-  uint32_t word, k16;
-  if (stream_kv == 0) {
-    word = pcg(key + (uint32_t)(64 * t + (c >> 1)));
-    k16 = (c & 1) ? word >> 16 : word & 0xFFFFu;
-  } else {
-    word = pcg(key + (uint32_t)(128 * (t >> 1) + c));
-    k16 = (t & 1) ? word >> 16 : word & 0xFFFFu;
-  }
-  out[e] = (uint16_t)k16;
+  const int64_t t = pos0 + e / 128;
+  const int c = (int)(e % 128);
+  const uint32_t word = pcg(key + (uint32_t)(64 * t + (c >> 1)));
+  out[e] = (uint16_t)((c & 1) ? word >> 16 : word & 0xFFFFu);
 }
 
 }  // namespace wc
@@ -394,17 +380,17 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
   return WC_EUNSUPPORTED;
 }
 
-extern "C" int wc_dither_fill(uint64_t seed, int layer, int kv_head, int stream_kv, int64_t pos0, int64_t n_pos,
-                              uint16_t* out, void* stream) {
-  if (!out || n_pos < 0 || pos0 < 0 || (stream_kv != 0 && stream_kv != 1) || pos0 + n_pos > (int64_t(1) << 26)) {
+extern "C" int wc_dither_fill(uint64_t seed, int layer, int kv_head, int64_t pos0, int64_t n_pos, uint16_t* out,
+                              void* stream) {
+  if (!out || n_pos < 0 || pos0 < 0 || pos0 + n_pos > (int64_t(1) << 26)) {
     set_error("wc_dither_fill: bad arguments");
     return WC_EINVAL;
   }
   if (n_pos == 0) return WC_OK;
-  uint32_t key = stream_key(seed, (uint32_t)layer, (uint32_t)kv_head, (uint32_t)stream_kv);
-  int64_t n = n_pos * 128;
+  const uint32_t key = stream_key(seed, (uint32_t)layer, (uint32_t)kv_head);
+  const int64_t n = n_pos * 128;
   hipLaunchKernelGGL(dither_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, key,
-                     stream_kv, pos0, n_pos, out);
+                     pos0, n_pos, out);
   return check_launch("wc_dither_fill");
 }
 

@@ -31,7 +31,8 @@
  * Cache layout (one layer = `num_pages` physical pages; arrays carry a
  * leading layer dimension of `num_layers`; P = num_pages, Hkv = num_kv_heads,
  * d = 128, page = 16 tokens for INT8/fp8, 32 for 2-bit):
- *  k_codes   INT8/fp8: [L][P][Hkv][16][128] bytes, token-major.
+ *  k_codes   INT8/fp8: [L][P][Hkv][16][128] bytes, token-major; INT8 codes
+ *            are stored as offset binary (code + 128).
  *            2-bit:    [L][P][Hkv][128][8] bytes (32 tokens of one channel,
  *                      4 codes per byte, token i in bits 2(i%4)).
  *  v_codes   INT8/fp8: [L][P][Hkv][4][128][4] bytes: token t of the page at
@@ -210,11 +211,13 @@ size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages);
 
 /*
  * wc_dither_fill -- test hook: the 16-bit dither draws k (xi = k/65536 - 1/2)
- * the kernels regenerate, for positions pos0 .. pos0+n_pos-1 of one stream
- * (stream 0 = keys, 1 = values), into device uint16 out[n_pos][128].
+ * the kernels regenerate for positions pos0 .. pos0+n_pos-1 of one (sequence
+ * seed, layer, KV head), into device uint16 out[n_pos][128].  The draw is a
+ * counter hash of (seed, layer, head, token, channel) (summary, Tier B
+ * paragraph): keys and values at one (token, channel) share it.
  */
-int wc_dither_fill(uint64_t seed, int layer, int kv_head, int stream_kv, int64_t pos0, int64_t n_pos,
-                   uint16_t* out, void* stream);
+int wc_dither_fill(uint64_t seed, int layer, int kv_head, int64_t pos0, int64_t n_pos, uint16_t* out,
+                   void* stream);
 
 const char* wc_last_error(void);
 const char* wc_version(void);

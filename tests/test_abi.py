@@ -112,4 +112,5 @@ def test_merge_and_gate_reject_bad_arguments():
     assert call(mp=5000) == L.WC_EINVAL
     assert call(wsb=1) == L.WC_EWORKSPACE
     assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
-    assert L.lib.wc_dither_fill(1, 0, 0, 2, 0, 4, p, None) == L.WC_EINVAL
+    assert L.lib.wc_dither_fill(1, 0, 0, -1, 4, p, None) == L.WC_EINVAL
+    assert L.lib.wc_dither_fill(1, 0, 0, 0, 4, None, None) == L.WC_EINVAL

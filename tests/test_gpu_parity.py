@@ -26,15 +26,13 @@ def _flush(msg):
 
 
 # ---------------------------------------------------------------- dither
-@pytest.mark.parametrize("stream", [0, 1])
-def test_dither_fill_bit_exact(stream):
+def test_dither_fill_bit_exact():
     L = H.need_gpu()
     for seed, layer, head, pos0, n in [(1, 0, 0, 0, 300), (2 ** 40 + 77, 27, 3, 12345, 257), (9, 5, 1, 2 ** 25, 64)]:
         out = torch.empty((n, 128), dtype=torch.int16, device="cuda")
-        L.wc_dither_fill(seed, layer, head, stream, pos0, n, out)
+        L.wc_dither_fill(seed, layer, head, pos0, n, out)
         got = out.cpu().numpy().view(np.uint16)
-        want = dither.dither_k16(seed, layer, head, stream, np.arange(pos0, pos0 + n)[:, None],
-                                 np.arange(128)[None, :])
+        want = dither.dither_k16(seed, layer, head, np.arange(pos0, pos0 + n)[:, None], np.arange(128)[None, :])
         assert np.array_equal(got, want)
 
 
@@ -75,6 +73,8 @@ def test_write_codes_bit_exact_and_witness(scheme, dtype):
                   else H.oracle_fp8_cache(k32, v32))
             gk = H.gather_k_codes(kc, sc.layer, sc.tab[b], S, g)
             gv = H.gather_v_codes(vc, sc.layer, sc.tab[b], S, g)
+            if scheme == "int8":                   # offset binary in HBM
+                gk, gv = (gk.astype(np.int16) - 128).astype(np.int8), (gv.astype(np.int16) - 128).astype(np.int8)
             assert np.array_equal(gk.view(oc["ck"].dtype), oc["ck"]), (b, g)
             assert np.array_equal(gv.view(oc["cv"].dtype), oc["cv"]), (b, g)
             w = H.gather_rows(wt, sc.layer, sc.tab[b], S, g)
