@@ -321,7 +321,8 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
       vnxt = load_v<SCHEME>(c, nxt.pg, n, kq);
     }
     const int tok0 = jj * 16;
-    const bool exact = cur.slot >= 0;
+    // the slot is the same for every lane: keep the branches scalar
+    const bool exact = __builtin_amdgcn_readfirstlane(cur.slot) >= 0;
     const bool full = tok0 + 16 <= S;          // wave-uniform: only the last page is ragged
 
     // ---------------- QK^T: three MFMA chains over 128 channels
@@ -330,24 +331,24 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     float kbias = 0.0f;
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     const uint32_t base = key + (uint32_t)(64 * (tok0 + n) + 16 * kq);
+    // draws of token n, channels 32k + 8j .. +7, as fp16 pairs 1024 + high byte
+    // (= 1152 + h) and 1024 + low byte; published to LDS for the values
+    auto draws = [&](int j, uint32_t (&hh)[4], uint32_t (&ll)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t hh[4], ll[4];
-      if (SCHEME == WC_DITHER_INT8) {
-        // draws of token n, channels 32k + 8j .. +7: 1024 + high byte (= 1152 + h)
-        // and 1024 + low byte, as fp16 pairs; the values reuse them from LDS
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
-          hh[e] = perm(kMagic, wd, 0x04030401u);
-          ll[e] = perm(kMagic, wd, 0x04020400u);
-        }
-        sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
-        sL[n][4 * kq + j] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
+        hh[e] = perm(kMagic, wd, 0x04030401u);
+        ll[e] = perm(kMagic, wd, 0x04020400u);
       }
-      if (!exact) {
-        uint32_t c0, c1, c2, c3;
+      sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+      sL[n][4 * kq + j] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+    };
+    if (!exact) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hh[4], ll[4], c0, c1, c2, c3;
         if (SCHEME == WC_DITHER_INT8) {
+          draws(j, hh, ll);
           codes_to_h(kw[2 * j], c0, c1);
           codes_to_h(kw[2 * j + 1], c2, c3);
         } else {
@@ -355,28 +356,29 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
           fp8_to_h(kw[2 * j + 1], c2, c3);
         }
         const h8 Ac = make_h8(c0, c1, c2, c3);
-        const h8 Qh = Qhi[j];
-        Dc = mfma32(Ac, Qh, j == 0 ? zero4 : Dc);
+        Dc = mfma32(Ac, Qhi[j], j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ac, Qlo[j], Dc);
         if (SCHEME == WC_DITHER_INT8) {
           const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
           const h8 Al = make_h8(ll[0], ll[1], ll[2], ll[3]);
-          Dh = mfma32(Ah, Qh, j == 0 ? zero4 : Dh);
-          Dl = mfma32(Al, Qh, j == 0 ? zero4 : Dl);
+          Dh = mfma32(Ah, Qhi[j], j == 0 ? zero4 : Dh);
+          Dl = mfma32(Al, Qhi[j], j == 0 ? zero4 : Dl);
           if (QF32) {
-            const h8 Ql = Qlo[j];
-            Dh = mfma32(Ah, Ql, Dh);
-            Dl = mfma32(Al, Ql, Dl);
+            Dh = mfma32(Ah, Qlo[j], Dh);
+            Dl = mfma32(Al, Qlo[j], Dl);
           }
         }
       }
-    }
-    if (!exact) {
       if (SCHEME == WC_DITHER_INT8) kbias = qbias;
     } else {
+      // repaired block: exact keys from the pool; the values still need the draws
       const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        if (SCHEME == WC_DITHER_INT8) {
+          uint32_t hh[4], ll[4];
+          draws(j, hh, ll);
+        }
         const uint4 v = xp[j];
         const h8 Ax = make_h8(v.x, v.y, v.z, v.w);
         Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
@@ -441,9 +443,12 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     // page takes the series path (wave-uniform).
     float ea = 0.0f, eb = 0.0f;
     if (meterA && !exact) {
-      bool tiny = false;
+      // some bound in (0, 2^-6)?  As unsigned bits, c - 1 < 2^-6 - 1 exactly then
+      uint32_t cmin = 0xFFFFFFFFu;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tiny |= (cA[r] > 0.0f && cA[r] < 0.015625f) || (cB[r] > 0.0f && cB[r] < 0.015625f);
+      for (int r = 0; r < 4; ++r)
+        cmin = min(cmin, min(__float_as_uint(cA[r]) - 1u, __float_as_uint(cB[r]) - 1u));
+      const bool tiny = cmin < 0x3C7FFFFFu;
       if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
