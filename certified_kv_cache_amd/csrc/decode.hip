@@ -100,6 +100,18 @@ __device__ __forceinline__ float sum4k(float v) {
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
+// Row (16-lane) data movement with DPP: shift by 8 into the upper or lower
+// half of every row, or rotate by 8.
+__device__ __forceinline__ float dpp_shr8_hi(float old, float src) {   // lanes 8..15 <- lanes 0..7
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), 0x118, 0xF, 0xC, false));
+}
+__device__ __forceinline__ uint32_t dpp_shl8_lo(uint32_t old, uint32_t src) {   // lanes 0..7 <- lanes 8..15
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x108, 0xF, 0x3, false);
+}
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   uint4 u = make_uint4(a, b, c, d);
   return __builtin_bit_cast(h8, u);
@@ -145,9 +157,12 @@ struct VLoad {
   float4 vs;
 };
 
+// With a compacted softmax lane (n, k) evaluates tokens 4k + r0 and
+// 4k + r0 + 1 only (r0 = 0 for n < 8, 2 for n >= 8): its scales are a pair
+// (r0 < 0: all four tokens).
 template <int SCHEME>
 __device__ __forceinline__ void load_k(const wc_cache& c, const DecodeArgs& a, int b, int g, int jj, int n, int kq,
-                                       bool meterA, KLoad& d) {
+                                       bool meterA, KLoad& d, int r0) {
   const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
   d.pg = ((int64_t)a.layer * c.num_pages + phys) * c.num_kv_heads + g;
   d.slot = c.exact_slot ? c.exact_slot[d.pg] : -1;
@@ -155,20 +170,36 @@ __device__ __forceinline__ void load_k(const wc_cache& c, const DecodeArgs& a, i
                                                    n * 128 + 32 * kq);
   d.k0 = kp[0];
   d.k1 = kp[1];
-  d.ks = SCHEME == WC_DITHER_INT8 ? *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq)
-                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+  if (SCHEME == WC_DITHER_INT8) {
+    if (r0 < 0) {
+      d.ks = *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq);
+    } else {
+      const float2 t = *reinterpret_cast<const float2*>(c.k_scale + d.pg * 16 + 4 * kq + r0);
+      d.ks = make_float4(t.x, t.y, 0.f, 0.f);
+    }
+  } else {
+    d.ks = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
   d.w = meterA ? *reinterpret_cast<const float2*>(c.witness + (d.pg * 16 + n) * 8 + 2 * kq) : make_float2(0.f, 0.f);
 }
 
 template <int SCHEME>
-__device__ __forceinline__ VLoad load_v(const wc_cache& c, int64_t pg, int n, int kq) {
+__device__ __forceinline__ VLoad load_v(const wc_cache& c, int64_t pg, int n, int kq, int r0) {
   VLoad d;
   const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.v_codes) + pg * 2048 +
                                                    kq * 512 + 32 * n);
   d.v0 = vp[0];
   d.v1 = vp[1];
-  d.vs = SCHEME == WC_DITHER_INT8 ? *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq)
-                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+  if (SCHEME == WC_DITHER_INT8) {
+    if (r0 < 0) {
+      d.vs = *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq);
+    } else {
+      const float2 t = *reinterpret_cast<const float2*>(c.v_scale + pg * 16 + 4 * kq + r0);
+      d.vs = make_float4(t.x, t.y, 0.f, 0.f);
+    }
+  } else {
+    d.vs = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
   return d;
 }
 
@@ -193,7 +224,9 @@ constexpr float kRescaleSlack = 8.0f;
 #define WC_DECODE_MIN_BLOCKS 2
 #endif
 
-template <int SCHEME, bool QF32>
+// CMP: the query group has at most 8 heads, so the softmax and meter run
+// compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
+template <int SCHEME, bool QF32, bool CMP>
 __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -298,6 +331,12 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
   const uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(a.seed[b], (uint32_t)a.layer, (uint32_t)g) : 0u;
+  // compacted softmax: lane (n, k) evaluates head n & 7, tokens 4k + r0, +1
+  constexpr int NV = CMP ? 2 : 4;
+  const int r0 = CMP ? 2 * (n >> 3) : 0;
+  const int ld0 = CMP ? r0 : -1;              // scale-pair offset for the loads
+  const float qs2c = CMP ? dpp_shr8_hi(qs2, qs2) : qs2;
+  const float kappac = CMP ? dpp_shr8_hi(kappa, kappa) : kappa;
   // Per-wave LDS tile of the page's dither bytes as fp16 operands: the key
   // side (lane = token) hashes each draw once and stores [token][8-channel
   // group]; the value side (lane = channel group) reads four tokens back.
@@ -317,8 +356,8 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   float vbias = 0.0f;                          // 1024 * sum of the value low-byte weights fed to the MFMA
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int jj) {
     if (jj + kNW < p1) {                       // next page, one page ahead of its use
-      load_k<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt);
-      vnxt = load_v<SCHEME>(c, nxt.pg, n, kq);
+      load_k<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt, ld0);
+      vnxt = load_v<SCHEME>(c, nxt.pg, n, kq, ld0);
     }
     const int tok0 = jj * 16;
     // the slot is the same for every lane: keep the branches scalar
@@ -384,29 +423,42 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
         Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
       }
-      const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
-      st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+      if (CMP) {
+        const float2 s2 = *reinterpret_cast<const float2*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq + r0);
+        st[0] = s2.x; st[1] = s2.y;
+      } else {
+        const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
+        st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+      }
     }
     // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs
     f4 Da = zero4;
     if (meterA && !exact) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
     // raw = sum q' (code - h 2^-8 - l 2^-16); kbias cancels the byte biases
-    float l2[4];
+    float raw[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float raw = Dc[r];
-      if (SCHEME == WC_DITHER_INT8 && !exact) raw = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw + kbias));
-      l2[r] = qs2 * st[r] * raw;
+      raw[r] = Dc[r];
+      if (SCHEME == WC_DITHER_INT8 && !exact) raw[r] = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw[r] + kbias));
     }
     float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
-    float cB[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cB[r] = (meterB && !exact) ? kappa * st[r] : 0.0f;
+    if (CMP) {                                 // lanes n + 8 take tokens 2, 3 of head n
+      raw[0] = dpp_shr8_hi(raw[0], raw[2]);
+      raw[1] = dpp_shr8_hi(raw[1], raw[3]);
+      cA[0] = dpp_shr8_hi(cA[0], cA[2]);
+      cA[1] = dpp_shr8_hi(cA[1], cA[3]);
+    }
+    float l2[4], cB[4];
     float sv[4] = {vl.vs.x, vl.vs.y, vl.vs.z, vl.vs.w};
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      l2[r] = qs2c * st[r] * raw[r];
+      cB[r] = (meterB && !exact) ? kappac * st[r] : 0.0f;
+    }
     if (!full) {                               // tokens past the end: no weight, no bound, finite scales
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = tok0 + 4 * kq + r < S;
+      for (int r = 0; r < NV; ++r) {
+        const bool ok = tok0 + 4 * kq + r0 + r < S;
         l2[r] = ok ? l2[r] : -INFINITY;
         cA[r] = ok ? cA[r] : 0.0f;
         cB[r] = ok ? cB[r] : 0.0f;
@@ -415,8 +467,15 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     }
 
     // ---------------- online softmax with lazy rescale
-    float tmax = max4k(fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3])));
-    const float svmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    float tmax = fmaxf(l2[0], l2[1]);
+    float svmax = fmaxf(sv[0], sv[1]);
+    if (!CMP) {
+      tmax = fmaxf(tmax, fmaxf(l2[2], l2[3]));
+      svmax = fmaxf(svmax, fmaxf(sv[2], sv[3]));
+    } else {
+      tmax = fmaxf(tmax, dpp_ror8(tmax));
+    }
+    tmax = max4k(tmax);
     const bool move = tmax > m_ref + kRescaleSlack || (svmax > 128.0f && tmax > m_ref);
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       const float m_new = move ? tmax : m_ref;
@@ -431,7 +490,7 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     }
     float p[4], dl[4], psum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < NV; ++r) {
       dl[r] = l2[r] - m_ref;
       p[r] = __builtin_amdgcn_exp2f(dl[r]);
       psum += p[r];
@@ -446,18 +505,18 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
       // some bound in (0, 2^-6)?  As unsigned bits, c - 1 < 2^-6 - 1 exactly then
       uint32_t cmin = 0xFFFFFFFFu;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < NV; ++r)
         cmin = min(cmin, min(__float_as_uint(cA[r]) - 1u, __float_as_uint(cB[r]) - 1u));
       const bool tiny = cmin < 0x3C7FFFFFu;
       if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < NV; ++r) {
           ea += __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
           if (meterB) eb += __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r];
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < NV; ++r) {
           ea += fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
           if (meterB) eb += fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f);
         }
@@ -466,17 +525,23 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
       nb += eb;
     }
     if (risk) {
-      const float er = sum4k(meterB ? eb : ea);
+      float er = meterB ? eb : ea;
+      if (CMP) er += dpp_ror8(er);
+      er = sum4k(er);
       if (kq == 0 && hv)
         a.block_logrisk[((int64_t)b * a.Hq + h) * a.max_pages + jj] =
             er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
     }
 
     // ---------------- PV: O^T += Vhat^T P^T
-    _Float16 pb[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(p[r] * sv[r]);
-    const h4 Bc = {pb[0], pb[1], pb[2], pb[3]};
+    h4 Bc;
+    if (CMP) {                                 // tokens 2, 3 come back from lane n + 8
+      const h2 own = {(_Float16)(p[0] * sv[0]), (_Float16)(p[1] * sv[1])};
+      const uint32_t up = dpp_shl8_lo(as_u32(own), as_u32(own));
+      Bc = make_h4(as_u32(own), up);
+    } else {
+      Bc = h4{(_Float16)(p[0] * sv[0]), (_Float16)(p[1] * sv[1]), (_Float16)(p[2] * sv[2]), (_Float16)(p[3] * sv[3])};
+    }
     const uint32_t vw[8] = {vl.v0.x, vl.v0.y, vl.v0.z, vl.v0.w, vl.v1.x, vl.v1.y, vl.v1.z, vl.v1.w};
     if (SCHEME == WC_DITHER_INT8) {
       const h4 Bh = Bc * (_Float16)(-0.00390625f);
@@ -518,8 +583,8 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   VLoad vA, vB;
   int jj = p0 + wave;
   if (jj < p1) {
-    load_k<SCHEME>(c, a, b, g, jj, n, kq, meterA, kA);
-    vA = load_v<SCHEME>(c, kA.pg, n, kq);
+    load_k<SCHEME>(c, a, b, g, jj, n, kq, meterA, kA, ld0);
+    vA = load_v<SCHEME>(c, kA.pg, n, kq, ld0);
   }
   while (jj < p1) {
     page(kA, vA, kB, vB, jj);
@@ -536,6 +601,11 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   }
 
   // ---------------------------------------------------------------- combine waves
+  if (CMP) {
+    l_run += dpp_ror8(l_run);
+    na += dpp_ror8(na);
+    nb += dpp_ror8(nb);
+  }
   l_run = sum4k(l_run);
   na = sum4k(na);
   nb = sum4k(nb);
@@ -684,17 +754,22 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
                n_split, layer, meter_mask, sm_scale, (float)(-log(dloc))};
   dim3 grid((unsigned)n_split, (unsigned)c.num_kv_heads, (unsigned)B);
   hipStream_t st = (hipStream_t)stream;
+  const bool cmp = a.G <= 8;
+#define WC_LAUNCH(SCH, QF, CM) hipLaunchKernelGGL((decode_kernel<SCH, QF, CM>), grid, dim3(256), 0, st, c, a)
   if (c.scheme == WC_DITHER_INT8) {
-    if (q_dtype == WC_BF16)
-      hipLaunchKernelGGL((decode_kernel<WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<WC_DITHER_INT8, true>), grid, dim3(256), 0, st, c, a);
+    if (q_dtype == WC_BF16) {
+      if (cmp) WC_LAUNCH(WC_DITHER_INT8, false, true); else WC_LAUNCH(WC_DITHER_INT8, false, false);
+    } else {
+      if (cmp) WC_LAUNCH(WC_DITHER_INT8, true, true); else WC_LAUNCH(WC_DITHER_INT8, true, false);
+    }
   } else {
-    if (q_dtype == WC_BF16)
-      hipLaunchKernelGGL((decode_kernel<WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<WC_FP8_E4M3, true>), grid, dim3(256), 0, st, c, a);
+    if (q_dtype == WC_BF16) {
+      if (cmp) WC_LAUNCH(WC_FP8_E4M3, false, true); else WC_LAUNCH(WC_FP8_E4M3, false, false);
+    } else {
+      if (cmp) WC_LAUNCH(WC_FP8_E4M3, true, true); else WC_LAUNCH(WC_FP8_E4M3, true, false);
+    }
   }
+#undef WC_LAUNCH
   return check_launch("wc_decode_attn_meter");
 }
 

@@ -227,3 +227,17 @@ def test_block_risk_matches_oracle(scheme):
             rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
             ref = r["block_risk"]
             assert np.all(np.abs(rho - ref) <= 2e-4 * ref + 1e-30), (b, g)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (9, 1), (8, 1)])
+def test_decode_group_sizes(Hq, Hkv):
+    # groups of more than 8 query heads take the uncompacted softmax path
+    L = H.need_gpu()
+    _flush(f"decode group {Hq}/{Hkv}")
+    lens = [300, 77]
+    n = sum(lens)
+    d = inputs.layer(seed=12, S=n, Hq=Hq, Hkv=Hkv, outliers=1)
+    q = inputs.layer(seed=13, S=1, Hq=Hq, Hkv=Hkv, batch=2)["q"]
+    sc = Scenario(L.WC_DITHER_INT8, d["k"], d["v"], q, lens, "bf16", Hkv=Hkv)
+    out = sc.decode(n_split=3, mask=3)
+    _check_decode(sc, out)
