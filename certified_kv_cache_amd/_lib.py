@@ -117,8 +117,10 @@ class KVCache:
             self.v_aux = torch.zeros(shp + (32, 4, 2), **f32)
             self.k_scale = self.v_scale = None
         else:
-            self.k_codes = torch.zeros(shp + (16, 128), **u8)
-            self.v_codes = torch.zeros(shp + (4, 128, 4), **u8)
+            # [half][32-channel group][token][16 channels] and
+            # [half][token group][8-channel group][channel][token]
+            self.k_codes = torch.zeros(shp + (2, 4, 16, 16), **u8)
+            self.v_codes = torch.zeros(shp + (2, 4, 16, 4, 4), **u8)
             self.k_aux = self.v_aux = None
             if scheme == WC_DITHER_INT8:
                 self.k_scale = torch.zeros(shp + (16,), **f32)

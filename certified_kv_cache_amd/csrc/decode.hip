@@ -48,6 +48,7 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ h2 make_h2(_Float16 a, _Float16 b) { return h2{a, b}; }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // fp16 bit pattern 0x64XX is 1024 + XX exactly.
@@ -59,15 +60,6 @@ __device__ __forceinline__ void codes_to_h(uint32_t u, uint32_t& lo, uint32_t& h
   const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   lo = as_u32(as_h2(perm(kMagic, u, 0x04010400u)) - bias);
   hi = as_u32(as_h2(perm(kMagic, u, 0x04030402u)) - bias);
-}
-
-// One hash word (two 16-bit draws k0 = low half, k1 = high half) -> fp16 pair
-// of the high bytes minus 128 (h) and of the low bytes (l): k - 32768 = 256 h + l.
-__device__ __forceinline__ void draw_to_h(uint32_t w, uint32_t& hh, uint32_t& ll) {
-  const h2 b1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const h2 b1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  hh = as_u32(as_h2(perm(kMagic, w, 0x04030401u)) - b1152);
-  ll = as_u32(as_h2(perm(kMagic, w, 0x04020400u)) - b1024);
 }
 
 // Two e4m3fn bytes (byte 0 and 1 of v after the caller's permute) -> fp16
@@ -84,14 +76,30 @@ __device__ __forceinline__ void fp8_to_h(uint32_t w, uint32_t& lo, uint32_t& hi)
   hi = fp8x2_to_h(perm(0u, w, 0x030C020Cu));  // bytes: 0, w2, 0, w3
 }
 
+// Maximum of two finite-or-infinite floats as one v_max_f32: values that
+// come out of lane moves would otherwise be re-quieted first (the kernel
+// never carries NaNs).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// max(v, v of lane n ^ 8 within the row) in one DPP instruction; the nop
+// covers the wait a DPP read needs after the VALU write of its source.
+__device__ __forceinline__ float vmax_ror8(float v) {
+  float r;
+  asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // Reductions over the four lanes n, n^16, n^32, n^48 (one head's k groups)
 // with the gfx950 row-swap permutes: VALU only, no LDS round trip.  Each swap
 // returns the lane's own value and its partner's, in some order.
 __device__ __forceinline__ float max4k(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
   auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  return vmax(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float sum4k(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -111,6 +119,12 @@ __device__ __forceinline__ uint32_t dpp_shl8_lo(uint32_t old, uint32_t src) {   
 __device__ __forceinline__ float dpp_ror8(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
+
+// Identity move the optimizer cannot see through: a value loaded inside a
+// rarely taken branch is consumed there, so the wait for the load is not
+// hoisted to the join where every iteration would pay it.
+__device__ __forceinline__ int settle(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xE4, 0xF, 0xF, false); }
+__device__ __forceinline__ float settle(float v) { return __int_as_float(settle(__float_as_int(v))); }
 
 __device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   uint4 u = make_uint4(a, b, c, d);
@@ -142,65 +156,77 @@ struct DecodeArgs {
 };
 
 // One page of one wave, keys: the lane's 32 key codes of token n, the key
-// scales of tokens 4k..4k+3, the witness bands 2k, 2k+1 of token n.
+// scales of its tokens, the witness bands 2k, 2k+1 of token n.
 struct KLoad {
   uint4 k0, k1;
   float4 ks;
   float2 w;
-  int slot;               // exact-pool slot (-1 = quantized)
-  int64_t pg;             // page-head block index
+  int slot;               // exact-pool slot (-1 = quantized), wave-uniform
 };
-// Values: 8 channels x 4 tokens of codes and the value scales of tokens
-// 4k..4k+3.  Both are loaded one page ahead of their use.
+// Values: 8 channels x 4 tokens of codes and the value scales of the lane's
+// tokens.  Both are loaded one page ahead of their use.
 struct VLoad {
   uint4 v0, v1;
   float4 vs;
 };
 
+// Byte offsets of one lane inside a page-head block (fixed for the kernel):
+// the page base is wave-uniform, so every load is a scalar base plus one of
+// these 32-bit lane offsets.
+// The code layouts put lane l's 16 bytes at 16 l in each 1 KB half of a
+// page, so every code load of a wave reads 1 KB in one contiguous run.
+struct LaneOff {
+  uint32_t k;             // key codes: token n, channels 32k..32k+15 (+1 KB: 32k+16..32k+31)
+  uint32_t s;             // scales: tokens 4k (+ r0) onward
+  uint32_t w;             // witness bands 2k, 2k+1 of token n (meter off: the key codes again)
+  uint32_t v;             // value codes: channels 8n..8n+3 (+1 KB: 8n+4..8n+7), tokens 4k..4k+3
+};
+
+// Buffer resource of one page-head block (raw, untyped, 32-bit data format):
+// the base is wave-uniform and lives in SGPRs, accesses past `bytes` read 0.
+constexpr int kRsrcFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int64_t off, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + off), (short)0,
+                                           bytes, kRsrcFlags);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // With a compacted softmax lane (n, k) evaluates tokens 4k + r0 and
-// 4k + r0 + 1 only (r0 = 0 for n < 8, 2 for n >= 8): its scales are a pair
-// (r0 < 0: all four tokens).
-template <int SCHEME>
-__device__ __forceinline__ void load_k(const wc_cache& c, const DecodeArgs& a, int b, int g, int jj, int n, int kq,
-                                       bool meterA, KLoad& d, int r0) {
-  const int phys = a.page_table[(int64_t)b * a.max_pages + jj];
-  d.pg = ((int64_t)a.layer * c.num_pages + phys) * c.num_kv_heads + g;
-  d.slot = c.exact_slot ? c.exact_slot[d.pg] : -1;
-  const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.k_codes) + d.pg * 2048 +
-                                                   n * 128 + 32 * kq);
-  d.k0 = kp[0];
-  d.k1 = kp[1];
+// 4k + r0 + 1 only (r0 = 0 for n < 8, 2 for n >= 8): its scales are a pair.
+// The load count and order never depend on run-time flags, and the lane
+// offsets stay in fixed registers, so the wait for one page's data never
+// waits on the page prefetched after it.
+template <int SCHEME, bool PAIR>
+__device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const LaneOff& lo, bool meterA, KLoad& d,
+                                          VLoad& e) {
+  const __amdgpu_buffer_rsrc_t kr = page_rsrc(c.k_codes, pg * 2048, 2048);
+  const __amdgpu_buffer_rsrc_t vr = page_rsrc(c.v_codes, pg * 2048, 2048);
+  const __amdgpu_buffer_rsrc_t wr = meterA ? page_rsrc(c.witness, pg * 512, 512) : kr;
+  d.k0 = bload16(kr, lo.k);
+  d.k1 = bload16(kr, lo.k + 1024);
+  d.w = bload8(wr, lo.w);
+  e.v0 = bload16(vr, lo.v);
+  e.v1 = bload16(vr, lo.v + 1024);
   if (SCHEME == WC_DITHER_INT8) {
-    if (r0 < 0) {
-      d.ks = *reinterpret_cast<const float4*>(c.k_scale + d.pg * 16 + 4 * kq);
-    } else {
-      const float2 t = *reinterpret_cast<const float2*>(c.k_scale + d.pg * 16 + 4 * kq + r0);
+    const __amdgpu_buffer_rsrc_t ksr = page_rsrc(c.k_scale, pg * 64, 64);
+    const __amdgpu_buffer_rsrc_t vsr = page_rsrc(c.v_scale, pg * 64, 64);
+    if (PAIR) {
+      const float2 t = bload8(ksr, lo.s), u = bload8(vsr, lo.s);
       d.ks = make_float4(t.x, t.y, 0.f, 0.f);
+      e.vs = make_float4(u.x, u.y, 0.f, 0.f);
+    } else {
+      d.ks = __builtin_bit_cast(float4, bload16(ksr, lo.s));
+      e.vs = __builtin_bit_cast(float4, bload16(vsr, lo.s));
     }
   } else {
     d.ks = make_float4(1.f, 1.f, 1.f, 1.f);
+    e.vs = make_float4(1.f, 1.f, 1.f, 1.f);
   }
-  d.w = meterA ? *reinterpret_cast<const float2*>(c.witness + (d.pg * 16 + n) * 8 + 2 * kq) : make_float2(0.f, 0.f);
-}
-
-template <int SCHEME>
-__device__ __forceinline__ VLoad load_v(const wc_cache& c, int64_t pg, int n, int kq, int r0) {
-  VLoad d;
-  const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(c.v_codes) + pg * 2048 +
-                                                   kq * 512 + 32 * n);
-  d.v0 = vp[0];
-  d.v1 = vp[1];
-  if (SCHEME == WC_DITHER_INT8) {
-    if (r0 < 0) {
-      d.vs = *reinterpret_cast<const float4*>(c.v_scale + pg * 16 + 4 * kq);
-    } else {
-      const float2 t = *reinterpret_cast<const float2*>(c.v_scale + pg * 16 + 4 * kq + r0);
-      d.vs = make_float4(t.x, t.y, 0.f, 0.f);
-    }
-  } else {
-    d.vs = make_float4(1.f, 1.f, 1.f, 1.f);
-  }
-  return d;
 }
 
 // expm1 for c >= 0: series below 2^-5, else 2^(c log2 e) - 1 on v_exp_f32.
@@ -218,18 +244,23 @@ __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
 // exceeds it by more than 8 (log2 units), so exp2 weights stay <= 256.
 constexpr float kRescaleSlack = 8.0f;
 
-// Minimum workgroups per CU the register allocation must allow (4 waves
-// each): 2 keeps the decode free of spills.
-#ifndef WC_DECODE_MIN_BLOCKS
-#define WC_DECODE_MIN_BLOCKS 2
+// Minimum workgroups per CU (4 waves each) the register allocation must
+// allow: three for bf16 queries (168 registers, no spills), two for fp32
+// queries (their split query operand needs more).
+#ifndef WC_DECODE_MIN_BLOCKS_FIT
+#define WC_DECODE_MIN_BLOCKS_FIT 3
 #endif
+template <int SCHEME, bool QF32, bool CMP>
+constexpr int decode_min_blocks() {
+  return !QF32 ? WC_DECODE_MIN_BLOCKS_FIT : 2;
+}
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 template <int SCHEME, bool QF32, bool CMP>
-__global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_cache c, DecodeArgs a) {
+__global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>())) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
   const int G = a.G;
   const int h = g * G + n;                     // query head of lane column n
@@ -334,16 +365,19 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   // compacted softmax: lane (n, k) evaluates head n & 7, tokens 4k + r0, +1
   constexpr int NV = CMP ? 2 : 4;
   const int r0 = CMP ? 2 * (n >> 3) : 0;
-  const int ld0 = CMP ? r0 : -1;              // scale-pair offset for the loads
+  LaneOff lo;
+  lo.k = (uint32_t)(16 * lane);
+  lo.s = (uint32_t)(4 * (4 * kq + r0));
+  lo.w = meterA ? (uint32_t)(4 * (8 * n + 2 * kq)) : lo.k;
+  lo.v = (uint32_t)(16 * lane);
   const float qs2c = CMP ? dpp_shr8_hi(qs2, qs2) : qs2;
   const float kappac = CMP ? dpp_shr8_hi(kappa, kappa) : kappa;
-  // Per-wave LDS tile of the page's dither bytes as fp16 operands: the key
-  // side (lane = token) hashes each draw once and stores [token][8-channel
-  // group]; the value side (lane = channel group) reads four tokens back.
-  // The same bytes alias the end-of-split combine buffer.
+  // Per-wave LDS tile of the page's dither high bytes as fp16 operands
+  // (1024 + byte): the key side (lane = token) hashes each draw once and
+  // stores [token][8-channel group]; the value side (lane = channel group)
+  // reads four tokens back.  The space is the end-of-split combine buffer.
   __shared__ __align__(16) uint4 smem[kNW * 2 * 16 * 16];
-  uint4 (*sH)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 2 * 256);
-  uint4 (*sL)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 2 * 256 + 256);
+  uint4 (*sH)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 256);
 
   // ---------------------------------------------------------------- state
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
@@ -353,15 +387,34 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
 
   // one page of this wave; the loop below alternates two prefetch buffers
   const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  float vbias = 0.0f;                          // 1024 * sum of the value low-byte weights fed to the MFMA
-  auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int jj) {
-    if (jj + kNW < p1) {                       // next page, one page ahead of its use
-      load_k<SCHEME>(c, a, b, g, jj + kNW, n, kq, meterA, nxt, ld0);
-      vnxt = load_v<SCHEME>(c, nxt.pg, n, kq, ld0);
-    }
+  float vsum = 0.0f;                           // sum of the value weights p s fed to the MFMA
+  // Page i of this wave is page p0 + wave + 4 i of the split.  Its physical
+  // page and exact-pool slot come from lane i % 64 of a batch read once per
+  // 64 pages, so the loop never waits on a page-table read.
+  const int npw = p1 - p0 > wave ? (p1 - p0 - wave + kNW - 1) / kNW : 0;
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int64_t pg_base = (int64_t)a.layer * c.num_pages;
+  int bphys = 0, bslot = -1;
+  auto batch = [&](int i0) {
+    const int i = i0 + lane;
+    const int ph = i < npw ? ptab[p0 + wave + kNW * i] : 0;
+    const int sl = (i < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
+    bphys = settle(ph);                        // the wait for these stays in this rare branch
+    bslot = settle(sl);
+  };
+  auto fetch = [&](int i, KLoad& d, VLoad& e) {
+    if ((i & 63) == 0) batch(i);
+    const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
+    d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
+    load_page<SCHEME, CMP>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
+  };
+  auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
+    // next page, one page ahead of its use; the last page loads itself again
+    // so that every iteration issues the same loads
+    fetch(min(i + 1, npw - 1), nxt, vnxt);
+    const int jj = p0 + wave + kNW * i;
     const int tok0 = jj * 16;
-    // the slot is the same for every lane: keep the branches scalar
-    const bool exact = __builtin_amdgcn_readfirstlane(cur.slot) >= 0;
+    const bool exact = cur.slot >= 0;          // wave-uniform
     const bool full = tok0 + 16 <= S;          // wave-uniform: only the last page is ragged
 
     // ---------------- QK^T: three MFMA chains over 128 channels
@@ -380,7 +433,6 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
         ll[e] = perm(kMagic, wd, 0x04020400u);
       }
       sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
-      sL[n][4 * kq + j] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
     };
     if (!exact) {
 #pragma unroll
@@ -423,12 +475,13 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
         Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
       }
+      // (settled here so that the wait for this load stays in this branch)
       if (CMP) {
         const float2 s2 = *reinterpret_cast<const float2*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq + r0);
-        st[0] = s2.x; st[1] = s2.y;
+        st[0] = settle(s2.x); st[1] = settle(s2.y);
       } else {
         const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
-        st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+        st[0] = settle(s4.x); st[1] = settle(s4.y); st[2] = settle(s4.z); st[3] = settle(s4.w);
       }
     }
     // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs
@@ -467,13 +520,13 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     }
 
     // ---------------- online softmax with lazy rescale
-    float tmax = fmaxf(l2[0], l2[1]);
-    float svmax = fmaxf(sv[0], sv[1]);
+    float tmax = vmax(l2[0], l2[1]);
+    float svmax = vmax(sv[0], sv[1]);
     if (!CMP) {
-      tmax = fmaxf(tmax, fmaxf(l2[2], l2[3]));
-      svmax = fmaxf(svmax, fmaxf(sv[2], sv[3]));
+      tmax = vmax(tmax, vmax(l2[2], l2[3]));
+      svmax = vmax(svmax, vmax(sv[2], sv[3]));
     } else {
-      tmax = fmaxf(tmax, dpp_ror8(tmax));
+      tmax = vmax_ror8(tmax);
     }
     tmax = max4k(tmax);
     const bool move = tmax > m_ref + kRescaleSlack || (svmax > 128.0f && tmax > m_ref);
@@ -483,7 +536,7 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
       l_run *= alpha;
       na *= alpha;
       nb *= alpha;
-      vbias *= alpha;
+      vsum *= alpha;
 #pragma unroll
       for (int t = 0; t < 8; ++t) O[t] *= alpha;
       m_ref = m_new;
@@ -544,31 +597,33 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
     }
     const uint32_t vw[8] = {vl.v0.x, vl.v0.y, vl.v0.z, vl.v0.w, vl.v1.x, vl.v1.y, vl.v1.z, vl.v1.w};
     if (SCHEME == WC_DITHER_INT8) {
-      const h4 Bh = Bc * (_Float16)(-0.00390625f);
-      const h4 Bl = Bc * (_Float16)(-1.52587890625e-05f);
-      vbias += 1024.0f * (((float)Bl[0] + (float)Bl[1]) + ((float)Bl[2] + (float)Bl[3]));
+      // Vhat = s (code - (h - 128) 2^-8 - l 2^-16): one 16x16x32 MFMA per channel
+      // tile takes the four codes and the four exact (128 - h) / 256 of the
+      // lane's tokens against P^T twice over; the low byte l enters through its
+      // mean 255/2 (its spread moves an output by < 2^-9 of one code step).
+      const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      vsum = __builtin_amdgcn_fdot2(make_h2(Bc[0], Bc[1]), ones, vsum, false);
+      vsum = __builtin_amdgcn_fdot2(make_h2(Bc[2], Bc[3]), ones, vsum, false);
+      const h8 B2 = make_h8(as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])),
+                            as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])));
       // the draws of tokens 4k..4k+3, channels 8n..8n+7 written by the key side
       __builtin_amdgcn_wave_barrier();
       const uint4 H0 = sH[4 * kq][n], H1 = sH[4 * kq + 1][n], H2 = sH[4 * kq + 2][n], H3 = sH[4 * kq + 3][n];
-      const uint4 L0 = sL[4 * kq][n], L1 = sL[4 * kq + 1][n], L2 = sL[4 * kq + 2][n], L3 = sL[4 * kq + 3][n];
       const uint32_t h0w[4] = {H0.x, H0.y, H0.z, H0.w}, h1w[4] = {H1.x, H1.y, H1.z, H1.w};
       const uint32_t h2w[4] = {H2.x, H2.y, H2.z, H2.w}, h3w[4] = {H3.x, H3.y, H3.z, H3.w};
-      const uint32_t l0w[4] = {L0.x, L0.y, L0.z, L0.w}, l1w[4] = {L1.x, L1.y, L1.z, L1.w};
-      const uint32_t l2w[4] = {L2.x, L2.y, L2.z, L2.w}, l3w[4] = {L3.x, L3.y, L3.z, L3.w};
-      const h2 b1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+      const h2 km = {(_Float16)-0.00390625f, (_Float16)-0.00390625f};
+      const h2 kb = {(_Float16)4.5f, (_Float16)4.5f};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        // channel 8n + t: half (t % 2) of word t / 2 of each token's group
+        // channel 8n + t: half (t % 2) of word t / 2 of each token's group;
+        // (1024 + h) (-2^-8) + 4.5 = (128 - h) / 256 exactly
         const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
         const int w = t >> 1;
         uint32_t c0, c1;
         codes_to_h(vw[t], c0, c1);
-        const uint32_t ha = as_u32(as_h2(perm(h1w[w], h0w[w], sel)) - b1152);
-        const uint32_t hb = as_u32(as_h2(perm(h3w[w], h2w[w], sel)) - b1152);
-        const uint32_t la = perm(l1w[w], l0w[w], sel), lb = perm(l3w[w], l2w[w], sel);   // 1024 + l
-        O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
-        O[t] = mfma16(make_h4(ha, hb), Bh, O[t]);
-        O[t] = mfma16(make_h4(la, lb), Bl, O[t]);
+        const uint32_t ha = as_u32(__builtin_elementwise_fma(as_h2(perm(h1w[w], h0w[w], sel)), km, kb));
+        const uint32_t hb = as_u32(__builtin_elementwise_fma(as_h2(perm(h3w[w], h2w[w], sel)), km, kb));
+        O[t] = mfma32(make_h8(c0, c1, ha, hb), B2, O[t]);
       }
     } else {
 #pragma unroll
@@ -581,21 +636,15 @@ __global__ void __launch_bounds__(256, WC_DECODE_MIN_BLOCKS) decode_kernel(wc_ca
   };
   KLoad kA, kB;
   VLoad vA, vB;
-  int jj = p0 + wave;
-  if (jj < p1) {
-    load_k<SCHEME>(c, a, b, g, jj, n, kq, meterA, kA, ld0);
-    vA = load_v<SCHEME>(c, kA.pg, n, kq, ld0);
-  }
-  while (jj < p1) {
-    page(kA, vA, kB, vB, jj);
-    jj += kNW;
-    if (jj >= p1) break;
-    page(kB, vB, kA, vA, jj);
-    jj += kNW;
+  if (npw > 0) fetch(0, kA, vA);
+  for (int i = 0; i < npw; i += 2) {
+    page(kA, vA, kB, vB, i);
+    if (i + 1 >= npw) break;
+    page(kB, vB, kA, vA, i + 1);
   }
   const float m_run = m_ref;
-  if (SCHEME == WC_DITHER_INT8) {
-    const float vb = sum4k(vbias);
+  if (SCHEME == WC_DITHER_INT8) {                // the low bytes' mean 255/2 times 2^-16
+    const float vb = sum4k(vsum) * 0.0019454956054688f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) O[t] -= vb;
   }

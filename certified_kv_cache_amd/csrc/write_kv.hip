@@ -149,15 +149,20 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
       const float tot = ss + shfl_xor(ss, 8);
       const float w = sqrtf(tot) * kWitnessGuard;
       if (live) {
-        uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + (pg * 16 + off) * 128 + 8 * lane16;
+        // channels 8 lane16 .. +7 of token off: half (lane16 % 4) / 2, 32-channel
+        // group lane16 / 4, bytes 8 (lane16 % 2) .. of the token's 16-byte chunk
+        uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 2048 + ((lane16 & 3) >> 1) * 1024 +
+                      (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
         *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
         if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = w;
         if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.k_scale[pg * 16 + off] = s;
       }
     } else if (live) {
-      uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 512 + (off & 3);
+      // channel 8 lane16 + k of token off: half k / 4, token group off / 4,
+      // channel group lane16, word k % 4, byte off % 4
+      uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) vc[(8 * lane16 + k) * 4] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
+      for (int k = 0; k < 8; ++k) vc[(k >> 2) * 1024 + (k & 3) * 4] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
       if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.v_scale[pg * 16 + off] = s;
     }
   }

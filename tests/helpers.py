@@ -45,16 +45,19 @@ def slots_for(page_table, ctx_lens, page_size=16):
 
 
 def gather_k_codes(kc, layer, pt_row, S, g):
-    """[S, 128] key codes of one sequence and KV head from [L][P][Hkv][16][128]."""
-    t = np.arange(S)
-    return kc[layer, pt_row[t // 16], g, t % 16]
+    """[S, 128] key codes of one sequence and KV head from [L][P][Hkv][2][4][16][16]:
+    token t, channel c at [(c % 32) // 16][c // 32][t % 16][c % 16]."""
+    t = np.arange(S)[:, None]
+    c = np.arange(128)[None, :]
+    return kc[layer, pt_row[t // 16], g, (c % 32) // 16, c // 32, t % 16, c % 16]
 
 
 def gather_v_codes(vc, layer, pt_row, S, g):
-    """[S, 128] value codes from [L][P][Hkv][4][128][4]."""
-    t = np.arange(S)
-    blk = vc[layer, pt_row[t // 16], g]          # [S, 4, 128, 4]
-    return blk[np.arange(S), (t % 16) // 4, :, t % 4]
+    """[S, 128] value codes from [L][P][Hkv][2][4][16][4][4]: token t, channel c
+    at [(c % 8) // 4][(t % 16) // 4][c // 8][c % 4][t % 4]."""
+    t = np.arange(S)[:, None]
+    c = np.arange(128)[None, :]
+    return vc[layer, pt_row[t // 16], g, (c % 8) // 4, (t % 16) // 4, c // 8, c % 4, t % 4]
 
 
 def gather_rows(arr, layer, pt_row, S, g):
