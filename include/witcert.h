@@ -31,13 +31,15 @@
  * Cache layout (one layer = `num_pages` physical pages; arrays carry a
  * leading layer dimension of `num_layers`; P = num_pages, Hkv = num_kv_heads,
  * d = 128, page = 16 tokens for INT8/fp8, 32 for 2-bit):
- *  k_codes   INT8/fp8: [L][P][Hkv][16][128] bytes, token-major; INT8 codes
- *            are stored as offset binary (code + 128).
+ *  k_codes   INT8/fp8: [L][P][Hkv][2][4][16][16] bytes per page-head
+ *            block: token t, channel c at [(c%32)/16][c/32][t][c%16] (each
+ *            1 KB half holds, for every token, 16 channels of each 32-channel
+ *            group).  INT8 codes are stored as offset binary (code + 128).
  *            2-bit:    [L][P][Hkv][128][8] bytes (32 tokens of one channel,
  *                      4 codes per byte, token i in bits 2(i%4)).
- *  v_codes   INT8/fp8: [L][P][Hkv][4][128][4] bytes: token t of the page at
- *                      ((t/4)*128 + c)*4 + t%4 (four tokens of one channel
- *                      are one 32-bit word).
+ *  v_codes   INT8/fp8: [L][P][Hkv][2][4][16][4][4] bytes: token t, channel c
+ *                      at [(c%8)/4][t/4][c/8][c%4][t%4] (four tokens of one
+ *                      channel are one 32-bit word).
  *            2-bit:    [L][P][Hkv][32][32] bytes (token-major, 4 codes/byte).
  *  k_scale,
  *  v_scale   INT8: fp32 [L][P][Hkv][16], s = absmax/127 of the row.
