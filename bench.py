@@ -204,6 +204,7 @@ def main():
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
     t_on2 = time_decode(decode, iters, mask=3, with_risk=False)
     t_on = min(t_on, t_on2)
+    t_risk = time_decode(decode, iters, mask=3, with_risk=True)
     bytes_on = decode_bytes(B, S, True)
     ach = bytes_on / (dec_step_us * 1e-6) / 1e9
     traffic = None
@@ -222,7 +223,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_GBS, 4), "traffic": traffic},
         "decode_us": round(dec_step_us, 2), "decode_meter_on_us": round(t_on, 2),
-        "decode_meter_off_us": round(t_off, 2), "meter_overhead": round(t_on / t_off - 1, 4),
+        "decode_meter_off_us": round(t_off, 2), "decode_meter_risk_us": round(t_risk, 2),
+        "meter_overhead": round(t_on / t_off - 1, 4),
         "pct_peak": round(100 * ach / PEAK_GBS, 2),
         "kv_tokens_per_s": round(B * S / (dec_step_us * 1e-6), 1),
         "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),

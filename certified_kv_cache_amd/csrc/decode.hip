@@ -247,18 +247,18 @@ constexpr float kRescaleSlack = 8.0f;
 // Minimum workgroups per CU (4 waves each) the register allocation must
 // allow: three for bf16 queries (168 registers, no spills), two for fp32
 // queries (their split query operand needs more).
-#ifndef WC_DECODE_MIN_BLOCKS_FIT
-#define WC_DECODE_MIN_BLOCKS_FIT 3
+#ifndef WC_DECODE_MIN_BLOCKS_BF16
+#define WC_DECODE_MIN_BLOCKS_BF16 3
 #endif
-template <int SCHEME, bool QF32, bool CMP>
+template <bool QF32>
 constexpr int decode_min_blocks() {
-  return !QF32 ? WC_DECODE_MIN_BLOCKS_FIT : 2;
+  return QF32 ? 2 : WC_DECODE_MIN_BLOCKS_BF16;
 }
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 template <int SCHEME, bool QF32, bool CMP>
-__global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>())) decode_kernel(wc_cache c, DecodeArgs a) {
+__global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
@@ -378,6 +378,8 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
   // reads four tokens back.  The space is the end-of-split combine buffer.
   __shared__ __align__(16) uint4 smem[kNW * 2 * 16 * 16];
   uint4 (*sH)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 256);
+  __shared__ float sRisk[kNW][16][16];
+  float (*sR)[16] = sRisk[wave];
 
   // ---------------------------------------------------------------- state
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
@@ -388,16 +390,19 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
   // one page of this wave; the loop below alternates two prefetch buffers
   const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
   float vsum = 0.0f;                           // sum of the value weights p s fed to the MFMA
-  // Page i of this wave is page p0 + wave + 4 i of the split.  Its physical
-  // page and exact-pool slot come from lane i % 64 of a batch read once per
-  // 64 pages, so the loop never waits on a page-table read.
-  const int npw = p1 - p0 > wave ? (p1 - p0 - wave + kNW - 1) / kNW : 0;
+  // Each wave takes a contiguous quarter of the split's pages: page i of
+  // this wave is page w0 + i.  Its physical page and exact-pool slot come
+  // from lane i % 64 of a batch read once per 64 pages, so the loop never
+  // waits on a page-table read.
+  const int per = (p1 - p0 + kNW - 1) / kNW;
+  const int w0 = p0 + wave * per;
+  const int npw = max(0, min(p1, w0 + per) - w0);
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int64_t pg_base = (int64_t)a.layer * c.num_pages;
   int bphys = 0, bslot = -1;
   auto batch = [&](int i0) {
     const int i = i0 + lane;
-    const int ph = i < npw ? ptab[p0 + wave + kNW * i] : 0;
+    const int ph = i < npw ? ptab[w0 + i] : 0;
     const int sl = (i < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
     bphys = settle(ph);                        // the wait for these stays in this rare branch
     bslot = settle(sl);
@@ -412,10 +417,16 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
     // next page, one page ahead of its use; the last page loads itself again
     // so that every iteration issues the same loads
     fetch(min(i + 1, npw - 1), nxt, vnxt);
-    const int jj = p0 + wave + kNW * i;
+    const int jj = w0 + i;
     const int tok0 = jj * 16;
     const bool exact = cur.slot >= 0;          // wave-uniform
     const bool full = tok0 + 16 <= S;          // wave-uniform: only the last page is ragged
+
+    // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs, issued first
+    // so that their latency hides behind the key work (zeroed below for a
+    // repaired block)
+    f4 Da = zero4;
+    if (meterA) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
 
     // ---------------- QK^T: three MFMA chains over 128 channels
     f4 Dc = zero4, Dh = zero4, Dl = zero4;
@@ -483,10 +494,18 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
         const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
         st[0] = settle(s4.x); st[1] = settle(s4.y); st[2] = settle(s4.z); st[3] = settle(s4.w);
       }
+      Da = zero4;
     }
-    // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs
-    f4 Da = zero4;
-    if (meterA && !exact) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
+    // the value side's draws (tokens 4k..4k+3, channels 8n..8n+7), read back
+    // now so that the LDS latency hides behind the softmax
+    uint4 H0, H1, H2, H3;
+    if (SCHEME == WC_DITHER_INT8) {
+      __builtin_amdgcn_wave_barrier();
+      H0 = sH[4 * kq][n];
+      H1 = sH[4 * kq + 1][n];
+      H2 = sH[4 * kq + 2][n];
+      H3 = sH[4 * kq + 3][n];
+    }
     // raw = sum q' (code - h 2^-8 - l 2^-16); kbias cancels the byte biases
     float raw[4];
 #pragma unroll
@@ -578,12 +597,12 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
       nb += eb;
     }
     if (risk) {
+      // block risks go through a per-wave LDS tile [head][16 pages] and out
+      // as 16-page runs of each head's row
       float er = meterB ? eb : ea;
       if (CMP) er += dpp_ror8(er);
       er = sum4k(er);
-      if (kq == 0 && hv)
-        a.block_logrisk[((int64_t)b * a.Hq + h) * a.max_pages + jj] =
-            er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
+      if (kq == 0 && n < G) sR[n][i & 15] = er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
     }
 
     // ---------------- PV: O^T += Vhat^T P^T
@@ -606,9 +625,6 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
       vsum = __builtin_amdgcn_fdot2(make_h2(Bc[2], Bc[3]), ones, vsum, false);
       const h8 B2 = make_h8(as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])),
                             as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])));
-      // the draws of tokens 4k..4k+3, channels 8n..8n+7 written by the key side
-      __builtin_amdgcn_wave_barrier();
-      const uint4 H0 = sH[4 * kq][n], H1 = sH[4 * kq + 1][n], H2 = sH[4 * kq + 2][n], H3 = sH[4 * kq + 3][n];
       const uint32_t h0w[4] = {H0.x, H0.y, H0.z, H0.w}, h1w[4] = {H1.x, H1.y, H1.z, H1.w};
       const uint32_t h2w[4] = {H2.x, H2.y, H2.z, H2.w}, h3w[4] = {H3.x, H3.y, H3.z, H3.w};
       const h2 km = {(_Float16)-0.00390625f, (_Float16)-0.00390625f};
@@ -632,6 +648,20 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<SCHEME, QF32, CMP>()))
         fp8_to_h(vw[t], c0, c1);
         O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
       }
+    }
+    if (risk && ((i & 15) == 15 || i == npw - 1)) {
+      __builtin_amdgcn_wave_barrier();
+      // the lane index is laundered so that no per-lane address of this rare
+      // flush is hoisted out of the loop (it would hold registers throughout)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int i0 = i & ~15, cnt = (i & 15) + 1, pj = ln & 15;
+      float* rrow = a.block_logrisk + ((int64_t)b * a.Hq + g * G) * a.max_pages + w0 + i0;
+      for (int q4 = 0; q4 < G; q4 += 4) {
+        const int hn = (ln >> 4) + q4;
+        if (hn < G && pj < cnt) rrow[(int64_t)hn * a.max_pages + pj] = sR[hn][pj];
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   };
   KLoad kA, kB;

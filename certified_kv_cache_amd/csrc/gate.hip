@@ -32,7 +32,7 @@ struct GateArgs {
   const float* lse;
   const int32_t* page_table;
   const int32_t* ctx_len;
-  uint64_t* fx;           // [B][Hq][max_pages]
+  uint64_t* fx;           // [B][Hq][max_pages], optional copy for the caller
   int32_t* sel;           // [B][Hkv][max_pages]
   int32_t* count;         // [B][Hkv]
   int32_t* base;          // [B][Hkv]
@@ -52,47 +52,62 @@ __device__ __forceinline__ uint64_t risk_fx(float logrisk, float lse) {
   return u > kFxCap ? kFxCap : u;
 }
 
-__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  const uint64_t r = red[0];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
 }
 
 __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a) {
   __shared__ uint64_t keys[kMaxSortPages];
   __shared__ uint64_t red[256];
+  __shared__ uint64_t hsum[16];
+  __shared__ float hlse[16];
+  __shared__ uint8_t rep[kMaxSortPages];
   __shared__ int kneed;
   const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
   const int hkv = c.num_kv_heads;
   const int S = a.ctx_len[b];
   const int P = (S + 15) >> 4;
   const int G = a.G;
-  // fixed-point risks of every (head, block), repaired blocks forced to 0
-  uint64_t xmax = 0;
-  for (int n = 0; n < G; ++n) {
-    const int h = g * G + n;
-    const float l = a.lse[b * a.Hq + h];
-    uint64_t part = 0;
-    for (int j = t; j < a.max_pages; j += 256) {
-      uint64_t v = 0;
-      if (j < P) {
-        const int phys = a.page_table[(int64_t)b * a.max_pages + j];
-        const int64_t pg = ((int64_t)a.layer * c.num_pages + phys) * hkv + g;
-        const bool rep = c.exact_slot[pg] >= 0;
-        v = rep ? 0 : risk_fx(a.logrisk[((int64_t)b * a.Hq + h) * a.max_pages + j], l);
-      }
-      a.fx[((int64_t)b * a.Hq + h) * a.max_pages + j] = v;
-      part += v;
+  const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;   // head n's row: row0 + n * max_pages
+  if (t < 16) {
+    hsum[t] = 0;
+    hlse[t] = t < G ? a.lse[b * a.Hq + g * G + t] : 0.0f;
+  }
+  // repaired blocks (exact keys in the pool) carry no risk
+  for (int j = t; j < P; j += 256) {
+    const int phys = a.page_table[(int64_t)b * a.max_pages + j];
+    rep[j] = c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] >= 0;
+  }
+  __syncthreads();
+  auto fx_of = [&](int n, int j) -> uint64_t {
+    return rep[j] ? 0 : risk_fx(a.logrisk[row0 + (int64_t)n * a.max_pages + j], hlse[n]);
+  };
+  // X_h = sum_j rho_fx(h, j): every page's loads of all heads are in flight
+  // together, then one wave reduction and one LDS add per head and wave
+  uint64_t part[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) part[n] = 0;
+  for (int j = t; j < P; j += 256) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      if (n < G) part[n] += fx_of(n, j);
+  }
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    if (n < G) {
+      const uint64_t v = wave_sum_u64(part[n]);
+      if ((t & 63) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(&hsum[n]), (unsigned long long)v);
     }
-    const uint64_t X = block_sum_u64(part, red);
-    xmax = X > xmax ? X : xmax;
+  }
+  __syncthreads();
+  uint64_t xmax = 0;
+  for (int n = 0; n < G; ++n) xmax = hsum[n] > xmax ? hsum[n] : xmax;
+  if (a.fx) {                                   // optional copy of every rho_fx for the caller
+    for (int n = 0; n < G; ++n)
+      for (int j = t; j < a.max_pages; j += 256)
+        a.fx[row0 + (int64_t)n * a.max_pages + j] = j < P ? fx_of(n, j) : 0;
   }
   if (t == 0) a.count[b * hkv + g] = 0;
   if (xmax <= a.T || P == 0) return;                     // uniform across the workgroup
@@ -106,7 +121,7 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
     if (j < P) {
       uint64_t m = 0;
       for (int n = 0; n < G; ++n) {
-        const uint64_t v = a.fx[((int64_t)b * a.Hq + g * G + n) * a.max_pages + j];
+        const uint64_t v = fx_of(n, j);
         m = v > m ? v : m;
       }
       k = m ? (m << 16) | (uint64_t)(65535 - j) : 0;
@@ -136,11 +151,10 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   const int per = (P + 255) / 256;
   const int i0 = t * per, i1 = min(P, i0 + per);
   for (int n = 0; n < G; ++n) {
-    const int64_t row = ((int64_t)b * a.Hq + g * G + n) * a.max_pages;
     uint64_t mine = 0;
     for (int i = i0; i < i1; ++i) {
       const uint64_t k = keys[i];
-      if (k) mine += a.fx[row + (65535 - (int)(k & 0xFFFF))];
+      if (k) mine += fx_of(n, 65535 - (int)(k & 0xFFFF));
     }
     // exclusive scan of the per-thread sums (Hillis-Steele in LDS)
     red[t] = mine;
@@ -160,7 +174,7 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
       const uint64_t k = keys[i];
       if (!k) break;
       if (pre < need) ++cnt;
-      pre += a.fx[row + (65535 - (int)(k & 0xFFFF))];
+      pre += fx_of(n, 65535 - (int)(k & 0xFFFF));
     }
     red[t] = (uint64_t)cnt;
     __syncthreads();
@@ -273,10 +287,9 @@ __global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, 
 using namespace wc;
 
 extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
-  (void)0;
   if (B < 0 || Hkv < 0 || max_pages < 0) return 0;
-  // fx is sized with 16 query heads per KV head (the maximum group)
-  return (size_t)B * Hkv * 16 * max_pages * 8 + (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 4 * 4;
+  // selected block indices, then count / base / take per (sequence, KV head)
+  return (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 3 * 4;
 }
 
 extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse, int B,
@@ -321,8 +334,7 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
   }
   const int hkv = c.num_kv_heads;
   char* ws = (char*)workspace;
-  uint64_t* fx = rho_fx ? rho_fx : (uint64_t*)ws;
-  ws += (size_t)B * hkv * 16 * max_pages * 8;
+  uint64_t* fx = rho_fx;
   int32_t* sel = (int32_t*)ws;
   ws += (size_t)B * hkv * max_pages * 4;
   int32_t* cnt = (int32_t*)ws;
