@@ -191,3 +191,4 @@ def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, h
 
 def wc_dither_fill(seed, layer, kv_head, pos0, n_pos, out, stream=None):
     _check("wc_dither_fill", lib.wc_dither_fill(int(seed), layer, kv_head, pos0, n_pos, _ptr(out), _stream(stream)))
+

@@ -165,6 +165,7 @@ int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_
 /* Bytes of the decode workspace: B * Hq * n_split * 132 * 4. */
 size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
 
+
 /*
  * wc_lse_merge -- merge KV-split partials by log-sum-exp (output and
  * certificate together; summary implementation paragraph and paperswithlean
