@@ -724,29 +724,64 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
 }
 
 // ---------------------------------------------------------------- LSE merge
-// One wave per (b, h): lanes take two output channels each.
+// One wave per (b, h).  Lanes take the splits for the maxima and the scalar
+// sums (wave reductions), then two output channels each with the split loop
+// unrolled so that its loads are in flight together.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += shfl_xor(v, m);
+  return v;
+}
+
 __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ part, int n_split, float* o,
                                                    float* lse, float* meter_a, float* meter_b) {
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* pp = part + (int64_t)bh * n_split * kPartial;
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[s * kPartial]);
-  float L = 0.f, NA = 0.f, NB = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float* q = pp + s * kPartial;
-      const float ms = q[0];
-      const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-      L = fmaf(w, q[1], L);
-      NA = fmaf(w, q[2], NA);
-      NB = fmaf(w, q[3], NB);
-      o0 = fmaf(w, q[4 + 2 * lane], o0);
-      o1 = fmaf(w, q[5 + 2 * lane], o1);
+  for (int s = lane; s < n_split; s += 64) M = fmaxf(M, pp[s * kPartial]);
+  M = wave_max(M);
+  auto weight = [&](float ms) { return (ms == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(ms - M); };
+  float L = 0.f, NA = 0.f, NB = 0.f;
+  for (int s = lane; s < n_split; s += 64) {
+    const float4 q = *reinterpret_cast<const float4*>(pp + s * kPartial);
+    const float w = weight(q.x);
+    L = fmaf(w, q.y, L);
+    NA = fmaf(w, q.z, NA);
+    NB = fmaf(w, q.w, NB);
+  }
+  L = wave_sum(L);
+  NA = wave_sum(NA);
+  NB = wave_sum(NB);
+  float o0 = 0.f, o1 = 0.f;
+  int s = 0;
+  for (; s + 8 <= n_split; s += 8) {
+    float mw[8];
+    float2 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      mw[k] = pp[(s + k) * kPartial];
+      v[k] = *reinterpret_cast<const float2*>(pp + (s + k) * kPartial + 4 + 2 * lane);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = weight(mw[k]);
+      o0 = fmaf(w, v[k].x, o0);
+      o1 = fmaf(w, v[k].y, o1);
     }
   }
+  for (; s < n_split; ++s) {
+    const float w = weight(pp[s * kPartial]);
+    const float2 v = *reinterpret_cast<const float2*>(pp + s * kPartial + 4 + 2 * lane);
+    o0 = fmaf(w, v.x, o0);
+    o1 = fmaf(w, v.y, o1);
+  }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  o[(int64_t)bh * 128 + 2 * lane] = o0 * inv;
-  o[(int64_t)bh * 128 + 2 * lane + 1] = o1 * inv;
+  *reinterpret_cast<float2*>(o + (int64_t)bh * 128 + 2 * lane) = make_float2(o0 * inv, o1 * inv);
   if (lane == 0) {
     lse[bh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
     const float ea = NA * inv, eb = NB * inv;

@@ -11,12 +11,14 @@
 // turned into 40-bit fixed point so every decision is integer arithmetic
 // and does not depend on summation order.
 //
-// Kernels: (1) per (sequence, KV head): fixed-point risks, trigger test,
-// bitonic sort of the candidates by risk in LDS, per-head scans for the
-// shortest sufficient prefix; (2) one workgroup: exclusive scan of the counts
-// in (sequence, head) order hands out exact-pool slots deterministically;
-// (3) copy each selected block from pinned host memory (zero-copy reads),
-// store it as fp16 with a per-token power of two, zero its witness, mark it.
+// Kernels: (1) per (sequence, KV head, 256-block chunk): fixed-point risks
+// of all the group's query heads and their chunk sums; (2) per (sequence, KV
+// head): trigger test on the sums, then (rarely) bitonic sort of the
+// candidates by risk in LDS and per-head scans for the shortest sufficient
+// prefix; (3) one workgroup: exclusive scan of the counts in (sequence, head)
+// order hands out exact-pool slots deterministically; (4) copy each selected
+// block from pinned host memory (zero-copy reads), store it as fp16 with a
+// per-token power of two, zero its witness, mark it.
 #include <math.h>
 
 #include "wc_common.h"
@@ -33,22 +35,28 @@ struct GateArgs {
   const int32_t* page_table;
   const int32_t* ctx_len;
   uint64_t* fx;           // [B][Hq][max_pages], optional copy for the caller
+  uint64_t* xpart;        // [B][Hq][nchunk]: per 256-block chunk sums of rho_fx
   int32_t* sel;           // [B][Hkv][max_pages]
   int32_t* count;         // [B][Hkv]
   int32_t* base;          // [B][Hkv]
   int32_t* take;          // [B][Hkv]
-  int B, Hq, G, max_pages, layer;
+  int B, Hq, G, max_pages, layer, nchunk;
   uint64_t T;
   int64_t budget;
 };
 
+// rho_fx = ceil(rho 2^40) capped at 2^47, rho = e^(logrisk - lse).  rho
+// 2^40 is an exact float (a power-of-two scaling below 2^47), so ceilf is
+// exact and the 64-bit integer is assembled from two exact 32-bit parts.
 __device__ __forceinline__ uint64_t risk_fx(float logrisk, float lse) {
   if (!(logrisk > -INFINITY)) return 0;                 // -inf (no risk) or NaN
-  const float rho = expf(logrisk - lse);
+  const float rho = __expf(logrisk - lse);
   if (!(rho < 128.0f)) return kFxCap;                   // >= 2^47 / 2^40, inf
   if (!(rho > 0.0f)) return 0;
-  const double v = ceil((double)rho * 1099511627776.0);  // exact: rho * 2^40
-  const uint64_t u = (uint64_t)v;
+  const float x = ceilf(rho * 1099511627776.0f);        // integer valued, < 2^47
+  const float hi = floorf(x * 2.3283064365386963e-10f); // x / 2^32
+  const float lo = x - hi * 4294967296.0f;
+  const uint64_t u = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
   return u > kFxCap ? kFxCap : u;
 }
 
@@ -58,10 +66,52 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// Fixed-point risks of one 256-block chunk of one (sequence, KV head), all
+// its query heads: chunk sums for the trigger test (and the optional copy).
+__global__ void __launch_bounds__(256) gate_risk_kernel(wc_cache c, GateArgs a) {
+  __shared__ uint64_t wsum[4][16];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int hkv = c.num_kv_heads;
+  const int P = (a.ctx_len[b] + 15) >> 4;
+  const int G = a.G;
+  const int j = chunk * 256 + t;
+  const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;
+  // every load is issued unconditionally (indices clamped into range) so that
+  // they are all in flight together
+  const int jc = min(j, a.max_pages - 1);
+  float lr[16], ls[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int nc = min(n, G - 1);
+    lr[n] = a.logrisk[row0 + (int64_t)nc * a.max_pages + jc];
+    ls[n] = a.lse[b * a.Hq + g * G + nc];
+  }
+  const int phys = a.page_table[(int64_t)b * a.max_pages + min(j, max(P - 1, 0))];
+  // repaired blocks (exact keys in the pool) carry no risk
+  const bool live = j < P && c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] < 0;
+  uint64_t part[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) part[n] = (n < G && live) ? risk_fx(lr[n], ls[n]) : 0;
+  if (a.fx && j < a.max_pages) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      if (n < G) a.fx[row0 + (int64_t)n * a.max_pages + j] = part[n];
+  }
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    if (n < G) {
+      const uint64_t v = wave_sum_u64(part[n]);
+      if ((t & 63) == 0) wsum[t >> 6][n] = v;
+    }
+  }
+  __syncthreads();
+  if (t < G)
+    a.xpart[((int64_t)b * a.Hq + g * G + t) * a.nchunk + chunk] = wsum[0][t] + wsum[1][t] + wsum[2][t] + wsum[3][t];
+}
+
 __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a) {
   __shared__ uint64_t keys[kMaxSortPages];
   __shared__ uint64_t red[256];
-  __shared__ uint64_t hsum[16];
   __shared__ float hlse[16];
   __shared__ uint8_t rep[kMaxSortPages];
   __shared__ int kneed;
@@ -71,11 +121,17 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   const int P = (S + 15) >> 4;
   const int G = a.G;
   const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;   // head n's row: row0 + n * max_pages
-  if (t < 16) {
-    hsum[t] = 0;
-    hlse[t] = t < G ? a.lse[b * a.Hq + g * G + t] : 0.0f;
+  // X_h from the chunk sums; the trigger test is uniform across the workgroup
+  uint64_t xmax = 0;
+  for (int n = 0; n < G; ++n) {
+    uint64_t X = 0;
+    for (int k = 0; k < a.nchunk; ++k) X += a.xpart[((int64_t)b * a.Hq + g * G + n) * a.nchunk + k];
+    xmax = X > xmax ? X : xmax;
   }
-  // repaired blocks (exact keys in the pool) carry no risk
+  if (t == 0) a.count[b * hkv + g] = 0;
+  if (xmax <= a.T || P == 0) return;
+
+  if (t < 16) hlse[t] = t < G ? a.lse[b * a.Hq + g * G + t] : 0.0f;
   for (int j = t; j < P; j += 256) {
     const int phys = a.page_table[(int64_t)b * a.max_pages + j];
     rep[j] = c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] >= 0;
@@ -84,33 +140,6 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   auto fx_of = [&](int n, int j) -> uint64_t {
     return rep[j] ? 0 : risk_fx(a.logrisk[row0 + (int64_t)n * a.max_pages + j], hlse[n]);
   };
-  // X_h = sum_j rho_fx(h, j): every page's loads of all heads are in flight
-  // together, then one wave reduction and one LDS add per head and wave
-  uint64_t part[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) part[n] = 0;
-  for (int j = t; j < P; j += 256) {
-#pragma unroll
-    for (int n = 0; n < 16; ++n)
-      if (n < G) part[n] += fx_of(n, j);
-  }
-#pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    if (n < G) {
-      const uint64_t v = wave_sum_u64(part[n]);
-      if ((t & 63) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(&hsum[n]), (unsigned long long)v);
-    }
-  }
-  __syncthreads();
-  uint64_t xmax = 0;
-  for (int n = 0; n < G; ++n) xmax = hsum[n] > xmax ? hsum[n] : xmax;
-  if (a.fx) {                                   // optional copy of every rho_fx for the caller
-    for (int n = 0; n < G; ++n)
-      for (int j = t; j < a.max_pages; j += 256)
-        a.fx[row0 + (int64_t)n * a.max_pages + j] = j < P ? fx_of(n, j) : 0;
-  }
-  if (t == 0) a.count[b * hkv + g] = 0;
-  if (xmax <= a.T || P == 0) return;                     // uniform across the workgroup
 
   // sort key: max_h rho_fx (47 bits) << 16 | (65535 - j): descending = risk
   // descending, ties to the lower block index; non-candidates are 0.
@@ -288,8 +317,10 @@ using namespace wc;
 
 extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
   if (B < 0 || Hkv < 0 || max_pages < 0) return 0;
-  // selected block indices, then count / base / take per (sequence, KV head)
-  return (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 3 * 4;
+  // chunk sums (up to 16 query heads per KV head), selected block indices,
+  // then count / base / take per (sequence, KV head)
+  const size_t nchunk = ((size_t)max_pages + 255) / 256;
+  return (size_t)B * Hkv * 16 * nchunk * 8 + (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 3 * 4;
 }
 
 extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse, int B,
@@ -335,14 +366,19 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
   const int hkv = c.num_kv_heads;
   char* ws = (char*)workspace;
   uint64_t* fx = rho_fx;
+  const int nchunk = (max_pages + 255) / 256;
+  uint64_t* xpart = (uint64_t*)ws;
+  ws += (size_t)B * hkv * 16 * nchunk * 8;
   int32_t* sel = (int32_t*)ws;
   ws += (size_t)B * hkv * max_pages * 4;
   int32_t* cnt = (int32_t*)ws;
   int32_t* base = cnt + B * hkv;
   int32_t* take = base + B * hkv;
-  GateArgs a{block_logrisk, lse, page_table, ctx_len, fx, sel, cnt, base, take, B, Hq, Hq / hkv, max_pages, layer,
-             (uint64_t)floor(et * 1099511627776.0), budget_blocks};
+  GateArgs a{block_logrisk, lse, page_table, ctx_len, fx, xpart, sel, cnt, base, take, B, Hq, Hq / hkv, max_pages,
+             layer, nchunk, (uint64_t)floor(et * 1099511627776.0), budget_blocks};
   hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(gate_risk_kernel, dim3((unsigned)nchunk, (unsigned)hkv, (unsigned)B), dim3(256), 0, st, c, a);
+  if (int e = check_launch("wc_gate_pagein risk")) return e;
   hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a);
   if (int e = check_launch("wc_gate_pagein select")) return e;
   hipLaunchKernelGGL(gate_assign_kernel, dim3(1), dim3(256), 0, st, a, B * hkv, c.pool_capacity, pool_used,
