@@ -358,6 +358,7 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
   // the high and low dither bytes enter the key MFMAs as 1152 + h and
   // 1024 + l; scaled by -2^-8 and -2^-16 their bias is -qsum (4.5 + 2^-6)
   const float qbias = qsum * 4.515625f;
+  const f4 kb4 = SCHEME == WC_DITHER_INT8 ? f4{qbias, qbias, qbias, qbias} : f4{0.f, 0.f, 0.f, 0.f};
   const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
   const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
@@ -431,7 +432,6 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
     // ---------------- QK^T: three MFMA chains over 128 channels
     f4 Dc = zero4, Dh = zero4, Dl = zero4;
     float st[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
-    float kbias = 0.0f;
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     const uint32_t base = key + (uint32_t)(64 * (tok0 + n) + 16 * kq);
     // draws of token n, channels 32k + 8j .. +7, as fp16 pairs 1024 + high byte
@@ -458,7 +458,8 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
           fp8_to_h(kw[2 * j + 1], c2, c3);
         }
         const h8 Ac = make_h8(c0, c1, c2, c3);
-        Dc = mfma32(Ac, Qhi[j], j == 0 ? zero4 : Dc);
+        // the code chain starts from the byte-bias correction (INT8)
+        Dc = mfma32(Ac, Qhi[j], j == 0 ? kb4 : Dc);
         if (QF32) Dc = mfma32(Ac, Qlo[j], Dc);
         if (SCHEME == WC_DITHER_INT8) {
           const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
@@ -471,7 +472,6 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
           }
         }
       }
-      if (SCHEME == WC_DITHER_INT8) kbias = qbias;
     } else {
       // repaired block: exact keys from the pool; the values still need the draws
       const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
@@ -506,12 +506,13 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
       H2 = sH[4 * kq + 2][n];
       H3 = sH[4 * kq + 3][n];
     }
-    // raw = sum q' (code - h 2^-8 - l 2^-16); kbias cancels the byte biases
+    // raw = sum q' (code - h 2^-8 - l 2^-16); the chain's start value cancels the byte biases
     float raw[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // (a repaired block left Dh, Dl and the start value at zero: raw = Dc exactly)
       raw[r] = Dc[r];
-      if (SCHEME == WC_DITHER_INT8 && !exact) raw[r] = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw[r] + kbias));
+      if (SCHEME == WC_DITHER_INT8) raw[r] = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw[r]));
     }
     float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
     if (CMP) {                                 // lanes n + 8 take tokens 2, 3 of head n
@@ -521,11 +522,12 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
       cA[1] = dpp_shr8_hi(cA[1], cA[3]);
     }
     float l2[4], cB[4];
+    const float kapB = (meterB && !exact) ? kappac : 0.0f;
     float sv[4] = {vl.vs.x, vl.vs.y, vl.vs.z, vl.vs.w};
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       l2[r] = qs2c * st[r] * raw[r];
-      cB[r] = (meterB && !exact) ? kappac * st[r] : 0.0f;
+      cB[r] = kapB * st[r];
     }
     if (!full) {                               // tokens past the end: no weight, no bound, finite scales
 #pragma unroll
@@ -539,18 +541,24 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
     }
 
     // ---------------- online softmax with lazy rescale
-    float tmax = vmax(l2[0], l2[1]);
+    // Each lane tests its own tokens; only when some lane needs it does the
+    // head's maximum get reduced (a head's lanes always agree on m_ref).
+    float lmax = vmax(l2[0], l2[1]);
     float svmax = vmax(sv[0], sv[1]);
     if (!CMP) {
-      tmax = vmax(tmax, vmax(l2[2], l2[3]));
+      lmax = vmax(lmax, vmax(l2[2], l2[3]));
       svmax = vmax(svmax, vmax(sv[2], sv[3]));
-    } else {
-      tmax = vmax_ror8(tmax);
     }
-    tmax = max4k(tmax);
-    const bool move = tmax > m_ref + kRescaleSlack || (svmax > 128.0f && tmax > m_ref);
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float m_new = move ? tmax : m_ref;
+    const bool need = lmax > m_ref + kRescaleSlack || (svmax > 128.0f && lmax > m_ref);
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      float tmax = lmax, anyn = need ? 1.0f : 0.0f;
+      if (CMP) {
+        tmax = vmax_ror8(tmax);
+        anyn = vmax_ror8(anyn);
+      }
+      tmax = max4k(tmax);
+      anyn = max4k(anyn);
+      const float m_new = anyn > 0.0f ? tmax : m_ref;
       const float alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
       l_run *= alpha;
       na *= alpha;
