@@ -148,6 +148,27 @@ def decode_kv_torch(seed, batch, S, Hkv=4, d=128, device="cuda", chunk=8192):
     return k, v
 
 
+def ragged_kv_torch(seed, ctx_lens, Hkv=4, d=128, device="cuda", chunk=8192):
+    """bf16 K, V [sum(ctx_lens), Hkv, d] for a ragged batch, sequences back to
+    back, K RoPE'd at each sequence's own positions 0..S_b-1."""
+    import torch
+    lens = torch.as_tensor(np.asarray(ctx_lens, dtype=np.int64), device=device)
+    n = int(lens.sum().item())
+    starts = torch.cumsum(lens, 0) - lens
+    pos_all = torch.arange(n, device=device) - torch.repeat_interleave(starts, lens)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    k = torch.empty((n, Hkv, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((n, Hkv, d), dtype=torch.bfloat16, device=device)
+    for t0 in range(0, n, chunk):
+        t1 = min(n, t0 + chunk)
+        kk = torch.randn((t1 - t0, Hkv, d), generator=gen, device=device, dtype=torch.float32)
+        vv = torch.randn((t1 - t0, Hkv, d), generator=gen, device=device, dtype=torch.float32)
+        k[t0:t1] = _torch_rope(kk.to(torch.float64), pos_all[t0:t1]).to(torch.float32).to(torch.bfloat16)
+        v[t0:t1] = vv.to(torch.bfloat16)
+    return k, v
+
+
 def query_torch(seed, batch, Hq=28, d=128, device="cuda"):
     import torch
     gen = torch.Generator(device=device)
