@@ -284,9 +284,9 @@ def test_gate_flow_64_ragged_fp8():
         torch.cuda.synchronize()
         ra2_np = ra2.cpu().numpy()
         _flush(f"    {total} blocks repaired; max meter {float(ra.cpu().numpy().max()):.4g} -> {float(ra2_np.max()):.4g}")
-        # not a theorem (a repair also renormalizes the softmax), but the
-        # repaired heads should land at about tau
-        assert float(ra2_np.max()) <= max(tau, float(ra.cpu().numpy().max())) * 1.05
+        # untriggered heads already had R <= tau; repaired ones should land at
+        # about tau (not a theorem: a repair also renormalizes the softmax)
+        assert float(ra2_np.max()) <= tau * 1.05 + 1e-12
         slots = cache.exact_slot.cpu().numpy()[0]
         for (b, g), (k32, v32, qg, oc, r) in ref.items():
             S_ = int(lens[b])
