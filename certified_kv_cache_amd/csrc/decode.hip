@@ -244,6 +244,12 @@ __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
 // exceeds it by more than 8 (log2 units), so exp2 weights stay <= 256.
 constexpr float kRescaleSlack = 8.0f;
 
+// Pages each wave keeps in flight ahead of the one it processes.
+#ifndef WC_PREFETCH_DEPTH
+#define WC_PREFETCH_DEPTH 1
+#endif
+constexpr int kDepth = WC_PREFETCH_DEPTH;
+
 // Minimum workgroups per CU (4 waves each) the register allocation must
 // allow: three for bf16 queries (168 registers, no spills), two for fp32
 // queries (their split query operand needs more).
@@ -376,9 +382,11 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
   // Per-wave LDS tile of the page's dither high bytes as fp16 operands
   // (1024 + byte): the key side (lane = token) hashes each draw once and
   // stores [token][8-channel group]; the value side (lane = channel group)
-  // reads four tokens back.  The space is the end-of-split combine buffer.
+  // reads four tokens back.  Rows are padded to 17 slots so that neither
+  // side's 16 lanes of one instruction share a bank.  The space is the
+  // end-of-split combine buffer.
   __shared__ __align__(16) uint4 smem[kNW * 2 * 16 * 16];
-  uint4 (*sH)[16] = reinterpret_cast<uint4 (*)[16]>(smem + wave * 256);
+  uint4 (*sH)[17] = reinterpret_cast<uint4 (*)[17]>(smem + wave * 16 * 17);
   __shared__ float sRisk[kNW][16][16];
   float (*sR)[16] = sRisk[wave];
 
@@ -415,9 +423,9 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
     load_page<SCHEME, CMP>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
   };
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
-    // next page, one page ahead of its use; the last page loads itself again
+    // the page kDepth ahead; past the end the last page loads itself again
     // so that every iteration issues the same loads
-    fetch(min(i + 1, npw - 1), nxt, vnxt);
+    fetch(min(i + kDepth, npw - 1), nxt, vnxt);
     const int jj = w0 + i;
     const int tok0 = jj * 16;
     const bool exact = cur.slot >= 0;          // wave-uniform
@@ -672,13 +680,30 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
       __builtin_amdgcn_wave_barrier();
     }
   };
-  KLoad kA, kB;
-  VLoad vA, vB;
-  if (npw > 0) fetch(0, kA, vA);
-  for (int i = 0; i < npw; i += 2) {
-    page(kA, vA, kB, vB, i);
-    if (i + 1 >= npw) break;
-    page(kB, vB, kA, vA, i + 1);
+  if constexpr (kDepth == 1) {
+    KLoad kA, kB;
+    VLoad vA, vB;
+    if (npw > 0) fetch(0, kA, vA);
+    for (int i = 0; i < npw; i += 2) {
+      page(kA, vA, kB, vB, i);
+      if (i + 1 >= npw) break;
+      page(kB, vB, kA, vA, i + 1);
+    }
+  } else {
+    // a ring of kDepth + 1 page buffers: page i is processed while pages
+    // i + 1 .. i + kDepth are in flight
+    KLoad kb[kDepth + 1];
+    VLoad vb[kDepth + 1];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (npw > 0) fetch(min(d, npw - 1), kb[d], vb[d]);
+    for (int i = 0; i < npw; i += kDepth + 1) {
+#pragma unroll
+      for (int u = 0; u <= kDepth; ++u) {
+        if (i + u >= npw) break;
+        page(kb[u], vb[u], kb[(u + kDepth) % (kDepth + 1)], vb[(u + kDepth) % (kDepth + 1)], i + u);
+      }
+    }
   }
   const float m_run = m_ref;
   if (SCHEME == WC_DITHER_INT8) {                // the low bytes' mean 255/2 times 2^-16
