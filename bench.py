@@ -39,9 +39,10 @@ def decode_source_sha():
     return h.hexdigest()[:16]
 
 
-def decode_bytes(B, S, meter):
-    """Algorithmic HBM bytes of one decode launch: cache, page table, query."""
-    per_tok = 128 + 128 + 4 + 4 + (32 if meter else 0)   # K, V codes, K, V scales, witness
+def decode_bytes(B, S, meter, scales=True):
+    """Algorithmic HBM bytes of one decode launch: cache, page table, query.
+    (scales=False: the fp8 raw-cast cache, which stores none.)"""
+    per_tok = 128 + 128 + (8 if scales else 0) + (32 if meter else 0)   # K, V codes, K, V scales, witness
     P = -(-S // 16)
     return B * S * HKV * per_tok + B * P * 4 + B * HQ * D * 2 + B * 4 + B * 8
 
@@ -86,7 +87,32 @@ def setup(B, S, seed=3):
     del store
     torch.cuda.synchronize()
     return dict(L=L, cache=cache, k=k, v=v, q=q, tab=tab_d, ctx=torch.full((B,), S, dtype=torch.int32, device=dev),
-                seed=sd, new=new, host=host, npages=npages, tab_np=tab, seeds=seeds)
+                seed=sd, new=new, host=host, npages=npages, tab_np=tab, seeds=seeds, slot=slot, pos=pos)
+
+
+def fp8_variant(w, B, S, iters):
+    """The same workload on the fp8 raw-cast cache (Tier A only)."""
+    import torch
+    L = w["L"]
+    cache = L.KVCache(L.WC_FP8_E4M3, 1, w["npages"], HKV)
+    L.wc_write_kv(cache, w["k"], w["v"], w["slot"], w["pos"], torch.zeros_like(w["pos"], dtype=torch.int64))
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    sm = 1.0 / math.sqrt(D)
+
+    def decode(mask=1, with_risk=True):
+        L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    t_risk = time_decode(decode, iters, mask=1, with_risk=True)
+    t_on = time_decode(decode, iters, mask=1, with_risk=False)
+    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    nb = decode_bytes(B, S, True, scales=False)
+    del cache
+    return {"decode_us": round(t_risk, 2), "decode_meter_on_us": round(t_on, 2), "decode_meter_off_us": round(t_off, 2),
+            "meter_overhead": round(t_on / t_off - 1, 4), "decode_bytes": nb,
+            "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
 def make_step(w, B, S):
@@ -167,6 +193,150 @@ def cpu_baseline(w, B, S, pairs=6):
                        f"{total:.1f} s single-threaded float64 numpy")
 
 
+def prefill_write(iters, seed=4, NL=28, NT=4096):
+    """Write path at prefill scale: 28 layers x 4 KV heads x 4096 tokens, bf16
+    K/V with per-(layer, head, channel) variance log-uniform in [0.1, 10]; one
+    wc_write_kv call per scheme writes all layers."""
+    import numpy as np
+    import torch
+
+    from certified_kv_cache_amd import _lib as L
+    from certified_kv_cache_amd import inputs
+    k, v = inputs.prefill_kv_torch(seed, layers=NL, n_tok=NT, Hkv=HKV)
+    in_bytes = 2 * k.numel() * 2
+    out = {"metric": "write path throughput: GB/s written and total GB/s (% of HBM peak)", "unit": "GB/s",
+           "data": "synthetic", "config": {"workload": f"prefill write {NL} layers x {HKV} KV heads x {NT} tokens, bf16"},
+           "schemes": {}}
+    for name, sch in (("int8", L.WC_DITHER_INT8), ("fp8", L.WC_FP8_E4M3), ("kivi2", L.WC_KIVI2)):
+        ps = 32 if sch == L.WC_KIVI2 else 16
+        tab, npages = inputs.page_table(seed, [NT], page_size=ps)
+        cache = L.KVCache(sch, NL, npages, HKV)
+        t = np.arange(NT)
+        slot = torch.from_numpy(tab[0, t // ps].astype(np.int64) * ps + t % ps).cuda()
+        pos = torch.arange(NT, dtype=torch.int32, device="cuda")
+        sd = torch.full((NT,), 777, dtype=torch.int64, device="cuda")
+        n_tok_heads = NL * NT * HKV
+        if sch == L.WC_DITHER_INT8:
+            written = n_tok_heads * (2 * D + 2 * 4 + 32)
+        elif sch == L.WC_FP8_E4M3:
+            written = n_tok_heads * (2 * D + 32)
+        else:                                   # 2-bit codes (2 x d/4 B per token-head), group params, witness
+            written = n_tok_heads * (2 * D // 4 + 32) + NL * HKV * (NT // 32) * (D * 2 * 4 + 32 * 4 * 2 * 4)
+        L.wc_write_kv(cache, k, v, slot, pos, sd)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            L.wc_write_kv(cache, k, v, slot, pos, sd)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / iters * 1e3
+        tot = in_bytes + written
+        out["schemes"][name] = {"us": round(us, 2), "bytes_written": written, "bytes_total": tot,
+                                "written_GBps": round(written / (us * 1e-6) / 1e9, 1),
+                                "total_GBps": round(tot / (us * 1e-6) / 1e9, 1),
+                                "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
+        del cache
+    return out
+
+
+def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05)):
+    """Ragged decode with the gate: 64 sequences, contexts uniform in
+    [1024, 32768], fp8 raw-cast cache on `n_layers` resident layers, exact keys
+    in pinned host memory.  Each step appends one token per sequence and layer,
+    then per layer decodes (Tier A, block risks), merges and gates at tau.
+    Reports page-in bytes of the cold first step and the mean of the rest."""
+    import numpy as np
+    import torch
+
+    from certified_kv_cache_amd import _lib as L
+    from certified_kv_cache_amd import inputs
+    dev = torch.device("cuda")
+    lens0 = np.random.default_rng(seed).integers(1024, 32769, NB)
+    cap = lens0 + n_steps                              # room for the appended tokens
+    tab, npages = inputs.page_table(seed, cap)
+    mp = tab.shape[1]
+    tab_d = torch.from_numpy(tab).to(dev)
+    q = inputs.query_torch(seed, NB, Hq=HQ)
+    seeds_d = torch.zeros(NB, dtype=torch.int64, device=dev)
+    n0 = int(lens0.sum())
+    slot0 = torch.from_numpy(np.concatenate([tab[b, np.arange(S_) // 16].astype(np.int64) * 16 + np.arange(S_) % 16
+                                             for b, S_ in enumerate(lens0)])).to(dev)
+    pos0 = torch.from_numpy(np.concatenate([np.arange(S_) for S_ in lens0]).astype(np.int32)).to(dev)
+    host = torch.empty((n_layers, npages, HKV, 16, D), dtype=torch.bfloat16, pin_memory=True)
+    layer_kv = []
+    for layer in range(n_layers):                      # per-layer K/V, its exact keys to the host store
+        k, v = inputs.ragged_kv_torch(seed * 100 + layer, cap, Hkv=HKV)
+        store = torch.zeros((npages, HKV, 16, D), dtype=torch.bfloat16, device=dev)
+        starts = np.concatenate([[0], np.cumsum(cap)[:-1]])
+        idx = torch.from_numpy(np.concatenate([starts[b] + np.arange(S_) for b, S_ in enumerate(cap)])).to(dev)
+        slot_all = torch.from_numpy(np.concatenate([tab[b, np.arange(S_) // 16].astype(np.int64) * 16 +
+                                                    np.arange(S_) % 16 for b, S_ in enumerate(cap)])).to(dev)
+        store[slot_all // 16, :, slot_all % 16, :] = k[idx]
+        host[layer].copy_(store)
+        del store
+        first = torch.from_numpy(np.concatenate([starts[b] + np.arange(S_) for b, S_ in enumerate(lens0)])).to(dev)
+        later = [torch.from_numpy(starts + lens0 + s).to(dev) for s in range(n_steps)]
+        layer_kv.append((k[first].contiguous(), v[first].contiguous(),
+                         [(k[i].contiguous(), v[i].contiguous()) for i in later]))
+        del k, v
+    torch.cuda.synchronize()
+    sm = 1.0 / math.sqrt(D)
+    part = torch.empty(L.wc_decode_workspace_bytes(NB, HQ, NSPLIT) // 4, device=dev)
+    risk = torch.empty((NB, HQ, mp), device=dev)
+    o = torch.empty((NB, HQ, D), device=dev)
+    lse = torch.empty((NB, HQ), device=dev)
+    ra = torch.empty((NB, HQ), device=dev)
+    gws = torch.empty(L.wc_gate_workspace_bytes(NB, HKV, mp), dtype=torch.uint8, device=dev)
+    res = {"metric": "gated ragged decode: page-in bytes per step and attention throughput", "data": "synthetic",
+           "config": {"workload": f"{NB} sequences, contexts U[1024, 32768], {n_layers} resident layers, fp8 raw-cast, "
+                                  f"{n_steps} steps, exact keys in pinned host memory", "layers": n_layers,
+                      "steps": n_steps, "tokens": n0}, "tau": {}}
+    for tau in taus:
+        cache = L.KVCache(L.WC_FP8_E4M3, n_layers, npages, HKV, pool_capacity=int(npages) * HKV * n_layers)
+        for layer in range(n_layers):
+            kf, vf, _ = layer_kv[layer]
+            L.wc_write_kv(cache, kf, vf, slot0, pos0, torch.zeros_like(slot0), layer0=layer)
+        pool_used = torch.zeros(1, dtype=torch.int64, device=dev)
+        paged = torch.zeros(1, dtype=torch.int64, device=dev)
+        per_step, dec_us = [], []
+        for s in range(n_steps):
+            lens = lens0 + s + 1
+            ctx = torch.from_numpy(lens.astype(np.int32)).to(dev)
+            pos = torch.from_numpy((lens - 1).astype(np.int32)).to(dev)
+            slot = torch.from_numpy(tab[np.arange(NB), (lens - 1) // 16].astype(np.int64) * 16 + (lens - 1) % 16).to(dev)
+            before = int(paged.item())
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t_dec = 0.0
+            for layer in range(n_layers):
+                kn, vn = layer_kv[layer][2][s]
+                L.wc_write_kv(cache, kn, vn, slot, pos, torch.zeros_like(slot), layer0=layer)
+                a.record()
+                L.wc_decode_attn_meter(cache, layer, q, tab_d, ctx, seeds_d, part, sm, 1, DELTA[0], *DELTA[1:],
+                                       NSPLIT, block_logrisk=risk)
+                b.record()
+                L.wc_lse_merge(part, NB, HQ, NSPLIT, o, lse, ra)
+                L.wc_gate_pagein(cache, layer, risk, lse, tab_d, ctx, tau, host, pool_used, paged, gws)
+                torch.cuda.synchronize()
+                t_dec += a.elapsed_time(b) * 1e3
+            per_step.append(int(paged.item()) - before)
+            dec_us.append(t_dec)
+        nbytes = decode_bytes_ragged(lens0 + n_steps, scales=False) * n_layers
+        res["tau"][str(tau)] = {
+            "pagein_bytes_step1": per_step[0],
+            "pagein_bytes_later_mean": round(float(np.mean(per_step[1:])), 1),
+            "decode_us_per_step": round(float(np.mean(dec_us[1:])), 1),
+            "attention_GBps": round(nbytes / (float(np.mean(dec_us[1:])) * 1e-6) / 1e9, 1)}
+        del cache
+        torch.cuda.empty_cache()
+    return res
+
+
+def decode_bytes_ragged(lens, scales=True):
+    """Algorithmic decode bytes of one layer over a ragged batch (meter on)."""
+    per_tok = 128 + 128 + (8 if scales else 0) + 32
+    return int(sum(int(S_) * HKV * per_tok + (-(-int(S_) // 16)) * 4 for S_ in lens)) + len(lens) * (HQ * D * 2 + 12)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,12 +347,22 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill-write", "gate-flow"],
+                    help="decode: the headline line (default); prefill-write: the 28-layer write path per scheme; "
+                         "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps")
+    ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; the path shards without communication "
               "(see the design notes), so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.workload == "prefill-write":
+        print(json.dumps(prefill_write(args.steps)), flush=True)
+        return
+    if args.workload == "gate-flow":
+        print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)))), flush=True)
+        return
     B, S = args.batch, args.ctx
     w = setup(B, S)
     step, decode, outs = make_step(w, B, S)
@@ -227,6 +407,7 @@ def main():
         "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),
         "pages_paged_in": int(outs["paged"].item()) // 4096,
     }
+    out["fp8_variant"] = fp8_variant(w, B, S, iters)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
     if args.copy_ref:
