@@ -481,26 +481,40 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
         }
       }
     } else {
-      // repaired block: exact keys from the pool; the values still need the draws
+      // repaired block: exact keys from the pool; the values still need the
+      // draws.  All loads are issued before the hashing so that their latency
+      // overlaps it.
       const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
+      uint4 xv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (SCHEME == WC_DITHER_INT8) {
+      for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+      float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (CMP) {
+        const float2 s2 = *reinterpret_cast<const float2*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq + r0);
+        s4.x = s2.x;
+        s4.y = s2.y;
+      } else {
+        s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
+      }
+      if (SCHEME == WC_DITHER_INT8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
           uint32_t hh[4], ll[4];
           draws(j, hh, ll);
         }
-        const uint4 v = xp[j];
-        const h8 Ax = make_h8(v.x, v.y, v.z, v.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // (settled here so that the wait for these loads stays in this branch)
+        const h8 Ax = make_h8(settle((int)xv[j].x), settle((int)xv[j].y), settle((int)xv[j].z), settle((int)xv[j].w));
         Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
         if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
       }
-      // (settled here so that the wait for this load stays in this branch)
-      if (CMP) {
-        const float2 s2 = *reinterpret_cast<const float2*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq + r0);
-        st[0] = settle(s2.x); st[1] = settle(s2.y);
-      } else {
-        const float4 s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
-        st[0] = settle(s4.x); st[1] = settle(s4.y); st[2] = settle(s4.z); st[3] = settle(s4.w);
+      st[0] = settle(s4.x);
+      st[1] = settle(s4.y);
+      if (!CMP) {
+        st[2] = settle(s4.z);
+        st[3] = settle(s4.w);
       }
       Da = zero4;
     }
