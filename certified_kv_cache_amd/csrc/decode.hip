@@ -229,6 +229,46 @@ __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const L
   }
 }
 
+// When a layer's arrays are under 4 GB, one resource per array and layer
+// serves every page: the page enters as a 32-bit scalar offset, which saves
+// the per-page resource set-up.
+struct LayerBufs {
+  __amdgpu_buffer_rsrc_t k, v, w, ks, vs;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t layer_rsrc(const void* base, int64_t off, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + off), (short)0,
+                                           (int)(uint32_t)bytes, kRsrcFlags);
+}
+__device__ __forceinline__ uint4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ float2 bload8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+// pg: page-head block index within the layer (phys * Hkv + g)
+template <int SCHEME, bool PAIR>
+__device__ __forceinline__ void load_page_soff(const LayerBufs& lb, uint32_t pg, const LaneOff& lo, bool meterA,
+                                               KLoad& d, VLoad& e) {
+  d.k0 = bload16s(lb.k, lo.k, pg * 2048u);
+  d.k1 = bload16s(lb.k, lo.k + 1024, pg * 2048u);
+  d.w = bload8s(lb.w, lo.w, meterA ? pg * 512u : pg * 2048u);
+  e.v0 = bload16s(lb.v, lo.v, pg * 2048u);
+  e.v1 = bload16s(lb.v, lo.v + 1024, pg * 2048u);
+  if (SCHEME == WC_DITHER_INT8) {
+    if (PAIR) {
+      const float2 t = bload8s(lb.ks, lo.s, pg * 64u), u = bload8s(lb.vs, lo.s, pg * 64u);
+      d.ks = make_float4(t.x, t.y, 0.f, 0.f);
+      e.vs = make_float4(u.x, u.y, 0.f, 0.f);
+    } else {
+      d.ks = __builtin_bit_cast(float4, bload16s(lb.ks, lo.s, pg * 64u));
+      e.vs = __builtin_bit_cast(float4, bload16s(lb.vs, lo.s, pg * 64u));
+    }
+  } else {
+    d.ks = make_float4(1.f, 1.f, 1.f, 1.f);
+    e.vs = make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+}
+
 // expm1 for c >= 0: series below 2^-5, else 2^(c log2 e) - 1 on v_exp_f32.
 __device__ __forceinline__ float expm1_fast(float c) {
   const float e = __builtin_amdgcn_exp2f(c * kLog2e) - 1.0f;
@@ -263,7 +303,7 @@ constexpr int decode_min_blocks() {
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
-template <int SCHEME, bool QF32, bool CMP>
+template <int SCHEME, bool QF32, bool CMP, bool SOFF>
 __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -408,6 +448,18 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
   const int npw = max(0, min(p1, w0 + per) - w0);
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int64_t pg_base = (int64_t)a.layer * c.num_pages;
+  LayerBufs lb;
+  if (SOFF) {
+    const int64_t lph = c.num_pages * c.num_kv_heads;     // page-head blocks per layer
+    const int64_t l0 = (int64_t)a.layer * lph;
+    lb.k = layer_rsrc(c.k_codes, l0 * 2048, (uint64_t)lph * 2048);
+    lb.v = layer_rsrc(c.v_codes, l0 * 2048, (uint64_t)lph * 2048);
+    lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
+    if (SCHEME == WC_DITHER_INT8) {
+      lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
+      lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
+    }
+  }
   int bphys = 0, bslot = -1;
   auto batch = [&](int i0) {
     const int i = i0 + lane;
@@ -420,7 +472,10 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
     if ((i & 63) == 0) batch(i);
     const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
     d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
-    load_page<SCHEME, CMP>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
+    if (SOFF)
+      load_page_soff<SCHEME, CMP>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
+    else
+      load_page<SCHEME, CMP>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
   };
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
     // the page kDepth ahead; past the end the last page loads itself again
@@ -916,7 +971,15 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   dim3 grid((unsigned)n_split, (unsigned)c.num_kv_heads, (unsigned)B);
   hipStream_t st = (hipStream_t)stream;
   const bool cmp = a.G <= 8;
-#define WC_LAUNCH(SCH, QF, CM) hipLaunchKernelGGL((decode_kernel<SCH, QF, CM>), grid, dim3(256), 0, st, c, a)
+  // one buffer resource per layer array when its byte offsets fit 32 bits
+  const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * 2048u <= 0xFFFFFFFFull;
+#define WC_LAUNCH(SCH, QF, CM)                                                                        \
+  do {                                                                                           \
+    if (soff)                                                                                    \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true>), grid, dim3(256), 0, st, c, a);      \
+    else                                                                                         \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false>), grid, dim3(256), 0, st, c, a);     \
+  } while (0)
   if (c.scheme == WC_DITHER_INT8) {
     if (q_dtype == WC_BF16) {
       if (cmp) WC_LAUNCH(WC_DITHER_INT8, false, true); else WC_LAUNCH(WC_DITHER_INT8, false, false);
