@@ -39,7 +39,12 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kNW = 4;            // waves per workgroup
+// Waves per workgroup (four measured fastest: three and six were slower).
+#ifndef WC_DECODE_WAVES
+#define WC_DECODE_WAVES 4
+#endif
+constexpr int kNW = WC_DECODE_WAVES;
+constexpr int kThreads = 64 * kNW;
 constexpr int kPartial = 132;     // floats per (b, h, split) partial
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -290,21 +295,22 @@ constexpr float kRescaleSlack = 8.0f;
 #endif
 constexpr int kDepth = WC_PREFETCH_DEPTH;
 
-// Minimum workgroups per CU (4 waves each) the register allocation must
-// allow: three for bf16 queries (168 registers, no spills), two for fp32
-// queries (their split query operand needs more).
+// Waves per SIMD the register allocation must allow: three for bf16 queries
+// (168 registers, no spills), two for fp32 queries (their split query
+// operand needs more).
 #ifndef WC_DECODE_MIN_BLOCKS_BF16
 #define WC_DECODE_MIN_BLOCKS_BF16 3
 #endif
 template <bool QF32>
-constexpr int decode_min_blocks() {
+constexpr int decode_waves_per_simd() {
   return QF32 ? 2 : WC_DECODE_MIN_BLOCKS_BF16;
 }
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 template <int SCHEME, bool QF32, bool CMP, bool SOFF>
-__global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kernel(wc_cache c, DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<QF32>())))
+decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
@@ -804,7 +810,7 @@ __global__ void __launch_bounds__(256, (decode_min_blocks<QF32>())) decode_kerne
     sM[wave][n][3] = nb;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * kPartial; e += 256) {
+  for (int e = threadIdx.x; e < G * kPartial; e += kThreads) {
     const int hn = e / kPartial, f = e % kPartial;
     float M = -INFINITY;
 #pragma unroll
@@ -976,9 +982,9 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
 #define WC_LAUNCH(SCH, QF, CM)                                                                        \
   do {                                                                                           \
     if (soff)                                                                                    \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true>), grid, dim3(256), 0, st, c, a);      \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true>), grid, dim3(kThreads), 0, st, c, a); \
     else                                                                                         \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false>), grid, dim3(256), 0, st, c, a);     \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false>), grid, dim3(kThreads), 0, st, c, a); \
   } while (0)
   if (c.scheme == WC_DITHER_INT8) {
     if (q_dtype == WC_BF16) {
