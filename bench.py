@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HQ, HKV, D, NSPLIT = 28, 4, 128, 16
+G_ = HQ // HKV
 DELTA = (1e-2, 28, 28, 256)
 TAU = 0.2
 PEAK_GBS = 8000.0
@@ -158,38 +159,45 @@ def time_decode(decode, iters, **kw):
     return a.elapsed_time(b) / iters * 1e3
 
 
-def cpu_baseline(w, B, S, pairs=6):
+def cpu_baseline(w, B, S, budget_s=12.0):
     """The float64 oracle's read path (dither regeneration, dequantization,
-    attention, Tier A/B, TV meter) on `pairs` (sequence, KV head) pairs of the
-    same workload, one thread, scaled to GB/s of the same algorithmic bytes."""
+    attention, Tier A/B, TV meter) on (sequence, KV head) pairs of the same
+    workload, one thread, taken in a seeded random order until about
+    `budget_s` seconds of timed work; scaled to GB/s of the same algorithmic
+    bytes.  The cache the read path consumes (codes, scales, witness) is made
+    by the oracle's write path outside the timed region."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import dither, meter, quant
     sm = 1.0 / math.sqrt(D)
     lt = math.log(2 * S / meter.delta_loc(*DELTA))
-    rng = np.random.default_rng(0)
-    picks = [(int(rng.integers(B)), int(g)) for g in rng.integers(0, HKV, pairs)]
-    total = 0.0
+    order = np.random.default_rng(0).permutation(B * HKV)
+    total, done = 0.0, 0
     with threadpool_limits(limits=1):
-        for b, g in picks:
+        for idx in order:
+            b, g = int(idx) // HKV, int(idx) % HKV
             k32 = w["k"][b * S:(b + 1) * S, g].float().cpu().numpy()
             v32 = w["v"][b * S:(b + 1) * S, g].float().cpu().numpy()
-            q = w["q"][b, g * 7:(g + 1) * 7].float().cpu().numpy().astype(np.float64)
+            q = w["q"][b, g * G_:(g + 1) * G_].float().cpu().numpy().astype(np.float64)
             seed = int(w["seeds"][b])
             pos = np.arange(S)
-            ck, sk, _ = quant.dither_int8(k32, dither.dither_rows(seed, 0, g, pos))
-            cv, sv, _ = quant.dither_int8(v32, dither.dither_rows(seed, 0, g, pos))
-            wt = quant.witness(k32, quant.dequant_dither_int8(ck, sk, dither.dither_rows(seed, 0, g, pos)))
+            xi0 = dither.dither_rows(seed, 0, g, pos)
+            ck, sk, _ = quant.dither_int8(k32, xi0)
+            cv, sv, _ = quant.dither_int8(v32, xi0)
+            wt = quant.witness(k32, quant.dequant_dither_int8(ck, sk, xi0))
             t0 = time.perf_counter()
             xi = dither.dither_rows(seed, 0, g, pos)
             khat = quant.dequant_dither_int8(ck, sk, xi)
             vhat = quant.dequant_dither_int8(cv, sv, xi)
             meter.decode_group(q, k32, khat, v32, vhat, wt, sm, k_scale=sk, log_term=lt)
             total += time.perf_counter() - t0
-    sample_bytes = pairs * decode_bytes(B, S, True) / (B * HKV)
+            done += 1
+            if total >= budget_s:
+                break
+    sample_bytes = done * decode_bytes(B, S, True) / (B * HKV)
     return dict(value=round(sample_bytes / total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{pairs} of {B * HKV} (sequence, KV head) pairs, all {S} tokens, "
+                sample=f"{done} of {B * HKV} (sequence, KV head) pairs, all {S} tokens each, "
                        f"{total:.1f} s single-threaded float64 numpy")
 
 
@@ -341,7 +349,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the decode reaches its steady rate after ~100-200 back-to-back launches
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
@@ -381,7 +390,9 @@ def main():
     t_risk = time_decode(decode, iters, mask=3, with_risk=True)
     t_on = time_decode(decode, iters, mask=3, with_risk=False)
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
-    t_on = min(t_on, time_decode(decode, iters, mask=3, with_risk=False))
+    t_risk2 = time_decode(decode, iters, mask=3, with_risk=True)
+    t_on2 = time_decode(decode, iters, mask=3, with_risk=False)
+    t_risk, t_on = min(t_risk, t_risk2), min(t_on, t_on2)
     dec_step_us = t_risk
     bytes_on = decode_bytes(B, S, True)
     ach = bytes_on / (dec_step_us * 1e-6) / 1e9
