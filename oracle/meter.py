@@ -29,7 +29,8 @@ Readings (the design doc lists them):
   (A^2 - 1)/2 = E (1 + E/2) =: R.  R is reported unclamped; the TV bound is
   min(1, R).
 * Tier B uses s_{c,t} = s_t (one scale per token and KV head), S = the
-  sequence's full context length, H = query heads.
+  sequence's full context length, H = query heads; with the outlier bypass
+  (oracle/outlier.py) s_{c,t} = 0 on the bypassed channels.
 * Repaired (exact) tokens have c_t = 0 in both tiers and k^ = k.
 * The block risk used by the gate is rho_{h,j} = sum_{t in block j}
   p~_t expm1(c_t) for the gate's tier, so that sum_j rho_{h,j} = E_h.
@@ -60,22 +61,22 @@ def tier_a(q, w, sm_scale, num_bands=8):
     return sm_scale * qn @ np.asarray(w, dtype=np.float64).T  # [Hq, S]
 
 
-def tier_b(q, s, sm_scale, log_term):
-    """u[h, t] = sqrt(2 varsigma^2 log_term), varsigma^2 = sm^2 sum_c q_c^2 s_t^2 / 12.
+def tier_b_sigma2(q, s, sm_scale, bypass=None):
+    """Variance proxy varsigma^2[h, t] = sm^2 sum_c q_c^2 s_{c,t}^2 / 12.
 
-    log_term = log(2 S / delta_loc).
+    s_{c,t} = s_t, except on the outlier-bypass channels ``bypass`` (stored
+    exactly, s_{c,t} = 0), which drop out of the sum.
     """
-    q = np.asarray(q, dtype=np.float64)
-    s = np.asarray(s, dtype=np.float64)
-    var = sm_scale ** 2 * np.sum(q ** 2, axis=-1)[:, None] * (s[None, :] ** 2) / 12.0
-    return np.sqrt(2.0 * var * log_term)
-
-
-def tier_b_sigma2(q, s, sm_scale):
-    """Variance proxy varsigma^2[h, t] alone (for the Tier B pins)."""
-    q = np.asarray(q, dtype=np.float64)
+    q = np.array(q, dtype=np.float64)
+    if bypass is not None and len(bypass):
+        q[:, np.asarray(bypass, dtype=np.int64)] = 0.0
     s = np.asarray(s, dtype=np.float64)
     return sm_scale ** 2 * np.sum(q ** 2, axis=-1)[:, None] * (s[None, :] ** 2) / 12.0
+
+
+def tier_b(q, s, sm_scale, log_term, bypass=None):
+    """u[h, t] = sqrt(2 varsigma^2 log_term); log_term = log(2 S / delta_loc)."""
+    return np.sqrt(2.0 * tier_b_sigma2(q, s, sm_scale, bypass) * log_term)
 
 
 def softmax(l):
@@ -97,11 +98,12 @@ def tv(p, p_tilde):
 
 
 def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
-                 repaired=None, page_size=16, gate_tier="auto", num_bands=8):
+                 repaired=None, page_size=16, gate_tier="auto", num_bands=8, bypass=None):
     """Decode of the query heads sharing one KV head, over S cached tokens.
 
     q [G, d]; k, khat, v, vhat [S, d]; w [S, B]; k_scale [S] (dithered INT8,
-    enables Tier B); repaired bool [S] (exact tokens: k^ = k and c = 0).
+    enables Tier B); repaired bool [S] (exact tokens: k^ = k and c = 0);
+    bypass: the outlier-bypass channels of the keys (Tier B drops them).
     Returns a dict of float64 arrays, per head unless noted:
       o_tilde [G, d]  compressed output sum_t p~_t v^_t (what the GPU returns)
       lse [G]         log sum_t exp(l~_t)
@@ -126,7 +128,7 @@ def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
     a[:, rep] = 0.0
     E_A, R_A, _ = meter_from(pt, a)
     if k_scale is not None and log_term is not None:
-        u = tier_b(q, k_scale, sm_scale, log_term)
+        u = tier_b(q, k_scale, sm_scale, log_term, bypass)
         u[:, rep] = 0.0
         E_B, R_B, _ = meter_from(pt, u)
     else:
