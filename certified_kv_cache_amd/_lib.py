@@ -29,7 +29,8 @@ class WcCache(ctypes.Structure):
                 ("k_codes", _c_void_p), ("v_codes", _c_void_p), ("k_scale", _c_void_p),
                 ("v_scale", _c_void_p), ("k_aux", _c_void_p), ("v_aux", _c_void_p),
                 ("witness", _c_void_p), ("exact_slot", _c_void_p), ("exact_pool", _c_void_p),
-                ("exact_scale", _c_void_p), ("pool_capacity", _i64)]
+                ("exact_scale", _c_void_p), ("pool_capacity", _i64), ("num_outliers", _i32),
+                ("reserved", _i32), ("outlier_ch", _c_void_p), ("k_outlier", _c_void_p)]
 
 
 class WitcertError(RuntimeError):
@@ -52,6 +53,7 @@ def _load():
         "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
+        "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -69,7 +71,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
-           "wc_gate_pagein", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_last_error", "wc_version"]
+           "wc_gate_pagein", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select", "wc_last_error",
+           "wc_version"]
 
 
 def _check(fn, code):
@@ -102,7 +105,7 @@ class KVCache:
     """Device tensors of one paged cache (all layers) plus its C descriptor."""
 
     def __init__(self, scheme, num_layers, num_pages, num_kv_heads, device="cuda", pool_capacity=0,
-                 page_size=None):
+                 page_size=None, num_outliers=0):
         self.scheme = scheme
         self.L, self.P, self.H = num_layers, num_pages, num_kv_heads
         ps = page_size or (32 if scheme == WC_KIVI2 else 16)
@@ -135,11 +138,21 @@ class KVCache:
             self.exact_scale = torch.zeros((pool_capacity, 16), **f32)
         else:
             self.exact_slot = self.exact_pool = self.exact_scale = None
+        # outlier bypass: channels [L][Hkv][m] (filled by wc_outlier_select or
+        # the caller) and the exact bf16 keys on them [L][P][Hkv][16][m]
+        self.num_outliers = num_outliers
+        if num_outliers > 0:
+            self.outlier_ch = torch.zeros((num_layers, num_kv_heads, num_outliers), dtype=torch.int32,
+                                          device=device)
+            self.k_outlier = torch.zeros(shp + (16, num_outliers), dtype=torch.int16, device=device)
+        else:
+            self.outlier_ch = self.k_outlier = None
         self.desc = WcCache(scheme, 128, num_kv_heads, 8, ps, num_layers, num_pages,
                             *[t.data_ptr() if t is not None else None for t in
                               (self.k_codes, self.v_codes, self.k_scale, self.v_scale, self.k_aux,
                                self.v_aux, self.witness, self.exact_slot, self.exact_pool, self.exact_scale)],
-                            pool_capacity)
+                            pool_capacity, num_outliers, 0,
+                            *[t.data_ptr() if t is not None else None for t in (self.outlier_ch, self.k_outlier)])
 
     def ref(self):
         return ctypes.byref(self.desc)
@@ -187,6 +200,19 @@ def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, h
         cache.ref(), layer, _ptr(block_logrisk), _ptr(lse), B, Hq, _ptr(page_table), max_pages, _ptr(ctx_len),
         float(tau), int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged), _ptr(selected),
         _ptr(rho_fx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def wc_outlier_select(x, m, channels, stream=None):
+    """x: [n_layers, n_tok, Hkv, 128] or [n_tok, Hkv, 128] (bf16 or fp32, contiguous);
+    channels: int32 [n_layers, Hkv, m]."""
+    if x.dim() == 3:
+        x = x[None]
+    assert x.is_contiguous() and channels.dtype == torch.int32 and channels.is_contiguous()
+    n_layers, n_tok, hkv = x.shape[0], x.shape[1], x.shape[2]
+    assert channels.numel() == n_layers * hkv * m
+    _check("wc_outlier_select", lib.wc_outlier_select(_ptr(x), _dtype_code(x), n_layers, n_tok, hkv,
+                                                      n_tok * hkv * x.shape[3], m, _ptr(channels),
+                                                      _stream(stream)))
 
 
 def wc_dither_fill(seed, layer, kv_head, pos0, n_pos, out, stream=None):

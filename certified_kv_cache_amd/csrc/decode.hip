@@ -26,8 +26,11 @@
 //        value codes of channel 8n + tile, tokens 4k..4k+3, one 32-bit word of
 //        the value page layout.  Lane (n, k) ends with channels 32k..32k+31 of
 //        head n.
-//   Tier A  a^T[token][head] = W[token][band] . beta[head][band] as one MFMA
-//        16x16x32 with hi/lo fp16 splits (w_hi b_hi + w_lo b_hi + w_hi b_lo).
+//   Tier A  a^T[token][head] = W[token][band] . beta[head][band] on two fp32
+//        MFMAs 16x16x4.
+//   Outlier bypass  the exact part of the logits on the bypassed channels,
+//        X[token][i] . Q[head][O[i]], on m/4 more fp32 MFMAs 16x16x4; the query
+//        operands of the key chains are zero on those channels.
 #include <math.h>
 
 #include "wc_common.h"
@@ -166,6 +169,7 @@ struct KLoad {
   uint4 k0, k1;
   float4 ks;
   float2 w;
+  uint2 xo;               // outlier bypass: the lane's bf16 side-store entries
   int slot;               // exact-pool slot (-1 = quantized), wave-uniform
 };
 // Values: 8 channels x 4 tokens of codes and the value scales of the lane's
@@ -185,6 +189,7 @@ struct LaneOff {
   uint32_t s;             // scales: tokens 4k (+ r0) onward
   uint32_t w;             // witness bands 2k, 2k+1 of token n (meter off: the key codes again)
   uint32_t v;             // value codes: channels 8n..8n+3 (+1 KB: 8n+4..8n+7), tokens 4k..4k+3
+  uint32_t o;             // outlier side store: entries k m/4 .. of token n
 };
 
 // Buffer resource of one page-head block (raw, untyped, 32-bit data format):
@@ -200,15 +205,25 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ float2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 
 // With a compacted softmax lane (n, k) evaluates tokens 4k + r0 and
 // 4k + r0 + 1 only (r0 = 0 for n < 8, 2 for n >= 8): its scales are a pair.
 // The load count and order never depend on run-time flags, and the lane
 // offsets stay in fixed registers, so the wait for one page's data never
 // waits on the page prefetched after it.
-template <int SCHEME, bool PAIR>
+template <int SCHEME, bool PAIR, int NO4>
 __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const LaneOff& lo, bool meterA, KLoad& d,
                                           VLoad& e) {
+  if (NO4 > 0) {                               // side store: 32 m bytes per page-head block
+    const __amdgpu_buffer_rsrc_t orr = page_rsrc(c.k_outlier, pg * (128 * NO4), 128 * NO4);
+    if (NO4 == 4)
+      d.xo = __builtin_bit_cast(uint2, bload8(orr, lo.o));
+    else
+      d.xo = make_uint2(bload4(orr, lo.o), 0u);
+  }
   const __amdgpu_buffer_rsrc_t kr = page_rsrc(c.k_codes, pg * 2048, 2048);
   const __amdgpu_buffer_rsrc_t vr = page_rsrc(c.v_codes, pg * 2048, 2048);
   const __amdgpu_buffer_rsrc_t wr = meterA ? page_rsrc(c.witness, pg * 512, 512) : kr;
@@ -238,7 +253,7 @@ __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const L
 // serves every page: the page enters as a 32-bit scalar offset, which saves
 // the per-page resource set-up.
 struct LayerBufs {
-  __amdgpu_buffer_rsrc_t k, v, w, ks, vs;
+  __amdgpu_buffer_rsrc_t k, v, w, ks, vs, o;
 };
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t layer_rsrc(const void* base, int64_t off, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + off), (short)0,
@@ -250,10 +265,19 @@ __device__ __forceinline__ uint4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ float2 bload8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
   return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
+__device__ __forceinline__ uint32_t bload4s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
 // pg: page-head block index within the layer (phys * Hkv + g)
-template <int SCHEME, bool PAIR>
+template <int SCHEME, bool PAIR, int NO4>
 __device__ __forceinline__ void load_page_soff(const LayerBufs& lb, uint32_t pg, const LaneOff& lo, bool meterA,
                                                KLoad& d, VLoad& e) {
+  if (NO4 > 0) {
+    if (NO4 == 4)
+      d.xo = __builtin_bit_cast(uint2, bload8s(lb.o, lo.o, pg * (128u * NO4)));
+    else
+      d.xo = make_uint2(bload4s(lb.o, lo.o, pg * (128u * NO4)), 0u);
+  }
   d.k0 = bload16s(lb.k, lo.k, pg * 2048u);
   d.k1 = bload16s(lb.k, lo.k + 1024, pg * 2048u);
   d.w = bload8s(lb.w, lo.w, meterA ? pg * 512u : pg * 2048u);
@@ -308,7 +332,8 @@ constexpr int decode_waves_per_simd() {
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
-template <int SCHEME, bool QF32, bool CMP, bool SOFF>
+// NO4: outlier bypass with m = 4 NO4 exact key channels (0 = none).
+template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<QF32>())))
 decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -354,10 +379,40 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   }
   float qmax = 0.0f, bsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    qmax = fmaxf(qmax, fabsf(qf[i]));
-    bsum[i >> 3] = fmaf(qf[i], qf[i], bsum[i >> 3]);
+  for (int i = 0; i < 32; ++i) bsum[i >> 3] = fmaf(qf[i], qf[i], bsum[i >> 3]);   // Tier A: the full query
+  // Outlier bypass: the key chains see the query with the bypassed channels
+  // zeroed; entry k m/4 + j of the side store (channel O[k m/4 + j]) meets
+  // head n's query there in MFMA j: bO[j] = q[O[k m/4 + j]] sm log2 e.
+  float bO[4] = {0.f, 0.f, 0.f, 0.f};
+  float qz2 = 0.0f;                            // sum of q^2 off the bypassed channels (Tier B)
+  if (NO4 > 0) {
+    const int32_t* oc = c.outlier_ch + ((int64_t)a.layer * c.num_kv_heads + g) * (4 * NO4);
+    uint32_t omask = 0;
+#pragma unroll
+    for (int e = 0; e < 4 * NO4; ++e) {
+      const int ch = oc[e] & 127;
+      omask |= (ch >> 5) == kq ? 1u << (ch & 31) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      qf[i] = ((omask >> i) & 1u) ? 0.0f : qf[i];
+      qz2 = fmaf(qf[i], qf[i], qz2);
+    }
+    qz2 += shfl_xor(qz2, 16);
+    qz2 += shfl_xor(qz2, 32);
+    if (hv) {
+      const int64_t qrow = ((int64_t)b * a.Hq + h) * 128;
+#pragma unroll
+      for (int j = 0; j < NO4; ++j) {
+        const int ch = oc[kq * NO4 + j] & 127;
+        const float qv = QF32 ? reinterpret_cast<const float*>(a.q)[qrow + ch]
+                              : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qrow + ch]);
+        bO[j] = qv * (a.sm_scale * kLog2e);
+      }
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
   qmax = fmaxf(qmax, shfl_xor(qmax, 16));
   qmax = fmaxf(qmax, shfl_xor(qmax, 32));
   int qe = 0;
@@ -412,7 +467,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const float qbias = qsum * 4.515625f;
   const f4 kb4 = SCHEME == WC_DITHER_INT8 ? f4{qbias, qbias, qbias, qbias} : f4{0.f, 0.f, 0.f, 0.f};
   const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
-  const float kappa = a.sm_scale * sqrtf(qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
+  const float kappa = a.sm_scale * sqrtf(NO4 > 0 ? qz2 : qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
   const uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(a.seed[b], (uint32_t)a.layer, (uint32_t)g) : 0u;
   // compacted softmax: lane (n, k) evaluates head n & 7, tokens 4k + r0, +1
@@ -423,6 +478,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   lo.s = (uint32_t)(4 * (4 * kq + r0));
   lo.w = meterA ? (uint32_t)(4 * (8 * n + 2 * kq)) : lo.k;
   lo.v = (uint32_t)(16 * lane);
+  lo.o = (uint32_t)(2 * NO4 * (4 * n + kq));
   const float qs2c = CMP ? dpp_shr8_hi(qs2, qs2) : qs2;
   const float kappac = CMP ? dpp_shr8_hi(kappa, kappa) : kappa;
   // Per-wave LDS tile of the page's dither high bytes as fp16 operands
@@ -461,6 +517,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     lb.k = layer_rsrc(c.k_codes, l0 * 2048, (uint64_t)lph * 2048);
     lb.v = layer_rsrc(c.v_codes, l0 * 2048, (uint64_t)lph * 2048);
     lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
+    if (NO4 > 0) lb.o = layer_rsrc(c.k_outlier, l0 * (128 * NO4), (uint64_t)lph * (128 * NO4));
     if (SCHEME == WC_DITHER_INT8) {
       lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
       lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
@@ -479,9 +536,9 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
     d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
     if (SOFF)
-      load_page_soff<SCHEME, CMP>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
+      load_page_soff<SCHEME, CMP, NO4>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
     else
-      load_page<SCHEME, CMP>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
+      load_page<SCHEME, CMP, NO4>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
   };
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
     // the page kDepth ahead; past the end the last page loads itself again
@@ -497,6 +554,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     // repaired block)
     f4 Da = zero4;
     if (meterA) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
+    // exact logits on the bypassed channels (log2 units), also for repaired
+    // blocks: their pool keys meet the zeroed query
+    f4 Do = zero4;
+    if (NO4 > 0) {
+      Do = mfma_f32(__uint_as_float(cur.xo.x << 16), bO[0], Do);
+      Do = mfma_f32(__uint_as_float(cur.xo.x & 0xFFFF0000u), bO[1], Do);
+      if (NO4 == 4) {
+        Do = mfma_f32(__uint_as_float(cur.xo.y << 16), bO[2], Do);
+        Do = mfma_f32(__uint_as_float(cur.xo.y & 0xFFFF0000u), bO[3], Do);
+      }
+    }
 
     // ---------------- QK^T: three MFMA chains over 128 channels
     f4 Dc = zero4, Dh = zero4, Dl = zero4;
@@ -598,11 +666,16 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       if (SCHEME == WC_DITHER_INT8) raw[r] = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw[r]));
     }
     float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
+    float lo2[4] = {Do[0], Do[1], Do[2], Do[3]};
     if (CMP) {                                 // lanes n + 8 take tokens 2, 3 of head n
       raw[0] = dpp_shr8_hi(raw[0], raw[2]);
       raw[1] = dpp_shr8_hi(raw[1], raw[3]);
       cA[0] = dpp_shr8_hi(cA[0], cA[2]);
       cA[1] = dpp_shr8_hi(cA[1], cA[3]);
+      if (NO4 > 0) {
+        lo2[0] = dpp_shr8_hi(lo2[0], lo2[2]);
+        lo2[1] = dpp_shr8_hi(lo2[1], lo2[3]);
+      }
     }
     float l2[4], cB[4];
     const float kapB = (meterB && !exact) ? kappac : 0.0f;
@@ -610,6 +683,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       l2[r] = qs2c * st[r] * raw[r];
+      if (NO4 > 0) l2[r] += lo2[r];
       cB[r] = kapB * st[r];
     }
     if (!full) {                               // tokens past the end: no weight, no bound, finite scales
@@ -962,6 +1036,16 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: exact_slot set without exact_pool/exact_scale");
     return WC_EINVAL;
   }
+  if (c.num_outliers != 0) {
+    if (c.scheme != WC_DITHER_INT8 || (c.num_outliers != 8 && c.num_outliers != 16)) {
+      set_error("wc_decode_attn_meter: the outlier bypass needs the dithered INT8 scheme and m = 8 or 16");
+      return WC_EUNSUPPORTED;
+    }
+    if (!c.outlier_ch || !c.k_outlier) {
+      set_error("wc_decode_attn_meter: outlier bypass needs outlier_ch and k_outlier");
+      return WC_EINVAL;
+    }
+  }
   if (!(sm_scale > 0.0f) || !(delta_req > 0.0 && delta_req < 1.0) || L < 1 || H < 1 || T < 1) {
     set_error("wc_decode_attn_meter: need sm_scale > 0, 0 < delta_req < 1, L, H, T >= 1");
     return WC_EINVAL;
@@ -979,12 +1063,21 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   const bool cmp = a.G <= 8;
   // one buffer resource per layer array when its byte offsets fit 32 bits
   const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * 2048u <= 0xFFFFFFFFull;
-#define WC_LAUNCH(SCH, QF, CM)                                                                        \
-  do {                                                                                           \
-    if (soff)                                                                                    \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true>), grid, dim3(kThreads), 0, st, c, a); \
-    else                                                                                         \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false>), grid, dim3(kThreads), 0, st, c, a); \
+#define WC_LAUNCH_NO(SCH, QF, CM, NO)                                                                 \
+  do {                                                                                               \
+    if (soff)                                                                                        \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true, NO>), grid, dim3(kThreads), 0, st, c, a); \
+    else                                                                                             \
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false, NO>), grid, dim3(kThreads), 0, st, c, a); \
+  } while (0)
+#define WC_LAUNCH(SCH, QF, CM)                                               \
+  do {                                                                       \
+    if (SCH != WC_DITHER_INT8 || c.num_outliers == 0)                        \
+      WC_LAUNCH_NO(SCH, QF, CM, 0);                                          \
+    else if (c.num_outliers == 8)                                            \
+      WC_LAUNCH_NO(SCH, QF, CM, (SCH == WC_DITHER_INT8 ? 2 : 0));            \
+    else                                                                     \
+      WC_LAUNCH_NO(SCH, QF, CM, (SCH == WC_DITHER_INT8 ? 4 : 0));            \
   } while (0)
   if (c.scheme == WC_DITHER_INT8) {
     if (q_dtype == WC_BF16) {
@@ -1000,6 +1093,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     }
   }
 #undef WC_LAUNCH
+#undef WC_LAUNCH_NO
   return check_launch("wc_decode_attn_meter");
 }
 

@@ -71,9 +71,10 @@ struct RowArgs {
 // Quantize the 8 channels of one lane; returns codes packed little-endian
 // in two words (INT8: offset binary code + 128) and the residual r = x^ - x.
 // words[w] holds the draws of channels 8 lane16 + 2w (low half) and + 1.
+// Bit i of `exact` marks a bypassed channel: code 0, residual 0.
 template <int SCHEME>
 __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, const uint32_t (&words)[4],
-                                       uint32_t (&packed)[2], float (&r)[8]) {
+                                       uint32_t exact, uint32_t (&packed)[2], float (&r)[8]) {
   packed[0] = packed[1] = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -89,8 +90,12 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
         const float y = add_rn(mul_rn(x[i], inv), xi);
         q = fminf(fmaxf(rintf(y), -128.0f), 127.0f);
       }
-      code = (uint32_t)((int32_t)q + 128);
       xr = s == 0.0f ? -x[i] : fmaf(s, q - xi, -x[i]);   // q - xi exact; one rounding
+      if ((exact >> i) & 1u) {
+        q = 0.0f;
+        xr = 0.0f;
+      }
+      code = (uint32_t)((int32_t)q + 128);
     } else {
       code = f32_to_e4m3(x[i]);
       xr = e4m3_to_f32(code) - x[i];
@@ -100,7 +105,10 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
   }
 }
 
-template <typename T, int SCHEME>
+// OUTL: dithered INT8 keys with the outlier bypass (bf16 input): the
+// channels of outlier_ch are excluded from the key absmax, coded 0 with a
+// zero residual, and their exact bf16 keys go to k_outlier.
+template <typename T, int SCHEME, bool OUTL>
 __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
                                                          const T* __restrict__ vin, RowArgs a) {
   const int lane16 = threadIdx.x & 15;
@@ -118,6 +126,19 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
   const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
   const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
 
+  // bypassed channels among the lane's 8 (bit i = channel 8 lane16 + i); the
+  // row's lane16 < m also copies entry lane16 of the side store
+  uint32_t omask = 0;
+  int ochan = -1;
+  if (OUTL) {
+    const int m = c.num_outliers;
+    const int32_t* oc = c.outlier_ch + ((int64_t)layer * a.hkv + g) * m;
+    for (int e = 0; e < m; ++e) {
+      const int ch = oc[e];
+      omask |= (ch >> 3) == lane16 ? 1u << (ch & 7) : 0u;
+    }
+    if (lane16 < m) ochan = oc[lane16] & 127;    // (in range even for a corrupt list)
+  }
   uint32_t words[4] = {0u, 0u, 0u, 0u};
   if (SCHEME == WC_DITHER_INT8) {
     const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
@@ -129,9 +150,10 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
     const bool isv = which == 1;
     float x[8];
     load8<T>((isv ? vin : kin) + in_off, x);
+    const uint32_t ex = isv ? 0u : omask;
     float am = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
+    for (int k = 0; k < 8; ++k) am = fmaxf(am, ((ex >> k) & 1u) ? 0.0f : fabsf(x[k]));
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, shfl_xor(am, m));
     float s = 0.0f, inv = 0.0f;
@@ -141,7 +163,7 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
     }
     uint32_t packed[2];
     float r[8];
-    quant8<SCHEME>(x, s, inv, words, packed, r);
+    quant8<SCHEME>(x, s, inv, words, ex, packed, r);
     if (!isv) {
       float ss = 0.0f;
 #pragma unroll
@@ -156,6 +178,9 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
         *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
         if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = w;
         if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.k_scale[pg * 16 + off] = s;
+        if (OUTL && ochan >= 0)
+          c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] =
+              reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
       }
     } else if (live) {
       // channel 8 lane16 + k of token off: half k / 4, token group off / 4,
@@ -286,6 +311,49 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
   }
 }
 
+// ---------------------------------------------------------------- outlier channels
+// One workgroup of 128 threads per (KV head, layer): thread c accumulates
+// E_c = sum_t x_{t,c}^2 in float32 in token order (loads eight tokens ahead),
+// then ranks the channels by (E desc, c asc) through LDS; the m first are
+// written in ascending channel order.
+template <typename T>
+__global__ void __launch_bounds__(128) outlier_select_kernel(const T* __restrict__ x, int64_t n_tok, int hkv,
+                                                             int64_t layer_stride, int m, int32_t* out) {
+  __shared__ float e[128];
+  __shared__ int sel[128];
+  const int c = threadIdx.x, g = blockIdx.x, l = blockIdx.y;
+  const T* p = x + (int64_t)l * layer_stride + (int64_t)g * 128 + c;
+  const int64_t stride = (int64_t)hkv * 128;
+  float acc = 0.0f;
+  int64_t t = 0;
+  for (; t + 8 <= n_tok; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ldf<T>(p + (t + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = add_rn(acc, mul_rn(v[u], v[u]));
+  }
+  for (; t < n_tok; ++t) {
+    const float v = ldf<T>(p + t * stride);
+    acc = add_rn(acc, mul_rn(v, v));
+  }
+  if (acc != acc) acc = INFINITY;              // NaN ranks as +inf: the order stays total
+  e[c] = acc;
+  __syncthreads();
+  int rank = 0;
+  for (int o = 0; o < 128; ++o) {
+    const float eo = e[o];
+    rank += (eo > acc || (eo == acc && o < c)) ? 1 : 0;
+  }
+  sel[c] = rank < m ? 1 : 0;
+  __syncthreads();
+  if (rank < m) {
+    int at = 0;
+    for (int o = 0; o < c; ++o) at += sel[o];
+    if (at < m) out[((int64_t)l * hkv + g) * m + at] = c;
+  }
+}
+
 // ---------------------------------------------------------------- dither fill (test hook)
 __global__ void dither_fill_kernel(uint32_t key, int64_t pos0, int64_t n_pos, uint16_t* out) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -344,21 +412,38 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
       set_error("wc_write_kv: INT8 cache needs k_scale and v_scale");
       return WC_EINVAL;
     }
+    if (c.num_outliers != 0) {
+      if (c.scheme != WC_DITHER_INT8 || (c.num_outliers != 8 && c.num_outliers != 16)) {
+        set_error("wc_write_kv: the outlier bypass needs the dithered INT8 scheme and m = 8 or 16");
+        return WC_EUNSUPPORTED;
+      }
+      if (in_dtype != WC_BF16) {
+        set_error("wc_write_kv: the outlier bypass stores bf16 keys: input must be WC_BF16");
+        return WC_EUNSUPPORTED;
+      }
+      if (!c.outlier_ch || !c.k_outlier) {
+        set_error("wc_write_kv: outlier bypass needs outlier_ch and k_outlier");
+        return WC_EINVAL;
+      }
+    }
     const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
     dim3 grid((unsigned)((rows + 15) / 16));
     if (c.scheme == WC_DITHER_INT8) {
-      if (in_dtype == WC_BF16)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8>), grid, dim3(256), 0, st, c,
+      if (c.num_outliers != 0)
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8, true>), grid, dim3(256), 0, st, c,
+                           (const uint16_t*)k, (const uint16_t*)v, a);
+      else if (in_dtype == WC_BF16)
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c,
                            (const uint16_t*)k, (const uint16_t*)v, a);
       else
-        hipLaunchKernelGGL((write_rows_kernel<float, WC_DITHER_INT8>), grid, dim3(256), 0, st, c,
+        hipLaunchKernelGGL((write_rows_kernel<float, WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c,
                            (const float*)k, (const float*)v, a);
     } else {
       if (in_dtype == WC_BF16)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_FP8_E4M3>), grid, dim3(256), 0, st, c,
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c,
                            (const uint16_t*)k, (const uint16_t*)v, a);
       else
-        hipLaunchKernelGGL((write_rows_kernel<float, WC_FP8_E4M3>), grid, dim3(256), 0, st, c,
+        hipLaunchKernelGGL((write_rows_kernel<float, WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c,
                            (const float*)k, (const float*)v, a);
     }
     return check_launch("wc_write_kv");
@@ -383,6 +468,35 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
   }
   set_error("wc_write_kv: unknown scheme %d", c.scheme);
   return WC_EUNSUPPORTED;
+}
+
+extern "C" int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, int num_kv_heads,
+                                 int64_t layer_stride, int m, int32_t* channels, void* stream) {
+  if ((!x && n_tok > 0) || !channels) {
+    set_error("wc_outlier_select: null pointer");
+    return WC_EINVAL;
+  }
+  if (n_layers < 1 || n_layers > 65535 || n_tok < 0 || num_kv_heads < 1 || m < 1 || m > 128) {
+    set_error("wc_outlier_select: need n_layers in 1..65535, n_tok >= 0, num_kv_heads >= 1, m in 1..128");
+    return WC_EINVAL;
+  }
+  if (n_layers > 1 && layer_stride < n_tok * num_kv_heads * 128) {
+    set_error("wc_outlier_select: layer_stride smaller than one layer");
+    return WC_EINVAL;
+  }
+  if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
+    set_error("wc_outlier_select: in_dtype must be WC_F32 or WC_BF16");
+    return WC_EUNSUPPORTED;
+  }
+  dim3 grid((unsigned)num_kv_heads, (unsigned)n_layers);
+  hipStream_t st = (hipStream_t)stream;
+  if (in_dtype == WC_BF16)
+    hipLaunchKernelGGL((outlier_select_kernel<uint16_t>), grid, dim3(128), 0, st, (const uint16_t*)x, n_tok,
+                       num_kv_heads, layer_stride, m, channels);
+  else
+    hipLaunchKernelGGL((outlier_select_kernel<float>), grid, dim3(128), 0, st, (const float*)x, n_tok,
+                       num_kv_heads, layer_stride, m, channels);
+  return check_launch("wc_outlier_select");
 }
 
 extern "C" int wc_dither_fill(uint64_t seed, int layer, int kv_head, int64_t pos0, int64_t n_pos, uint16_t* out,

@@ -51,6 +51,21 @@
  *  exact_pool fp16 [capacity][16][128] and exact_scale fp32 [capacity][16]:
  *            a repaired block's exact keys as fp16(k * 2^e_t) with the
  *            per-token power of two 2^-e_t in exact_scale.
+ *  outlier_ch int32 [L][Hkv][m] (m = num_outliers): the outlier-bypass
+ *            channels O of each layer and KV head, ascending and distinct.
+ *  k_outlier bf16 [L][P][Hkv][16][m]: entry i of a token is its exact key on
+ *            channel O[i].
+ *
+ * Outlier bypass (dithered INT8 keys, m = 8 or 16).  The summary reports the
+ * capacity of the certified INT8 cache with an outlier bypass too, and
+ * results per outlier budget m (capacity and negative-results paragraphs);
+ * the pages give no more detail.  Reading implemented here: the m channels of largest key
+ * energy of a (layer, KV head) (wc_outlier_select) are stored exactly in
+ * k_outlier; the row scale is the absmax of the other channels, the INT8 code
+ * on O is 0 and the residual there is 0 (so is its share of the witness); the
+ * decode adds the exact O part of each logit, and Tier B sums q_c^2 over the
+ * channels off O only (s_{c,t} = 0 on O in the Tier B paragraph's proxy).
+ * Values are not bypassed.
  */
 #ifndef WITCERT_H
 #define WITCERT_H
@@ -100,6 +115,10 @@ typedef struct {
   uint16_t* exact_pool;
   float* exact_scale;
   int64_t pool_capacity;
+  int32_t num_outliers; /* m: 0 (no bypass), 8 or 16 (dithered INT8 only)     */
+  int32_t reserved;     /* 0                                                 */
+  int32_t* outlier_ch;  /* [L][Hkv][m] when m > 0                            */
+  uint16_t* k_outlier;  /* bf16 [L][P][Hkv][16][m] when m > 0                */
 } wc_cache;
 
 /*
@@ -121,11 +140,32 @@ typedef struct {
  *  pos        device int32 [n_tok]: the token's 0-based position in its
  *             sequence (dither counter).
  *  seed       device uint64 [n_tok]: dither seed of the token's sequence.
- * Writes k_codes, v_codes, scales (or aux) and the key witness.
+ * Writes k_codes, v_codes, scales (or aux) and the key witness; with the
+ * outlier bypass (num_outliers > 0, bf16 input only) also k_outlier, reading
+ * the channels of each layer from outlier_ch.
  */
 int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
                 int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
                 const int32_t* pos, const uint64_t* seed, void* stream);
+
+/*
+ * wc_outlier_select -- the outlier-bypass channels of each (layer, KV head).
+ *
+ * For every layer l < n_layers and KV head g, the energy of channel c is
+ * E_c = sum_t x[l][t][g][c]^2 accumulated in float32 in token order
+ * (E <- fp32(E + fp32(x*x)); x*x is exact for bf16 input); a NaN energy
+ * counts as +inf.  The m channels of largest E_c, ties to the lower channel,
+ * are written in ascending order to channels[l][g][0..m-1] (the layout of
+ * wc_cache.outlier_ch).  Reading of "top-m energy channels" for the outlier
+ * bypass (see the cache layout notes above).
+ *
+ *  x        device, dtype in_dtype (WC_F32 | WC_BF16), [n_layers][n_tok][Hkv][128],
+ *           layer l at l * layer_stride elements (the calibration keys).
+ *  m        1..128.
+ *  channels device int32 [n_layers][Hkv][m].
+ */
+int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, int num_kv_heads,
+                      int64_t layer_stride, int m, int32_t* channels, void* stream);
 
 /*
  * wc_decode_attn_meter -- fused split-KV decode attention and meter.
@@ -134,7 +174,8 @@ int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, 
  * compressed attention sum_t p~_t v^_t and the meter accumulators of the
  * WitCert summary: Tier A (Theorem 2) c_t = sm_scale * sum_b ||q_b|| w_{t,b};
  * Tier B (dithered INT8 only) c_t = sqrt(2 varsigma_t^2 log(2S/delta_loc)),
- * varsigma_t^2 = sm_scale^2 s_t^2 ||q||^2 / 12, delta_loc = delta_req/(L*H*T);
+ * varsigma_t^2 = sm_scale^2 s_t^2 ||q||^2 / 12, delta_loc = delta_req/(L*H*T)
+ * (||q||^2 over the channels off O with the outlier bypass);
  * aggregated by E = sum_t p~_t expm1(c_t) (improvements list: TV <=
  * min(1, (A^2-1)/2), A = 1 + E).  Repaired blocks use exact keys and c = 0.
  *

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from certified_kv_cache_amd import inputs
-from oracle import dither, meter, quant
+from oracle import dither, meter, outlier, quant
 
 SM = 1.0 / math.sqrt(128)
 
@@ -66,15 +66,22 @@ def gather_rows(arr, layer, pt_row, S, g):
     return arr[layer, pt_row[t // 16], g, t % 16]
 
 
-def oracle_int8_cache(k32, v32, seed, layer, g, S):
-    """Oracle write of one (sequence, KV head): codes, scales, dequantized, witness."""
+def oracle_int8_cache(k32, v32, seed, layer, g, S, bypass=None):
+    """Oracle write of one (sequence, KV head): codes, scales, dequantized, witness.
+
+    bypass: outlier-bypass channels of the keys (their exact values in "side")."""
     pos = np.arange(S)
     xk = xv = dither.dither_rows(seed, layer, g, pos)
-    ck, sk, _ = quant.dither_int8(k32, xk)
+    if bypass is not None and len(bypass):
+        ck, sk, _, side = outlier.dither_int8_bypass(k32, xk, bypass)
+        khat = outlier.dequant_bypass(ck, sk, xk, side, bypass)
+    else:
+        ck, sk, _ = quant.dither_int8(k32, xk)
+        khat = quant.dequant_dither_int8(ck, sk, xk)
+        side = None
     cv, sv, _ = quant.dither_int8(v32, xv)
-    khat = quant.dequant_dither_int8(ck, sk, xk)
     vhat = quant.dequant_dither_int8(cv, sv, xv)
-    return dict(ck=ck, sk=sk, cv=cv, sv=sv, khat=khat, vhat=vhat, w=quant.witness(k32, khat))
+    return dict(ck=ck, sk=sk, cv=cv, sv=sv, khat=khat, vhat=vhat, w=quant.witness(k32, khat), side=side)
 
 
 def oracle_fp8_cache(k32, v32):

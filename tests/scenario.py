@@ -10,13 +10,13 @@ import numpy as np
 import torch
 
 from certified_kv_cache_amd import inputs
-from oracle import meter
+from oracle import meter, outlier
 from tests import helpers as H
 
 
 class Scenario:
     def __init__(self, scheme, k, v, q, ctx_lens, dtype, Hkv, layer=1, num_layers=2, seed=5, pool_capacity=0,
-                 extra_pages=3, delta=(1e-2, 28, 28, 256)):
+                 extra_pages=3, delta=(1e-2, 28, 28, 256), num_outliers=0):
         from certified_kv_cache_amd import _lib as L
         self.L = L
         self.scheme, self.dtype, self.Hkv = scheme, dtype, Hkv
@@ -28,7 +28,14 @@ class Scenario:
         self.tab, self.num_pages = inputs.page_table(seed, self.ctx, extra_pages=extra_pages)
         self.seeds = inputs.seeds(self.B, base=1000 + seed)
         self.k, self.v, self.q = k, v, q
-        self.cache = L.KVCache(scheme, num_layers, self.num_pages, Hkv, pool_capacity=pool_capacity)
+        self.cache = L.KVCache(scheme, num_layers, self.num_pages, Hkv, pool_capacity=pool_capacity,
+                               num_outliers=num_outliers)
+        # outlier bypass: the oracle's top-energy channels over all cached keys of each head
+        self.bypass = None
+        if num_outliers:
+            k32 = H.to_f32(k, dtype)
+            self.bypass = np.stack([outlier.top_energy_channels(k32[:, g], num_outliers) for g in range(Hkv)])
+            self.cache.outlier_ch[layer] = torch.from_numpy(self.bypass).cuda()
         slot, pos, seq = H.slots_for(self.tab, self.ctx)
         self.dev = dict(
             slot=torch.from_numpy(slot).cuda(), pos=torch.from_numpy(pos).cuda(),
@@ -72,11 +79,12 @@ class Scenario:
         S = int(self.ctx[b])
         k32, v32, q = self.seq_inputs(b, g)
         if self.scheme == self.L.WC_DITHER_INT8:
-            oc = H.oracle_int8_cache(k32, v32, int(self.seeds[b]), self.layer, g, S)
+            O = None if self.bypass is None else self.bypass[g]
+            oc = H.oracle_int8_cache(k32, v32, int(self.seeds[b]), self.layer, g, S, bypass=O)
             dl = meter.delta_loc(*self.delta)
             lt = math.log(2 * S / dl) if S > 0 else 0.0
             res = meter.decode_group(q, k32, oc["khat"], v32, oc["vhat"], oc["w"], sm, k_scale=oc["sk"],
-                                     log_term=lt, repaired=repaired)
+                                     log_term=lt, repaired=repaired, bypass=O)
         else:
             oc = H.oracle_fp8_cache(k32, v32)
             res = meter.decode_group(q, k32, oc["khat"], v32, oc["vhat"], oc["w"], sm, repaired=repaired)

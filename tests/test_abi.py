@@ -114,3 +114,29 @@ def test_merge_and_gate_reject_bad_arguments():
     assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
     assert L.lib.wc_dither_fill(1, 0, 0, -1, 4, p, None) == L.WC_EINVAL
     assert L.lib.wc_dither_fill(1, 0, 0, 0, 4, None, None) == L.WC_EINVAL
+
+
+def test_outlier_bypass_rejects_bad_arguments():
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    sel = L.lib.wc_outlier_select
+    assert sel(None, 1, 1, 64, 4, 0, 8, p, None) == L.WC_EINVAL
+    assert sel(p, 1, 1, 64, 4, 0, 0, p, None) == L.WC_EINVAL          # m = 0
+    assert sel(p, 1, 1, 64, 4, 0, 129, p, None) == L.WC_EINVAL        # m > d
+    assert sel(p, 1, 2, 64, 4, 10, 8, p, None) == L.WC_EINVAL         # layer stride
+    assert sel(p, 3, 1, 64, 4, 0, 8, p, None) == L.WC_EUNSUPPORTED    # dtype
+    w = L.lib.wc_write_kv
+    byp = dict(num_outliers=8, outlier_ch=16, k_outlier=16)
+    assert w(ctypes.byref(_cache(L, **byp)), 0, 1, p, p, 0, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED  # fp32 in
+    assert w(ctypes.byref(_cache(L, num_outliers=12, outlier_ch=16, k_outlier=16)), 0, 1, p, p, 1, 4, 0, p, p, p,
+             None) == L.WC_EUNSUPPORTED
+    assert w(ctypes.byref(_cache(L, scheme=1, **byp)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert w(ctypes.byref(_cache(L, num_outliers=8)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
+    d = L.lib.wc_decode_attn_meter
+    ws = L.wc_decode_workspace_bytes(2, 28, 4)
+
+    def call(cache):
+        return d(ctypes.byref(cache), 0, p, 1, 2, 28, p, 8, p, p, 0.088, 3, 1e-2, 28, 28, 256, 4, p, ws, None, None)
+
+    assert call(_cache(L, num_outliers=4, outlier_ch=16, k_outlier=16)) == L.WC_EUNSUPPORTED
+    assert call(_cache(L, num_outliers=16)) == L.WC_EINVAL                        # no side store
