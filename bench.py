@@ -116,6 +116,32 @@ def fp8_variant(w, B, S, iters):
             "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
+def outlier_variant(w, B, S, iters, m):
+    """The same workload with the outlier bypass of the keys (m exact bf16
+    channels per KV head, chosen by key energy over the first 4096 cached
+    tokens), Tier A+B with block risks."""
+    import torch
+    L = w["L"]
+    cache = L.KVCache(L.WC_DITHER_INT8, 1, w["npages"], HKV, num_outliers=m)
+    L.wc_outlier_select(w["k"][:4096].contiguous(), m, cache.outlier_ch)
+    L.wc_write_kv(cache, w["k"], w["v"], w["slot"], w["pos"], w["seed"].repeat_interleave(S))
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    sm = 1.0 / math.sqrt(D)
+
+    def decode(mask=3, with_risk=True):
+        L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    t_risk = min(time_decode(decode, iters, mask=3, with_risk=True), time_decode(decode, iters, mask=3, with_risk=True))
+    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    nb = decode_bytes(B, S, True) + B * S * HKV * 2 * m
+    del cache
+    return {"m": m, "decode_us": round(t_risk, 2), "decode_meter_off_us": round(t_off, 2), "decode_bytes": nb,
+            "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
 def make_step(w, B, S):
     import torch
     L = w["L"]
@@ -419,6 +445,7 @@ def main():
         "pages_paged_in": int(outs["paged"].item()) // 4096,
     }
     out["fp8_variant"] = fp8_variant(w, B, S, iters)
+    out["outlier_variant"] = [outlier_variant(w, B, S, iters, m) for m in (8, 16)]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
     if args.copy_ref:

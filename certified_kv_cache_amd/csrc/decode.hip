@@ -325,16 +325,19 @@ constexpr int kDepth = WC_PREFETCH_DEPTH;
 #ifndef WC_DECODE_MIN_BLOCKS_BF16
 #define WC_DECODE_MIN_BLOCKS_BF16 3
 #endif
-template <bool QF32>
+#ifndef WC_DECODE_MIN_BLOCKS_OUTL
+#define WC_DECODE_MIN_BLOCKS_OUTL 3
+#endif
+template <bool QF32, int NO4>
 constexpr int decode_waves_per_simd() {
-  return QF32 ? 2 : WC_DECODE_MIN_BLOCKS_BF16;
+  return QF32 ? 2 : NO4 > 0 ? WC_DECODE_MIN_BLOCKS_OUTL : WC_DECODE_MIN_BLOCKS_BF16;
 }
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 // NO4: outlier bypass with m = 4 NO4 exact key channels (0 = none).
 template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<QF32>())))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<QF32, NO4>())))
 decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
