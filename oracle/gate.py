@@ -20,6 +20,15 @@ so the gate works on E.  Per (sequence, KV head) with its G query heads:
    X_h - sum_{j in prefix} rho_fx[h, j] <= T; a budget caps the prefix.
 
 All of it is integer arithmetic, so the decision is exact given rho_fx.
+
+The tanh gate (the comparison the summary's page-in paragraph makes against
+the certificate): the tanh bound tanh(max_t c_t / 2) (oracle/meter.py) is
+<= tau for every head exactly when no unrepaired token has
+c_t > c* = 2 artanh(tau), so it repairs every unrepaired block whose largest
+per-token bound over the group's heads exceeds c*, ranked by that value
+(descending, ties to the lower block), capped by the budget.  c* and the
+comparisons are float32, the precision of the per-block maxima the kernel
+hands over (its decision is taken on those values).
 """
 import math
 
@@ -75,3 +84,24 @@ def select(rho_fx, repaired, T, budget=-1):
         for h in range(G):
             rem[h] -= rho[h][j]
     return chosen
+
+
+def tanh_threshold_f32(tau):
+    """c* = 2 artanh(tau) rounded to float32; +inf for tau >= 1 (the bound never exceeds 1)."""
+    if tau >= 1.0:
+        return np.float32(np.inf)
+    return np.float32(2.0 * math.atanh(float(tau)))
+
+
+def select_tanh(cmax, repaired, tau, budget=-1):
+    """Blocks the tanh gate repairs, in rank order, for one (sequence, KV head).
+
+    cmax: float32 [G, P] per-block largest bound of each head; repaired: bool [P].
+    """
+    cm = np.max(np.asarray(cmax, dtype=np.float32), axis=0) if len(cmax) else np.zeros(0, np.float32)
+    cs = tanh_threshold_f32(tau)
+    cand = [j for j in range(cm.shape[0]) if not repaired[j] and cm[j] > cs]
+    cand.sort(key=lambda j: (-float(cm[j]), j))
+    if budget >= 0:
+        cand = cand[:budget]
+    return cand

@@ -18,6 +18,14 @@ Sources (WitCert pages):
   (summary implementation paragraph; paperswithlean Figure 2 caption).
 * Gate risk per block (summary implementation paragraph; Figure 5
   caption): the block's share of the meter.
+* The deterministic tanh bound that the certificate is compared against
+  (summary, page-in paragraph; paperswithlean results and the coverage
+  table, where it is the delta = 0 reference).  The pages give no formula.
+  Derivation used here: if every logit moves by eps_t with |eps_t| <= c_t,
+  the log-ratio log(p~_t / p_t) spans at most 2 max_t c_t, and a log-ratio
+  range D gives TV <= tanh(D / 4) (attained by two groups of tokens at the
+  two ends of the range), so TV <= tanh(max_t c_t / 2).  It is evaluated per
+  tier: with Tier A's c it is deterministic (delta = 0).
 
 Readings (the design doc lists them):
 
@@ -97,6 +105,13 @@ def tv(p, p_tilde):
     return 0.5 * np.sum(np.abs(p - p_tilde), axis=-1)
 
 
+def tanh_bound(c):
+    """TV <= tanh(max_t c_t / 2) for per-token logit bounds c [..., S] (0 if S = 0)."""
+    c = np.asarray(c, dtype=np.float64)
+    cm = np.max(c, axis=-1, initial=0.0)
+    return np.tanh(0.5 * cm)
+
+
 def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
                  repaired=None, page_size=16, gate_tier="auto", num_bands=8, bypass=None):
     """Decode of the query heads sharing one KV head, over S cached tokens.
@@ -108,6 +123,8 @@ def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
       o_tilde [G, d]  compressed output sum_t p~_t v^_t (what the GPU returns)
       lse [G]         log sum_t exp(l~_t)
       E_A, R_A [G]    Tier A meter;  E_B, R_B [G] Tier B (NaN if no k_scale)
+      T_A, T_B [G]    tanh bounds tanh(max_t c_t / 2) of each tier (T_B NaN if no k_scale)
+      block_cmax [G, P]  per page max of the gate tier's c (the tanh gate's input)
       tv_true [G]     TV between exact and compressed attention
       o_exact [G, d]  exact attention output
       a, u [G, S]     per-token bounds; eps [G, S] = |l~ - l|
@@ -141,8 +158,12 @@ def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
     pad = P * page_size - S
     contrib = np.concatenate([contrib, np.zeros((q.shape[0], pad))], axis=1)
     block_risk = contrib.reshape(q.shape[0], P, page_size).sum(-1)
+    cpad = np.concatenate([cg, np.zeros((q.shape[0], pad))], axis=1)
+    block_cmax = cpad.reshape(q.shape[0], P, page_size).max(-1)
     return dict(o_tilde=pt @ np.asarray(vhat, dtype=np.float64), lse=lse,
                 E_A=E_A, R_A=R_A, E_B=E_B, R_B=R_B, tv_true=tv(p, pt),
+                T_A=tanh_bound(a), T_B=tanh_bound(u) if use_b else np.full(q.shape[0], np.nan),
+                block_cmax=block_cmax,
                 o_exact=p @ np.asarray(v, dtype=np.float64), a=a, u=u,
                 eps=np.abs(l_tilde - l_exact), block_risk=block_risk,
                 p_tilde=pt, p=p)
@@ -154,10 +175,11 @@ def split_ranges(num_pages, n_split):
 
 
 def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16):
-    """Per-split partials (m, l, o, N_A, N_B) of one KV head's query group.
+    """Per-split partials (m, l, o, N_A, N_B, C_A, C_B) of one KV head's query group.
 
     m = max l~ in the split, l = sum exp(l~ - m), o = sum exp(l~ - m) v^,
-    N_X = sum exp(l~ - m) expm1(c_X).  Empty splits have m = -inf, l = 0.
+    N_X = sum exp(l~ - m) expm1(c_X), C_X = max c_X over the split's tokens.
+    Empty splits have m = -inf, l = 0, C_X = 0.
     c_a, c_b: [G, S] per-token bounds (already zero on repaired tokens).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -170,14 +192,15 @@ def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16):
         G = q.shape[0]
         if t1 <= t0:
             parts.append(dict(m=np.full(G, -np.inf), l=np.zeros(G), o=np.zeros((G, vhat.shape[1])),
-                              N_A=np.zeros(G), N_B=np.zeros(G)))
+                              N_A=np.zeros(G), N_B=np.zeros(G), C_A=np.zeros(G), C_B=np.zeros(G)))
             continue
         ls = l_tilde[:, t0:t1]
         m = np.max(ls, axis=-1)
         e = np.exp(ls - m[:, None])
         parts.append(dict(m=m, l=e.sum(-1), o=e @ np.asarray(vhat[t0:t1], dtype=np.float64),
                           N_A=np.sum(e * np.expm1(c_a[:, t0:t1]), -1),
-                          N_B=np.sum(e * np.expm1(c_b[:, t0:t1]), -1)))
+                          N_B=np.sum(e * np.expm1(c_b[:, t0:t1]), -1),
+                          C_A=np.max(c_a[:, t0:t1], -1), C_B=np.max(c_b[:, t0:t1], -1)))
     return parts
 
 
@@ -185,7 +208,8 @@ def lse_merge(parts):
     """Merge split partials by log-sum-exp: output, LSE and both meters.
 
     M = max_s m_s, w_s = exp(m_s - M), L = sum w_s l_s, o = sum w_s o_s / L,
-    E_X = sum w_s N_X,s / L, LSE = M + log L, R_X = E_X (1 + E_X / 2).
+    E_X = sum w_s N_X,s / L, LSE = M + log L, R_X = E_X (1 + E_X / 2),
+    T_X = tanh(max_s C_X,s / 2).
     """
     m = np.stack([p["m"] for p in parts])
     M = np.max(m, axis=0)
@@ -199,6 +223,9 @@ def lse_merge(parts):
     Ls = np.where(L > 0, L, 1.0)
     E_A = np.where(L > 0, NA / Ls, 0.0)
     E_B = np.where(L > 0, NB / Ls, 0.0)
+    CA = np.max(np.stack([p["C_A"] for p in parts]), axis=0)
+    CB = np.max(np.stack([p["C_B"] for p in parts]), axis=0)
     return dict(o=np.where((L > 0)[:, None], o / Ls[:, None], 0.0),
                 lse=np.where(L > 0, M + np.log(Ls), -np.inf),
-                E_A=E_A, R_A=E_A * (1 + 0.5 * E_A), E_B=E_B, R_B=E_B * (1 + 0.5 * E_B))
+                E_A=E_A, R_A=E_A * (1 + 0.5 * E_A), E_B=E_B, R_B=E_B * (1 + 0.5 * E_B),
+                T_A=np.tanh(0.5 * CA), T_B=np.tanh(0.5 * CB))
