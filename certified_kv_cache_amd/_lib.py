@@ -16,8 +16,8 @@ LIB_PATH = os.environ.get("WITCERT_LIB") or os.path.join(_HERE, "libwitcert.so")
 WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
 WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2 = 0, 1, 2
 WC_F32, WC_BF16 = 0, 1
-WC_METER_A, WC_METER_B = 1, 2
-PARTIAL = 132
+WC_METER_A, WC_METER_B, WC_BLOCK_CMAX = 1, 2, 4
+PARTIAL = 136
 
 _c_void_p = ctypes.c_void_p
 _i32, _i64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
@@ -49,11 +49,13 @@ def _load():
         "wc_decode_attn_meter": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
                                  P, P, ctypes.c_float, ctypes.c_uint, ctypes.c_double, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P, P],
-        "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P],
+        "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P],
         "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
         "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
+        "wc_gate_pagein_tanh": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_double,
+                                _i64, P, P, P, P, P, ctypes.c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -71,8 +73,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
-           "wc_gate_pagein", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select", "wc_last_error",
-           "wc_version"]
+           "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select",
+           "wc_last_error", "wc_version"]
 
 
 def _check(fn, code):
@@ -184,9 +186,10 @@ def wc_decode_attn_meter(cache, layer, q, page_table, ctx_len, seed, partials, s
         _ptr(partials), partials.numel() * partials.element_size(), _ptr(block_logrisk), _stream(stream)))
 
 
-def wc_lse_merge(partials, B, Hq, n_split, o, lse, meter_a=None, meter_b=None, stream=None):
+def wc_lse_merge(partials, B, Hq, n_split, o, lse, meter_a=None, meter_b=None, tanh_a=None, tanh_b=None,
+                 stream=None):
     _check("wc_lse_merge", lib.wc_lse_merge(_ptr(partials), B, Hq, n_split, _ptr(o), _ptr(lse), _ptr(meter_a),
-                                            _ptr(meter_b), _stream(stream)))
+                                            _ptr(meter_b), _ptr(tanh_a), _ptr(tanh_b), _stream(stream)))
 
 
 def wc_gate_workspace_bytes(B, Hkv, max_pages):
@@ -213,6 +216,15 @@ def wc_outlier_select(x, m, channels, stream=None):
     _check("wc_outlier_select", lib.wc_outlier_select(_ptr(x), _dtype_code(x), n_layers, n_tok, hkv,
                                                       n_tok * hkv * x.shape[3], m, _ptr(channels),
                                                       _stream(stream)))
+
+
+def wc_gate_pagein_tanh(cache, layer, block_cmax, page_table, ctx_len, tau, host_exact_k, pool_used, bytes_paged,
+                        workspace, budget_blocks=-1, selected=None, stream=None):
+    B, Hq, max_pages = block_cmax.shape
+    _check("wc_gate_pagein_tanh", lib.wc_gate_pagein_tanh(
+        cache.ref(), layer, _ptr(block_cmax), B, Hq, _ptr(page_table), max_pages, _ptr(ctx_len), float(tau),
+        int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged), _ptr(selected),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def wc_dither_fill(seed, layer, kv_head, pos0, n_pos, out, stream=None):

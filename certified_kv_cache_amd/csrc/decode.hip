@@ -4,6 +4,10 @@
 // Tier B paragraph: u_t = sqrt(2 varsigma_t^2 log(2S/delta_loc)),
 // varsigma_t^2 = (1/d) sum_c q_c^2 s_{c,t}^2 / 12, delta_loc = delta_req/(L H T);
 // improvements list: TV <= min(1, (A^2 - 1)/2), A = sum_t p~_t e^{c_t};
+// page-in paragraph: the deterministic tanh bound the certificate is compared
+// with, taken here as TV <= tanh(max_t c_t / 2) (a logit move of at most c_t
+// per token bounds the log-ratio range by 2 max c; the range D gives
+// TV <= tanh(D / 4)); the kernel carries max_t c_t per tier;
 // implementation paragraph and the paperswithlean Figure 2 caption: output and
 // meter in one data pass, LSE-merged across KV splits.
 //
@@ -48,7 +52,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kNW = WC_DECODE_WAVES;
 constexpr int kThreads = 64 * kNW;
-constexpr int kPartial = 132;     // floats per (b, h, split) partial
+// floats per (b, h, split) partial: m, l, N_A, N_B, o[128], C_A, C_B, 0, 0
+constexpr int kPartial = 136;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -351,6 +356,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const bool meterA = (a.mask & WC_METER_A) != 0;
   const bool meterB = SCHEME == WC_DITHER_INT8 && (a.mask & WC_METER_B) != 0;
   const bool risk = a.block_logrisk != nullptr;
+  const bool riskmax = (a.mask & WC_BLOCK_CMAX) != 0;   // block output: max c instead of log risk
 
   // ---------------------------------------------------------------- query prep
   // lane (n, k) holds channels 32k..32k+31 of head n.
@@ -497,6 +503,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 
   // ---------------------------------------------------------------- state
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
+  float ca_max = 0.0f, cb_max = 0.0f;          // largest per-token bound of each tier (tanh bound)
   f4 O[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) O[t] = f4{0.f, 0.f, 0.f, 0.f};
@@ -763,14 +770,28 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       }
       na += ea;
       nb += eb;
+#pragma unroll
+      for (int r = 0; r < NV; ++r) {
+        ca_max = vmax(ca_max, cA[r]);
+        cb_max = vmax(cb_max, cB[r]);
+      }
     }
     if (risk) {
       // block risks go through a per-wave LDS tile [head][16 pages] and out
       // as 16-page runs of each head's row
-      float er = meterB ? eb : ea;
-      if (CMP) er += dpp_ror8(er);
-      er = sum4k(er);
-      if (kq == 0 && n < G) sR[n][i & 15] = er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
+      if (riskmax) {                           // the tanh gate's input: the block's largest c
+        float cm = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NV; ++r) cm = vmax(cm, meterB ? cB[r] : cA[r]);
+        if (CMP) cm = vmax(cm, dpp_ror8(cm));
+        cm = max4k(cm);
+        if (kq == 0 && n < G) sR[n][i & 15] = cm;
+      } else {
+        float er = meterB ? eb : ea;
+        if (CMP) er += dpp_ror8(er);
+        er = sum4k(er);
+        if (kq == 0 && n < G) sR[n][i & 15] = er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
+      }
     }
 
     // ---------------- PV: O^T += Vhat^T P^T
@@ -869,13 +890,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     l_run += dpp_ror8(l_run);
     na += dpp_ror8(na);
     nb += dpp_ror8(nb);
+    ca_max = vmax(ca_max, dpp_ror8(ca_max));
+    cb_max = vmax(cb_max, dpp_ror8(cb_max));
   }
   l_run = sum4k(l_run);
   na = sum4k(na);
   nb = sum4k(nb);
+  ca_max = max4k(ca_max);
+  cb_max = max4k(cb_max);
   __syncthreads();                             // the dither tiles are reused below
   float (*sO)[16][128] = reinterpret_cast<float (*)[16][128]>(smem);
-  __shared__ float sM[kNW][16][4];
+  __shared__ float sM[kNW][16][6];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -885,6 +910,8 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     sM[wave][n][1] = l_run;
     sM[wave][n][2] = na;
     sM[wave][n][3] = nb;
+    sM[wave][n][4] = ca_max;
+    sM[wave][n][5] = cb_max;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < G * kPartial; e += kThreads) {
@@ -895,6 +922,11 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     float val = 0.0f;
     if (f == 0) {
       val = M;
+    } else if (f >= 132) {                     // largest bounds: max over the waves
+      if (f < 134) {
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) val = fmaxf(val, sM[w][hn][f - 128]);
+      }
     } else if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kNW; ++w) {
@@ -924,24 +956,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ part, int n_split, float* o,
-                                                   float* lse, float* meter_a, float* meter_b) {
+                                                   float* lse, float* meter_a, float* meter_b, float* tanh_a,
+                                                   float* tanh_b) {
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* pp = part + (int64_t)bh * n_split * kPartial;
   float M = -INFINITY;
   for (int s = lane; s < n_split; s += 64) M = fmaxf(M, pp[s * kPartial]);
   M = wave_max(M);
   auto weight = [&](float ms) { return (ms == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(ms - M); };
-  float L = 0.f, NA = 0.f, NB = 0.f;
+  float L = 0.f, NA = 0.f, NB = 0.f, CA = 0.f, CB = 0.f;
   for (int s = lane; s < n_split; s += 64) {
     const float4 q = *reinterpret_cast<const float4*>(pp + s * kPartial);
+    const float2 cm = *reinterpret_cast<const float2*>(pp + s * kPartial + 132);
     const float w = weight(q.x);
     L = fmaf(w, q.y, L);
     NA = fmaf(w, q.z, NA);
     NB = fmaf(w, q.w, NB);
+    CA = fmaxf(CA, cm.x);
+    CB = fmaxf(CB, cm.y);
   }
   L = wave_sum(L);
   NA = wave_sum(NA);
   NB = wave_sum(NB);
+  CA = wave_max(CA);
+  CB = wave_max(CB);
   float o0 = 0.f, o1 = 0.f;
   int s = 0;
   for (; s + 8 <= n_split; s += 8) {
@@ -972,6 +1010,8 @@ __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ par
     const float ea = NA * inv, eb = NB * inv;
     if (meter_a) meter_a[bh] = ea * (1.0f + 0.5f * ea);
     if (meter_b) meter_b[bh] = eb * (1.0f + 0.5f * eb);
+    if (tanh_a) tanh_a[bh] = tanhf(0.5f * CA);
+    if (tanh_b) tanh_b[bh] = tanhf(0.5f * CB);
   }
 }
 
@@ -1011,7 +1051,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: bad B/Hq/max_pages/n_split/layer");
     return WC_EINVAL;
   }
-  if (meter_mask & ~(WC_METER_A | WC_METER_B)) {
+  if (meter_mask & ~(WC_METER_A | WC_METER_B | WC_BLOCK_CMAX)) {
     set_error("wc_decode_attn_meter: unknown meter_mask bits");
     return WC_EINVAL;
   }
@@ -1025,6 +1065,10 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   }
   if (block_logrisk && !(meter_mask & WC_METER_A)) {
     set_error("wc_decode_attn_meter: block risks need the meter on");
+    return WC_EINVAL;
+  }
+  if ((meter_mask & WC_BLOCK_CMAX) && !block_logrisk) {
+    set_error("wc_decode_attn_meter: WC_BLOCK_CMAX needs the block output");
     return WC_EINVAL;
   }
   if (c.scheme == WC_DITHER_INT8 && (!seed || !c.k_scale || !c.v_scale)) {
@@ -1101,13 +1145,13 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
 }
 
 extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
-                            float* meter_a, float* meter_b, void* stream) {
+                            float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, void* stream) {
   if (!partials || !o || !lse || B < 0 || Hq < 1 || n_split < 1 || n_split > 1024) {
     set_error("wc_lse_merge: bad arguments");
     return WC_EINVAL;
   }
   if (B == 0) return WC_OK;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split, o,
-                     lse, meter_a, meter_b);
+                     lse, meter_a, meter_b, tanh_a, tanh_b);
   return check_launch("wc_lse_merge");
 }

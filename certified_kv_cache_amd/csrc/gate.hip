@@ -19,6 +19,12 @@
 // order hands out exact-pool slots deterministically; (4) copy each selected
 // block from pinned host memory (zero-copy reads), store it as fp16 with a
 // per-token power of two, zero its witness, mark it.
+//
+// The tanh gate (the page-in comparison of the summary): the bound
+// tanh(max_t c_t / 2) is <= tau for every head exactly when no unrepaired
+// token has c_t > c* = 2 artanh(tau), so kernel (2) is replaced by one that
+// takes every unrepaired block whose largest bound over the group's heads
+// exceeds c*, ranked by that bound; (3) and (4) are shared.
 #include <math.h>
 
 #include "wc_common.h"
@@ -109,6 +115,27 @@ __global__ void __launch_bounds__(256) gate_risk_kernel(wc_cache c, GateArgs a) 
     a.xpart[((int64_t)b * a.Hq + g * G + t) * a.nchunk + chunk] = wsum[0][t] + wsum[1][t] + wsum[2][t] + wsum[3][t];
 }
 
+// Bitonic sort of keys[0 .. np2) (np2 a power of two) in LDS, descending;
+// 256 threads, every thread calls it.
+__device__ void sort_desc(uint64_t* keys, int np2, int t) {
+  for (int kk = 2; kk <= np2; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = t; i < np2; i += 256) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const bool desc = (i & kk) == 0;
+          const uint64_t x = keys[i], y = keys[ixj];
+          if (desc ? (x < y) : (x > y)) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a) {
   __shared__ uint64_t keys[kMaxSortPages];
   __shared__ uint64_t red[256];
@@ -158,22 +185,7 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
     keys[j] = k;
   }
   __syncthreads();
-  for (int kk = 2; kk <= np2; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < np2; i += 256) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const bool desc = (i & kk) == 0;
-          const uint64_t x = keys[i], y = keys[ixj];
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  sort_desc(keys, np2, t);
   // shortest prefix: per head, k_h = #{i : exclusive prefix sum < X_h - T}
   if (t == 0) kneed = 0;
   __syncthreads();
@@ -215,6 +227,49 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
     __syncthreads();
   }
   int k = kneed;
+  if (a.budget >= 0 && k > a.budget) k = (int)a.budget;
+  for (int i = t; i < k; i += 256) a.sel[((int64_t)b * hkv + g) * a.max_pages + i] = 65535 - (int)(keys[i] & 0xFFFF);
+  if (t == 0) a.count[b * hkv + g] = k;
+}
+
+// Tanh gate selection, one workgroup per (sequence, KV head): candidates are
+// the unrepaired blocks with max_h cmax[h][j] > c* (float32 comparison); sort
+// key = the float's bits (monotone for values >= 0) << 16 | (65535 - j).
+__global__ void __launch_bounds__(256) gate_tanh_select_kernel(wc_cache c, GateArgs a, const float* cmax,
+                                                               float cstar) {
+  __shared__ uint64_t keys[kMaxSortPages];
+  __shared__ int ncand[256];
+  const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int hkv = c.num_kv_heads;
+  const int P = (a.ctx_len[b] + 15) >> 4;
+  const int G = a.G;
+  const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;
+  int np2 = 1;
+  while (np2 < P) np2 <<= 1;
+  int mine = 0;
+  for (int j = t; j < np2; j += 256) {
+    uint64_t k = 0;
+    if (j < P) {
+      const int phys = a.page_table[(int64_t)b * a.max_pages + j];
+      if (c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] < 0) {
+        float m = 0.0f;
+        for (int n = 0; n < G; ++n) m = fmaxf(m, cmax[row0 + (int64_t)n * a.max_pages + j]);
+        if (m > cstar) {
+          k = ((uint64_t)__float_as_uint(m) << 16) | (uint64_t)(65535 - j);
+          ++mine;
+        }
+      }
+    }
+    keys[j] = k;
+  }
+  ncand[t] = mine;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (t < s2) ncand[t] += ncand[t + s2];
+    __syncthreads();
+  }
+  int k = ncand[0];
+  if (k > 0) sort_desc(keys, np2, t);
   if (a.budget >= 0 && k > a.budget) k = (int)a.budget;
   for (int i = t; i < k; i += 256) a.sel[((int64_t)b * hkv + g) * a.max_pages + i] = 65535 - (int)(keys[i] & 0xFFFF);
   if (t == 0) a.count[b * hkv + g] = k;
@@ -323,6 +378,92 @@ extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
   return (size_t)B * Hkv * 16 * nchunk * 8 + (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 3 * 4;
 }
 
+namespace {
+// Checks shared by both gates; fills the workspace carve-up.
+int gate_prepare(const char* fn, const wc_cache* cache, int layer, int B, int Hq, int max_pages,
+                 const void* host_exact_k, void* workspace, size_t ws_bytes, void** dev_host, GateArgs& a) {
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.page_size != 16 || c.num_kv_heads < 1 || c.num_bands != 8) {
+    set_error("%s: need head_dim 128, 8 bands, 16-token pages", fn);
+    return WC_EUNSUPPORTED;
+  }
+  if (!c.exact_slot || !c.exact_pool || !c.exact_scale || !c.witness || c.pool_capacity < 0) {
+    set_error("%s: cache needs exact_slot, exact_pool, exact_scale and witness", fn);
+    return WC_EINVAL;
+  }
+  if (B < 0 || Hq < 1 || Hq % c.num_kv_heads != 0 || Hq / c.num_kv_heads > 16 || max_pages < 1 ||
+      max_pages > kMaxSortPages || layer < 0 || layer >= c.num_layers) {
+    set_error("%s: bad B/Hq/max_pages (<= %d)/layer", fn, kMaxSortPages);
+    return WC_EINVAL;
+  }
+  if (ws_bytes < wc_gate_workspace_bytes(B, c.num_kv_heads, max_pages)) {
+    set_error("%s: workspace too small", fn);
+    return WC_EWORKSPACE;
+  }
+  // host store: translate to the device view of the pinned allocation
+  *dev_host = nullptr;
+  if (hipHostGetDevicePointer(dev_host, const_cast<void*>(host_exact_k), 0) != hipSuccess || !*dev_host) {
+    (void)hipGetLastError();
+    *dev_host = const_cast<void*>(host_exact_k);   // unified addressing: same pointer
+  }
+  const int hkv = c.num_kv_heads;
+  char* ws = (char*)workspace;
+  const int nchunk = (max_pages + 255) / 256;
+  a.xpart = (uint64_t*)ws;
+  ws += (size_t)B * hkv * 16 * nchunk * 8;
+  a.sel = (int32_t*)ws;
+  ws += (size_t)B * hkv * max_pages * 4;
+  a.count = (int32_t*)ws;
+  a.base = a.count + B * hkv;
+  a.take = a.base + B * hkv;
+  a.B = B;
+  a.Hq = Hq;
+  a.G = Hq / hkv;
+  a.max_pages = max_pages;
+  a.layer = layer;
+  a.nchunk = nchunk;
+  return WC_OK;
+}
+}  // namespace
+
+extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float* block_cmax, int B, int Hq,
+                                   const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
+                                   int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
+                                   int64_t* bytes_paged, int32_t* selected, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  if (!cache || !block_cmax || !page_table || !ctx_len || !host_exact_k || !pool_used || !bytes_paged ||
+      !workspace) {
+    set_error("wc_gate_pagein_tanh: null pointer");
+    return WC_EINVAL;
+  }
+  if (!(tau >= 0.0)) {
+    set_error("wc_gate_pagein_tanh: need tau >= 0");
+    return WC_EINVAL;
+  }
+  GateArgs a{};
+  void* dev_host = nullptr;
+  if (int e = gate_prepare("wc_gate_pagein_tanh", cache, layer, B, Hq, max_pages, host_exact_k, workspace, ws_bytes,
+                           &dev_host, a))
+    return e;
+  if (B == 0) return WC_OK;
+  const wc_cache& c = *cache;
+  a.page_table = page_table;
+  a.ctx_len = ctx_len;
+  a.budget = budget_blocks;
+  const float cstar = tau >= 1.0 ? INFINITY : (float)(2.0 * atanh(tau));
+  const int hkv = c.num_kv_heads;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(gate_tanh_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a, block_cmax,
+                     cstar);
+  if (int e = check_launch("wc_gate_pagein_tanh select")) return e;
+  hipLaunchKernelGGL(gate_assign_kernel, dim3(1), dim3(256), 0, st, a, B * hkv, c.pool_capacity, pool_used,
+                     bytes_paged, selected);
+  if (int e = check_launch("wc_gate_pagein_tanh assign")) return e;
+  hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,
+                     (const uint16_t*)dev_host);
+  return check_launch("wc_gate_pagein_tanh copy");
+}
+
 extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse, int B,
                               int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
                               int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
@@ -333,49 +474,27 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
     set_error("wc_gate_pagein: null pointer");
     return WC_EINVAL;
   }
-  const wc_cache& c = *cache;
-  if (c.head_dim != 128 || c.page_size != 16 || c.num_kv_heads < 1 || c.num_bands != 8) {
-    set_error("wc_gate_pagein: need head_dim 128, 8 bands, 16-token pages");
-    return WC_EUNSUPPORTED;
-  }
-  if (!c.exact_slot || !c.exact_pool || !c.exact_scale || !c.witness || c.pool_capacity < 0) {
-    set_error("wc_gate_pagein: cache needs exact_slot, exact_pool, exact_scale and witness");
-    return WC_EINVAL;
-  }
-  if (B < 0 || Hq < 1 || Hq % c.num_kv_heads != 0 || Hq / c.num_kv_heads > 16 || max_pages < 1 ||
-      max_pages > kMaxSortPages || layer < 0 || layer >= c.num_layers) {
-    set_error("wc_gate_pagein: bad B/Hq/max_pages (<= %d)/layer", kMaxSortPages);
-    return WC_EINVAL;
-  }
   const double et = sqrt(1.0 + 2.0 * tau) - 1.0;
   if (!(tau >= 0.0) || !(et < 64.0)) {
     set_error("wc_gate_pagein: need 0 <= tau and sqrt(1 + 2 tau) - 1 < 64");
     return WC_EINVAL;
   }
-  if (ws_bytes < wc_gate_workspace_bytes(B, c.num_kv_heads, max_pages)) {
-    set_error("wc_gate_pagein: workspace too small");
-    return WC_EWORKSPACE;
-  }
-  if (B == 0) return WC_OK;
-  // host store: translate to the device view of the pinned allocation
+  GateArgs a{};
   void* dev_host = nullptr;
-  if (hipHostGetDevicePointer(&dev_host, (void*)host_exact_k, 0) != hipSuccess || !dev_host) {
-    (void)hipGetLastError();
-    dev_host = (void*)host_exact_k;           // unified addressing: same pointer
-  }
+  if (int e = gate_prepare("wc_gate_pagein", cache, layer, B, Hq, max_pages, host_exact_k, workspace, ws_bytes,
+                           &dev_host, a))
+    return e;
+  if (B == 0) return WC_OK;
+  const wc_cache& c = *cache;
   const int hkv = c.num_kv_heads;
-  char* ws = (char*)workspace;
-  uint64_t* fx = rho_fx;
-  const int nchunk = (max_pages + 255) / 256;
-  uint64_t* xpart = (uint64_t*)ws;
-  ws += (size_t)B * hkv * 16 * nchunk * 8;
-  int32_t* sel = (int32_t*)ws;
-  ws += (size_t)B * hkv * max_pages * 4;
-  int32_t* cnt = (int32_t*)ws;
-  int32_t* base = cnt + B * hkv;
-  int32_t* take = base + B * hkv;
-  GateArgs a{block_logrisk, lse, page_table, ctx_len, fx, xpart, sel, cnt, base, take, B, Hq, Hq / hkv, max_pages,
-             layer, nchunk, (uint64_t)floor(et * 1099511627776.0), budget_blocks};
+  const int nchunk = a.nchunk;
+  a.logrisk = block_logrisk;
+  a.lse = lse;
+  a.page_table = page_table;
+  a.ctx_len = ctx_len;
+  a.fx = rho_fx;
+  a.T = (uint64_t)floor(et * 1099511627776.0);
+  a.budget = budget_blocks;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(gate_risk_kernel, dim3((unsigned)nchunk, (unsigned)hkv, (unsigned)B), dim3(256), 0, st, c, a);
   if (int e = check_launch("wc_gate_pagein risk")) return e;

@@ -95,6 +95,7 @@ extern "C" {
 /* meter_mask bits. */
 #define WC_METER_A 1u
 #define WC_METER_B 2u
+#define WC_BLOCK_CMAX 4u /* block output = largest per-token bound (tanh gate) */
 
 typedef struct {
   int32_t scheme;       /* WC_DITHER_INT8 | WC_FP8_E4M3 | WC_KIVI2          */
@@ -189,13 +190,18 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *             as with the meter on.
  *  n_split    1..1024 KV splits per (sequence, KV head): split i covers blocks
  *             [i*P_b/n_split, (i+1)*P_b/n_split) of the sequence's P_b blocks.
- *  partials   device fp32 workspace [B][Hq][n_split][132]: per split
- *             (m, l, N_A, N_B, o[128]) with m the running max of the logits in
- *             log2 units, l = sum 2^(l2 - m), N_X = sum 2^(l2 - m) expm1(c_X),
- *             o = sum 2^(l2 - m) v^.  ws_bytes >= wc_decode_workspace_bytes().
+ *  partials   device fp32 workspace [B][Hq][n_split][136]: per split
+ *             (m, l, N_A, N_B, o[128], C_A, C_B, 0, 0) with m the running max
+ *             of the logits in log2 units, l = sum 2^(l2 - m),
+ *             N_X = sum 2^(l2 - m) expm1(c_X), o = sum 2^(l2 - m) v^ and
+ *             C_X = max_t c_X (for the tanh bound).
+ *             ws_bytes >= wc_decode_workspace_bytes().
  *  block_logrisk  nullable device fp32 [B][Hq][max_pages]: natural log of
  *             sum_{t in block} exp(l_t) expm1(c_t) for the gate's tier (B if
- *             requested, else A); -inf for blocks without risk.
+ *             requested, else A); -inf for blocks without risk.  With
+ *             WC_BLOCK_CMAX in meter_mask it receives instead max_{t in block}
+ *             c_t of the gate's tier (0 for repaired blocks), the input of
+ *             wc_gate_pagein_tanh.
  */
 int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_dtype, int B, int Hq,
                          const int32_t* page_table, int max_pages, const int32_t* ctx_len,
@@ -203,7 +209,7 @@ int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_
                          int L, int H, int T, int n_split, float* partials, size_t ws_bytes,
                          float* block_logrisk, void* stream);
 
-/* Bytes of the decode workspace: B * Hq * n_split * 132 * 4. */
+/* Bytes of the decode workspace: B * Hq * n_split * 136 * 4. */
 size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
 
 
@@ -216,9 +222,16 @@ size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
  *  lse      device fp32 [B][Hq]: natural-log LSE of the logits (-inf if empty).
  *  meter_a, meter_b  nullable device fp32 [B][Hq]: R = E (1 + E/2), unclamped;
  *           the TV bound is min(1, R).  meter_b is 0 when Tier B is off.
+ *  tanh_a, tanh_b    nullable device fp32 [B][Hq]: the deterministic tanh
+ *           bound tanh(max_t c_t / 2) of each tier, which the summary's
+ *           page-in paragraph compares the certificate with (the pages give
+ *           no formula; this is the bound for logits that each move by at
+ *           most c_t: the log-ratio of the two softmaxes then spans at most
+ *           2 max c, and a span D gives TV <= tanh(D/4)).  0 when the tier
+ *           is off or the sequence is empty.
  */
 int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
-                 float* meter_a, float* meter_b, void* stream);
+                 float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, void* stream);
 
 /*
  * wc_gate_pagein -- meter-driven repair from the exact backing store.
@@ -252,6 +265,27 @@ int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk,
 
 /* Bytes of the gate workspace for B sequences, Hkv heads and max_pages blocks. */
 size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages);
+
+/*
+ * wc_gate_pagein_tanh -- the tanh gate the certificate is compared with
+ * (summary, page-in paragraph: the certificate pages in less than the
+ * deterministic tanh bound).  tanh(max_t c_t / 2) <= tau for every head
+ * exactly when no unrepaired token has c_t > c* = 2 artanh(tau) (c* = +inf
+ * for tau >= 1), so per (sequence b, KV head g) it repairs every unrepaired
+ * block j with max_h block_cmax[b][h][j] > c* (float32 comparison), ranked
+ * by that value (descending, ties to the lower index), capped by
+ * budget_blocks; pool slots, page-in, witness zeroing and `selected` are as
+ * in wc_gate_pagein.
+ *
+ *  block_cmax  device fp32 [B][Hq][max_pages]: the decode's block output
+ *              with WC_BLOCK_CMAX.
+ *  workspace   as for wc_gate_pagein (wc_gate_workspace_bytes()).
+ * Requires cache->exact_slot, exact_pool, exact_scale; tau >= 0.
+ */
+int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float* block_cmax, int B, int Hq,
+                        const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
+                        int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
+                        int64_t* bytes_paged, int32_t* selected, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * wc_dither_fill -- test hook: the 16-bit dither draws k (xi = k/65536 - 1/2)

@@ -48,24 +48,25 @@ class Scenario:
                           self.dev["pos"], self.dev["tseed"], layer0=layer)
         self.offsets = np.concatenate([[0], np.cumsum(self.ctx)])
 
-    def decode(self, n_split=4, mask=3, risk=False, sm=H.SM):
+    def decode(self, n_split=4, mask=3, risk=False, sm=H.SM, cmax=False):
         L = self.L
         B, Hq = self.B, self.Hq
         part = torch.empty(L.wc_decode_workspace_bytes(B, Hq, n_split) // 4, dtype=torch.float32, device="cuda")
-        br = torch.full((B, Hq, self.tab.shape[1]), float("nan"), device="cuda") if risk else None
+        br = torch.full((B, Hq, self.tab.shape[1]), float("nan"), device="cuda") if (risk or cmax) else None
         L.wc_decode_attn_meter(self.cache, self.layer, self.dev["q"], self.dev["tab"], self.dev["ctx"],
-                               self.dev["seed"], part, sm, mask, self.delta[0], *self.delta[1:], n_split,
-                               block_logrisk=br)
+                               self.dev["seed"], part, sm, mask | (L.WC_BLOCK_CMAX if cmax else 0), self.delta[0],
+                               *self.delta[1:], n_split, block_logrisk=br)
         o = torch.empty((B, Hq, 128), device="cuda")
         lse = torch.empty((B, Hq), device="cuda")
-        ra = torch.empty((B, Hq), device="cuda")
-        rb = torch.empty((B, Hq), device="cuda")
-        L.wc_lse_merge(part, B, Hq, n_split, o, lse, ra, rb)
+        ra, rb, ta, tb = (torch.empty((B, Hq), device="cuda") for _ in range(4))
+        L.wc_lse_merge(part, B, Hq, n_split, o, lse, ra, rb, ta, tb)
         torch.cuda.synchronize()
         out = dict(o=o.cpu().numpy(), lse=lse.cpu().numpy(), R_A=ra.cpu().numpy(), R_B=rb.cpu().numpy(),
-                   part=part.cpu().numpy())
+                   T_A=ta.cpu().numpy(), T_B=tb.cpu().numpy(), part=part.cpu().numpy())
         if risk:
             out["logrisk"] = br.cpu().numpy()
+        if cmax:
+            out["cmax"] = br.cpu().numpy()
         return out
 
     def seq_inputs(self, b, g):

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_workspace_sizes():
     L = _lib()
     assert L.lib.wc_version().startswith(b"witcert")
-    assert L.wc_decode_workspace_bytes(32, 28, 16) == 32 * 28 * 16 * 132 * 4
+    assert L.wc_decode_workspace_bytes(32, 28, 16) == 32 * 28 * 16 * 136 * 4
     assert L.wc_decode_workspace_bytes(-1, 28, 16) == 0
     assert L.wc_gate_workspace_bytes(2, 4, 10) > 0
 
@@ -97,8 +97,8 @@ def test_decode_rejects_bad_arguments():
 def test_merge_and_gate_reject_bad_arguments():
     L = _lib()
     p = ctypes.c_void_p(16)
-    assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None) == L.WC_EINVAL
-    assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None) == L.WC_EINVAL
+    assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None, None, None) == L.WC_EINVAL
+    assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None, None, None) == L.WC_EINVAL
     g = L.lib.wc_gate_pagein
     c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
     wsb = L.wc_gate_workspace_bytes(2, 4, 8)
@@ -140,3 +140,25 @@ def test_outlier_bypass_rejects_bad_arguments():
 
     assert call(_cache(L, num_outliers=4, outlier_ch=16, k_outlier=16)) == L.WC_EUNSUPPORTED
     assert call(_cache(L, num_outliers=16)) == L.WC_EINVAL                        # no side store
+
+
+def test_tanh_gate_and_cmax_reject_bad_arguments():
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    g = L.lib.wc_gate_pagein_tanh
+    c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
+    wsb = L.wc_gate_workspace_bytes(2, 4, 8)
+
+    def call(cache=c, tau=0.2, mp=8, wsb=wsb, cm=p):
+        return g(cache, 0, cm, 2, 28, p, mp, p, tau, -1, p, p, p, None, p, wsb, None)
+
+    assert call(cm=None) == L.WC_EINVAL
+    assert call(tau=-0.5) == L.WC_EINVAL
+    assert call(mp=5000) == L.WC_EINVAL
+    assert call(wsb=1) == L.WC_EWORKSPACE
+    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
+    d = L.lib.wc_decode_attn_meter
+    ws = L.wc_decode_workspace_bytes(2, 28, 4)
+    cc = ctypes.byref(_cache(L))
+    assert d(cc, 0, p, 1, 2, 28, p, 8, p, p, 0.088, 3 | L.WC_BLOCK_CMAX, 1e-2, 28, 28, 256, 4, p, ws, None,
+             None) == L.WC_EINVAL                      # block maxima need the block output

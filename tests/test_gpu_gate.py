@@ -141,3 +141,73 @@ def test_gate_budget_and_pool_capacity():
             take = min(len(want), left)
             left -= take
             assert list(sel[b, g, 1:1 + sel[b, g, 0]]) == want[:take]
+
+
+def _tanh_gate(L, sc, host, cmax, tau, budget=-1):
+    B, Hq, mp = sc.B, sc.Hq, sc.tab.shape[1]
+    ws = torch.empty(L.wc_gate_workspace_bytes(B, 4, mp), dtype=torch.uint8, device="cuda")
+    pool_used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    paged = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sel = torch.full((B, 4, mp + 1), -7, dtype=torch.int32, device="cuda")
+    L.wc_gate_pagein_tanh(sc.cache, sc.layer, torch.from_numpy(cmax).cuda(), sc.dev["tab"], sc.dev["ctx"], tau, host,
+                          pool_used, paged, ws, budget_blocks=budget, selected=sel)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), int(pool_used.item()), int(paged.item())
+
+
+@pytest.mark.parametrize("scheme", ["fp8", "int8"])
+def test_tanh_gate_bit_exact_and_bound_met(scheme):
+    lens = [300, 1000, 64]
+    L, sc, host = _setup(lens, seed=61, scheme=scheme)
+    print(f"tanh gate {scheme}", flush=True)
+    mask = 1 if scheme == "fp8" else 3
+    out = sc.decode(n_split=4, mask=mask, cmax=True)
+    tkey = "T_A" if scheme == "fp8" else "T_B"
+    cm = out["cmax"]
+    for b, S in enumerate(lens):
+        P = -(-S // 16)
+        for g in range(4):
+            _, r = sc.oracle(b, g)
+            hs = slice(g * 7, (g + 1) * 7)
+            got = cm[b, hs, :P].astype(np.float64)
+            assert np.all(np.abs(got - r["block_cmax"]) <= 1e-4 * r["block_cmax"] + 1e-30), (b, g)
+            # the merged tanh bound is the tanh of the largest block value
+            assert np.allclose(out[tkey][b, hs], np.tanh(0.5 * got.max(-1)), rtol=1e-5, atol=0)
+    # a threshold that repairs part of the blocks
+    tau = float(np.median(out[tkey]))
+    rep0 = sc.cache.exact_slot.cpu().numpy()[sc.layer].copy()
+    sel, used, paged = _tanh_gate(L, sc, host, cm, tau)
+    total = 0
+    for b, S in enumerate(lens):
+        P = -(-S // 16)
+        for g in range(4):
+            want = gate.select_tanh(cm[b, g * 7:(g + 1) * 7, :P], rep0[sc.tab[b, :P], g] >= 0, tau)
+            assert list(sel[b, g, 1:1 + sel[b, g, 0]]) == want, (b, g)
+            total += len(want)
+    assert 0 < total and used == total and paged == 4096 * total
+    # the repaired cache meets the bound: every head's tanh bound is now <= tau
+    after = sc.decode(n_split=4, mask=mask)
+    assert np.all(after[tkey] <= tau * (1 + 1e-6)), (after[tkey].max(), tau)
+    # witness zeroed and exact keys in place for what was paged in
+    slots = sc.cache.exact_slot.cpu().numpy()[sc.layer]
+    wit = sc.cache.witness.cpu().numpy()[sc.layer]
+    for b in range(len(lens)):
+        for g in range(4):
+            for j in sel[b, g, 1:1 + sel[b, g, 0]]:
+                assert slots[sc.tab[b, j], g] >= 0 and np.all(wit[sc.tab[b, j], g] == 0)
+
+
+def test_tanh_gate_budget_and_no_trigger():
+    lens = [300, 200]
+    L, sc, host = _setup(lens, seed=62)
+    print("tanh gate budget", flush=True)
+    out = sc.decode(n_split=2, mask=1, cmax=True)
+    sel, used, _ = _tanh_gate(L, sc, host, out["cmax"], 1.0)       # tanh < 1: never triggers
+    assert used == 0 and np.all(sel[:, :, 0] == 0)
+    sel, used, _ = _tanh_gate(L, sc, host, out["cmax"], 0.0, budget=3)
+    for b, S in enumerate(lens):
+        P = -(-S // 16)
+        for g in range(4):
+            want = gate.select_tanh(out["cmax"][b, g * 7:(g + 1) * 7, :P], np.zeros(P, bool), 0.0, budget=3)
+            assert list(sel[b, g, 1:1 + sel[b, g, 0]]) == want
+    assert used == int(sel[:, :, 0].sum())

@@ -147,9 +147,17 @@ def _check_decode(sc, out, n_check=None):
             ra = out["R_A"][b, hs]
             assert np.all(np.abs(ra - r["R_A"]) <= MET_TOL * r["R_A"]), (b, g, ra, r["R_A"])
             assert np.all(ra >= r["tv_true"]), (b, g)
+            # the tanh bound of Tier A: deterministic, sound
+            ta = out["T_A"][b, hs]
+            assert np.all(np.abs(ta - r["T_A"]) <= MET_TOL * r["T_A"] + 1e-7), (b, g, ta, r["T_A"])
+            assert np.all(ta >= r["tv_true"] * (1 - 1e-6)), (b, g)
             if sc.scheme == sc.L.WC_DITHER_INT8:
                 rb = out["R_B"][b, hs]
                 assert np.all(np.abs(rb - r["R_B"]) <= MET_TOL * r["R_B"]), (b, g, rb, r["R_B"])
+                tb = out["T_B"][b, hs]
+                assert np.all(np.abs(tb - r["T_B"]) <= MET_TOL * r["T_B"] + 1e-7), (b, g, tb, r["T_B"])
+            else:
+                assert np.all(out["T_B"][b, hs] == 0)
 
 
 def test_decode_tiny_fp32():
