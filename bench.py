@@ -273,12 +273,22 @@ def prefill_write(iters, seed=4, NL=28, NT=4096):
     return out
 
 
-def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05)):
+# gate variants: (label, meter_mask, gate) -- "cert" is the certificate gate on
+# the block risks of the gate tier (B when the mask has it, else A), "tanh" the
+# tanh gate on the blocks' largest bound of Tier A (deterministic, delta = 0)
+GATE_VARIANTS = {
+    "fp8": [("certificate_A", 1, "cert")],
+    "int8": [("certificate_B", 3, "cert"), ("certificate_A", 1, "cert"), ("tanh_A", 1, "tanh")],
+}
+
+
+def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="fp8"):
     """Ragged decode with the gate: 64 sequences, contexts uniform in
-    [1024, 32768], fp8 raw-cast cache on `n_layers` resident layers, exact keys
-    in pinned host memory.  Each step appends one token per sequence and layer,
-    then per layer decodes (Tier A, block risks), merges and gates at tau.
-    Reports page-in bytes of the cold first step and the mean of the rest."""
+    [1024, 32768], fp8 raw-cast (or dithered INT8) cache on `n_layers`
+    resident layers, exact keys in pinned host memory.  Each step appends one
+    token per sequence and layer, then per layer decodes (block risks or block
+    maxima), merges and gates at tau.  Reports page-in bytes of the cold first
+    step and the mean of the rest, per gate variant."""
     import numpy as np
     import torch
 
@@ -291,11 +301,13 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05)):
     mp = tab.shape[1]
     tab_d = torch.from_numpy(tab).to(dev)
     q = inputs.query_torch(seed, NB, Hq=HQ)
-    seeds_d = torch.zeros(NB, dtype=torch.int64, device=dev)
+    seeds_d = torch.arange(1000, 1000 + NB, dtype=torch.int64, device=dev)
+    sch = L.WC_FP8_E4M3 if scheme == "fp8" else L.WC_DITHER_INT8
     n0 = int(lens0.sum())
     slot0 = torch.from_numpy(np.concatenate([tab[b, np.arange(S_) // 16].astype(np.int64) * 16 + np.arange(S_) % 16
                                              for b, S_ in enumerate(lens0)])).to(dev)
     pos0 = torch.from_numpy(np.concatenate([np.arange(S_) for S_ in lens0]).astype(np.int32)).to(dev)
+    tseed0 = seeds_d.repeat_interleave(torch.from_numpy(lens0).to(dev))
     host = torch.empty((n_layers, npages, HKV, 16, D), dtype=torch.bfloat16, pin_memory=True)
     layer_kv = []
     for layer in range(n_layers):                      # per-layer K/V, its exact keys to the host store
@@ -321,15 +333,16 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05)):
     lse = torch.empty((NB, HQ), device=dev)
     ra = torch.empty((NB, HQ), device=dev)
     gws = torch.empty(L.wc_gate_workspace_bytes(NB, HKV, mp), dtype=torch.uint8, device=dev)
+    cname = "fp8 raw-cast" if scheme == "fp8" else "dithered INT8"
     res = {"metric": "gated ragged decode: page-in bytes per step and attention throughput", "data": "synthetic",
-           "config": {"workload": f"{NB} sequences, contexts U[1024, 32768], {n_layers} resident layers, fp8 raw-cast, "
+           "config": {"workload": f"{NB} sequences, contexts U[1024, 32768], {n_layers} resident layers, {cname}, "
                                   f"{n_steps} steps, exact keys in pinned host memory", "layers": n_layers,
-                      "steps": n_steps, "tokens": n0}, "tau": {}}
-    for tau in taus:
-        cache = L.KVCache(L.WC_FP8_E4M3, n_layers, npages, HKV, pool_capacity=int(npages) * HKV * n_layers)
+                      "steps": n_steps, "tokens": n0, "scheme": scheme}, "tau": {}}
+    for tau, (label, mask, kind) in [(t, v) for t in taus for v in GATE_VARIANTS[scheme]]:
+        cache = L.KVCache(sch, n_layers, npages, HKV, pool_capacity=int(npages) * HKV * n_layers)
         for layer in range(n_layers):
             kf, vf, _ = layer_kv[layer]
-            L.wc_write_kv(cache, kf, vf, slot0, pos0, torch.zeros_like(slot0), layer0=layer)
+            L.wc_write_kv(cache, kf, vf, slot0, pos0, tseed0, layer0=layer)
         pool_used = torch.zeros(1, dtype=torch.int64, device=dev)
         paged = torch.zeros(1, dtype=torch.int64, device=dev)
         per_step, dec_us = [], []
@@ -343,25 +356,35 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05)):
             t_dec = 0.0
             for layer in range(n_layers):
                 kn, vn = layer_kv[layer][2][s]
-                L.wc_write_kv(cache, kn, vn, slot, pos, torch.zeros_like(slot), layer0=layer)
+                L.wc_write_kv(cache, kn, vn, slot, pos, seeds_d, layer0=layer)
                 a.record()
-                L.wc_decode_attn_meter(cache, layer, q, tab_d, ctx, seeds_d, part, sm, 1, DELTA[0], *DELTA[1:],
+                L.wc_decode_attn_meter(cache, layer, q, tab_d, ctx, seeds_d, part, sm,
+                                       mask | (L.WC_BLOCK_CMAX if kind == "tanh" else 0), DELTA[0], *DELTA[1:],
                                        NSPLIT, block_logrisk=risk)
                 b.record()
                 L.wc_lse_merge(part, NB, HQ, NSPLIT, o, lse, ra)
-                L.wc_gate_pagein(cache, layer, risk, lse, tab_d, ctx, tau, host, pool_used, paged, gws)
+                if kind == "tanh":
+                    L.wc_gate_pagein_tanh(cache, layer, risk, tab_d, ctx, tau, host, pool_used, paged, gws)
+                else:
+                    L.wc_gate_pagein(cache, layer, risk, lse, tab_d, ctx, tau, host, pool_used, paged, gws)
                 torch.cuda.synchronize()
                 t_dec += a.elapsed_time(b) * 1e3
             per_step.append(int(paged.item()) - before)
             dec_us.append(t_dec)
-        nbytes = decode_bytes_ragged(lens0 + n_steps, scales=False) * n_layers
-        res["tau"][str(tau)] = {
+        nbytes = decode_bytes_ragged(lens0 + n_steps, scales=scheme == "int8") * n_layers
+        res["tau"].setdefault(str(tau), {})[label] = {
             "pagein_bytes_step1": per_step[0],
             "pagein_bytes_later_mean": round(float(np.mean(per_step[1:])), 1),
             "decode_us_per_step": round(float(np.mean(dec_us[1:])), 1),
             "attention_GBps": round(nbytes / (float(np.mean(dec_us[1:])) * 1e-6) / 1e9, 1)}
         del cache
         torch.cuda.empty_cache()
+    for tau, r in res["tau"].items():                 # the certificate's page-in saving over the tanh gate
+        if "tanh_A" in r:
+            tb = r["tanh_A"]["pagein_bytes_step1"]
+            for lab in ("certificate_B", "certificate_A"):
+                if tb > 0:
+                    r[lab]["pagein_reduction_vs_tanh"] = round(1.0 - r[lab]["pagein_bytes_step1"] / tb, 4)
     return res
 
 
@@ -382,9 +405,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill-write", "gate-flow"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill-write", "gate-flow", "gate-compare"],
                     help="decode: the headline line (default); prefill-write: the 28-layer write path per scheme; "
-                         "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps")
+                         "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps; "
+                         "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate")
     ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -397,6 +421,10 @@ def main():
         return
     if args.workload == "gate-flow":
         print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)))), flush=True)
+        return
+    if args.workload == "gate-compare":
+        print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)), taus=(0.1, 0.05, 0.02), scheme="int8")),
+              flush=True)
         return
     B, S = args.batch, args.ctx
     w = setup(B, S)
