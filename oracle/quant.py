@@ -9,7 +9,11 @@ Sources (WitCert pages):
   (32 B per token per head for 8 fp32 bands): summary, witness-theorem and
   implementation paragraphs.
 * fp8 raw cast and kivi-2bit as black-box schemes: summary, RULER results
-  paragraph ("fp8 raw", "kivi-2bit raw").
+  paragraph ("fp8 raw", "kivi-2bit raw"); round-to-nearest INT8 ("rtn-int8")
+  is the third scheme measured there.
+* Any scheme given as one tensor function x^ = f(x) is metered through the
+  same witness of its residual (summary implementation paragraph; the
+  abstract's scheme registration).
 
 Readings where the pages are silent (all listed in the design doc):
 
@@ -25,6 +29,8 @@ Readings where the pages are silent (all listed in the design doc):
   Keys are grouped over 32 consecutive tokens of one channel, values over 32
   consecutive channels of one token.
 * The witness is stored for keys only (32 B/token/head).
+* RTN INT8 uses the same row scale as the dithered quantizer, with no
+  dither: code = clamp(rint(fp32(x * inv_s)), -128, 127), x^ = s code.
 """
 import numpy as np
 
@@ -56,6 +62,29 @@ def dither_int8(x, xi):
 def dequant_dither_int8(code, s, xi):
     """x^ = s (code - xi), exact in float64."""
     return s.astype(np.float64)[:, None] * (code.astype(np.float64) - xi.astype(np.float64))
+
+
+def rtn_int8(x):
+    """Round-to-nearest INT8 of rows x (float32 [n, d]): (codes int8, s, inv_s).
+
+    Same float32 row scale as dither_int8; the code is the nearest level of
+    x * inv_s (rint: half to even), clamped to [-128, 127]; all-zero rows code 0.
+    """
+    x = np.asarray(x, dtype=F32)
+    absmax = np.max(np.abs(x), axis=-1)
+    zero = absmax == 0
+    safe = np.where(zero, F32(1), absmax).astype(F32)
+    s = np.where(zero, F32(0), safe / F32(127)).astype(F32)
+    inv = np.where(zero, F32(0), F32(127) / safe).astype(F32)
+    y = (x * inv[:, None]).astype(F32)
+    code = np.clip(np.rint(y), -128, 127)
+    code = np.where(zero[:, None], 0, code).astype(np.int8)
+    return code, s, inv
+
+
+def dequant_rtn_int8(code, s):
+    """x^ = s code, exact in float64."""
+    return s.astype(np.float64)[:, None] * code.astype(np.float64)
 
 
 def fp8_e4m3(x):

@@ -160,3 +160,34 @@ def test_witness_size_golden():
     w = quant.witness(np.zeros((3, 128)), np.ones((3, 128)))
     assert w.shape[1] == bands and np.dtype(np.float32).itemsize == per
     assert w.shape[1] * np.dtype(np.float32).itemsize == total
+
+
+def test_rtn_int8_is_the_nearest_level():
+    # Brute force: x^ = s code is the nearest of the 256 levels s * {-128..127}
+    # (ties, measured in the float32 product, go to the even code).
+    x = _rows(200, seed=30) * np.float32(3)
+    code, s, inv = quant.rtn_int8(x)
+    levels = np.arange(-128, 128, dtype=np.float64)
+    y = (x * inv[:, None]).astype(np.float32).astype(np.float64)
+    best = levels[np.argmin(np.abs(y[..., None] - levels), axis=-1)]
+    tie = np.abs(np.abs(y - np.floor(y)) - 0.5) < 1e-12
+    assert np.all((best == code) | tie)
+    xhat = quant.dequant_rtn_int8(code, s)
+    assert np.all(np.abs(xhat - x) <= s[:, None] * (0.5 + 1e-5))
+    # the row maximum maps to +-127 exactly
+    j = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(code[np.arange(200), j]) == 127)
+
+
+def test_rtn_residual_depends_on_the_input_unlike_dither():
+    # RTN's error is a deterministic function of x: two equal rows have equal
+    # residuals, and a constant row on the grid has none (no dither to randomize it)
+    x = np.tile(_rows(1, seed=31), (50, 1))
+    code, s, _ = quant.rtn_int8(x)
+    r = quant.dequant_rtn_int8(code, s) - x
+    assert np.all(r == r[0])
+    k = np.r_[np.arange(-127, 1), np.arange(1, 128)][:128]             # integers with |k| = 127 present
+    xg = (k.astype(np.float32) * np.float32(2.0 ** -6))[None, :]        # on the grid s = 2^-6
+    c2, s2, _ = quant.rtn_int8(xg)
+    assert s2[0] == np.float32(2.0 ** -6) and np.array_equal(c2[0], k.astype(np.int8))
+    assert np.all(quant.dequant_rtn_int8(c2, s2) == xg)
