@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("WITCERT_LIB") or os.path.join(_HERE, "libwitcert.so")
 
 WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
-WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2 = 0, 1, 2
+WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2, WC_RTN_INT8, WC_BF16_STORE = 0, 1, 2, 3, 4
 WC_F32, WC_BF16 = 0, 1
 WC_METER_A, WC_METER_B, WC_BLOCK_CMAX = 1, 2, 4
 PARTIAL = 136
@@ -54,6 +54,7 @@ def _load():
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
         "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
+        "wc_witness": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, P],
         "wc_gate_pagein_tanh": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_double,
                                 _i64, P, P, P, P, P, ctypes.c_size_t, P],
     }
@@ -74,7 +75,7 @@ lib = _load()
 
 EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
            "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select",
-           "wc_last_error", "wc_version"]
+           "wc_witness", "wc_last_error", "wc_version"]
 
 
 def _check(fn, code):
@@ -121,13 +122,20 @@ class KVCache:
             self.k_aux = torch.zeros(shp + (128, 2), **f32)
             self.v_aux = torch.zeros(shp + (32, 4, 2), **f32)
             self.k_scale = self.v_scale = None
+        elif scheme == WC_BF16_STORE:
+            # bf16 [8-channel group in 32][32-channel group][token][8] and
+            # [channel pair in 8][token group][8-channel group][channel parity][token]
+            self.k_codes = torch.zeros(shp + (4, 4, 16, 8), dtype=torch.int16, device=device)
+            self.v_codes = torch.zeros(shp + (4, 4, 16, 2, 4), dtype=torch.int16, device=device)
+            self.k_aux = self.v_aux = None
+            self.k_scale = self.v_scale = None
         else:
             # [half][32-channel group][token][16 channels] and
             # [half][token group][8-channel group][channel][token]
             self.k_codes = torch.zeros(shp + (2, 4, 16, 16), **u8)
             self.v_codes = torch.zeros(shp + (2, 4, 16, 4, 4), **u8)
             self.k_aux = self.v_aux = None
-            if scheme == WC_DITHER_INT8:
+            if scheme in (WC_DITHER_INT8, WC_RTN_INT8):
                 self.k_scale = torch.zeros(shp + (16,), **f32)
                 self.v_scale = torch.zeros(shp + (16,), **f32)
             else:
@@ -170,6 +178,16 @@ def wc_write_kv(cache, k, v, slot, pos, seed, layer0=0, stream=None):
     _check("wc_write_kv", lib.wc_write_kv(cache.ref(), layer0, n_layers, _ptr(k), _ptr(v), _dtype_code(k), n_tok,
                                           n_tok * k.shape[2] * k.shape[3], _ptr(slot), _ptr(pos), _ptr(seed),
                                           _stream(stream)))
+
+
+def wc_witness(cache, x, xhat, slot, layer0=0, stream=None):
+    """x, xhat: [n_layers, n_tok, Hkv, 128] or [n_tok, Hkv, 128] (same dtype, contiguous)."""
+    if x.dim() == 3:
+        x, xhat = x[None], xhat[None]
+    assert x.is_contiguous() and xhat.is_contiguous() and x.shape == xhat.shape and x.dtype == xhat.dtype
+    n_layers, n_tok = x.shape[0], x.shape[1]
+    _check("wc_witness", lib.wc_witness(cache.ref(), layer0, n_layers, _ptr(x), _ptr(xhat), _dtype_code(x), n_tok,
+                                        n_tok * x.shape[2] * x.shape[3], _ptr(slot), _stream(stream)))
 
 
 def wc_decode_workspace_bytes(B, Hq, n_split):

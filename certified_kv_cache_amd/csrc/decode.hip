@@ -32,6 +32,11 @@
 //        head n.
 //   Tier A  a^T[token][head] = W[token][band] . beta[head][band] on two fp32
 //        MFMAs 16x16x4.
+//   RTN INT8  the code chain alone (no dither); values through 16x16x16 f16
+//        MFMAs on the exact code integers, as the fp8 values.
+//   16-bit store  keys and values are bf16 (any scheme's output): QK on
+//        16x16x32 bf16 MFMAs against the unscaled bf16 query, PV with the
+//        attention weights split into bf16 hi + lo halves ([V|V] . [P_hi|P_lo]).
 //   Outlier bypass  the exact part of the logits on the bypassed channels,
 //        X[token][i] . Q[head][O[i]], on m/4 more fp32 MFMAs 16x16x4; the query
 //        operands of the key chains are zero on those channels.
@@ -45,6 +50,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
 // Waves per workgroup (four measured fastest: three and six were slower).
 #ifndef WC_DECODE_WAVES
@@ -154,6 +160,18 @@ __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
 __device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f4 mfma_bf(uint4 a, uint4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
+// Scheme traits: INT8 codes with row scales (dithered or RTN); the 16-bit store.
+template <int SCHEME>
+constexpr bool int8_codes() {
+  return SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
+}
+template <int SCHEME>
+constexpr int page_bytes() {                  // code bytes of one page-head block, K or V
+  return SCHEME == WC_BF16_STORE ? 4096 : 2048;
+}
 
 struct DecodeArgs {
   const void* q;
@@ -171,7 +189,7 @@ struct DecodeArgs {
 // One page of one wave, keys: the lane's 32 key codes of token n, the key
 // scales of its tokens, the witness bands 2k, 2k+1 of token n.
 struct KLoad {
-  uint4 k0, k1;
+  uint4 k0, k1, k2, k3;   // k2, k3: the 16-bit store only
   float4 ks;
   float2 w;
   uint2 xo;               // outlier bypass: the lane's bf16 side-store entries
@@ -180,7 +198,7 @@ struct KLoad {
 // Values: 8 channels x 4 tokens of codes and the value scales of the lane's
 // tokens.  Both are loaded one page ahead of their use.
 struct VLoad {
-  uint4 v0, v1;
+  uint4 v0, v1, v2, v3;
   float4 vs;
 };
 
@@ -229,15 +247,24 @@ __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const L
     else
       d.xo = make_uint2(bload4(orr, lo.o), 0u);
   }
-  const __amdgpu_buffer_rsrc_t kr = page_rsrc(c.k_codes, pg * 2048, 2048);
-  const __amdgpu_buffer_rsrc_t vr = page_rsrc(c.v_codes, pg * 2048, 2048);
+  constexpr int PB = page_bytes<SCHEME>();
+  const __amdgpu_buffer_rsrc_t kr = page_rsrc(c.k_codes, pg * PB, PB);
+  const __amdgpu_buffer_rsrc_t vr = page_rsrc(c.v_codes, pg * PB, PB);
   const __amdgpu_buffer_rsrc_t wr = meterA ? page_rsrc(c.witness, pg * 512, 512) : kr;
   d.k0 = bload16(kr, lo.k);
   d.k1 = bload16(kr, lo.k + 1024);
+  if (SCHEME == WC_BF16_STORE) {
+    d.k2 = bload16(kr, lo.k + 2048);
+    d.k3 = bload16(kr, lo.k + 3072);
+  }
   d.w = bload8(wr, lo.w);
   e.v0 = bload16(vr, lo.v);
   e.v1 = bload16(vr, lo.v + 1024);
-  if (SCHEME == WC_DITHER_INT8) {
+  if (SCHEME == WC_BF16_STORE) {
+    e.v2 = bload16(vr, lo.v + 2048);
+    e.v3 = bload16(vr, lo.v + 3072);
+  }
+  if (int8_codes<SCHEME>()) {
     const __amdgpu_buffer_rsrc_t ksr = page_rsrc(c.k_scale, pg * 64, 64);
     const __amdgpu_buffer_rsrc_t vsr = page_rsrc(c.v_scale, pg * 64, 64);
     if (PAIR) {
@@ -283,12 +310,21 @@ __device__ __forceinline__ void load_page_soff(const LayerBufs& lb, uint32_t pg,
     else
       d.xo = make_uint2(bload4s(lb.o, lo.o, pg * (128u * NO4)), 0u);
   }
-  d.k0 = bload16s(lb.k, lo.k, pg * 2048u);
-  d.k1 = bload16s(lb.k, lo.k + 1024, pg * 2048u);
-  d.w = bload8s(lb.w, lo.w, meterA ? pg * 512u : pg * 2048u);
-  e.v0 = bload16s(lb.v, lo.v, pg * 2048u);
-  e.v1 = bload16s(lb.v, lo.v + 1024, pg * 2048u);
-  if (SCHEME == WC_DITHER_INT8) {
+  constexpr uint32_t PB = page_bytes<SCHEME>();
+  d.k0 = bload16s(lb.k, lo.k, pg * PB);
+  d.k1 = bload16s(lb.k, lo.k + 1024, pg * PB);
+  if (SCHEME == WC_BF16_STORE) {
+    d.k2 = bload16s(lb.k, lo.k + 2048, pg * PB);
+    d.k3 = bload16s(lb.k, lo.k + 3072, pg * PB);
+  }
+  d.w = bload8s(lb.w, lo.w, meterA ? pg * 512u : pg * PB);
+  e.v0 = bload16s(lb.v, lo.v, pg * PB);
+  e.v1 = bload16s(lb.v, lo.v + 1024, pg * PB);
+  if (SCHEME == WC_BF16_STORE) {
+    e.v2 = bload16s(lb.v, lo.v + 2048, pg * PB);
+    e.v3 = bload16s(lb.v, lo.v + 3072, pg * PB);
+  }
+  if (int8_codes<SCHEME>()) {
     if (PAIR) {
       const float2 t = bload8s(lb.ks, lo.s, pg * 64u), u = bload8s(lb.vs, lo.s, pg * 64u);
       d.ks = make_float4(t.x, t.y, 0.f, 0.f);
@@ -333,16 +369,17 @@ constexpr int kDepth = WC_PREFETCH_DEPTH;
 #ifndef WC_DECODE_MIN_BLOCKS_OUTL
 #define WC_DECODE_MIN_BLOCKS_OUTL 3
 #endif
-template <bool QF32, int NO4>
+// The 16-bit store keeps twice the bytes of a page in flight: two waves.
+template <int SCHEME, bool QF32, int NO4>
 constexpr int decode_waves_per_simd() {
-  return QF32 ? 2 : NO4 > 0 ? WC_DECODE_MIN_BLOCKS_OUTL : WC_DECODE_MIN_BLOCKS_BF16;
+  return (QF32 || SCHEME == WC_BF16_STORE) ? 2 : NO4 > 0 ? WC_DECODE_MIN_BLOCKS_OUTL : WC_DECODE_MIN_BLOCKS_BF16;
 }
 
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 // NO4: outlier bypass with m = 4 NO4 exact key channels (0 = none).
 template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<QF32, NO4>())))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<SCHEME, QF32, NO4>())))
 decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,6 +491,32 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   }
   qsum += shfl_xor(qsum, 16);
   qsum += shfl_xor(qsum, 32);
+  // 16-bit store: the unscaled query as bf16 (exact for bf16 q; fp32 q adds
+  // the bf16 of the remainder as a second operand)
+  uint4 Qb[4], Qbl[4];
+  if (SCHEME == WC_BF16_STORE) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u0 = __float_as_uint(qf[8 * j + 2 * e]) & 0xFFFF0000u;
+        const uint32_t u1 = __float_as_uint(qf[8 * j + 2 * e + 1]) & 0xFFFF0000u;
+        hw[e] = (u0 >> 16) | u1;
+        if (QF32) {
+          const uint32_t r0 = __float_as_uint(qf[8 * j + 2 * e] - __uint_as_float(u0));
+          const uint32_t r1 = __float_as_uint(qf[8 * j + 2 * e + 1] - __uint_as_float(u1));
+          lw[e] = (r0 >> 16) | (r1 & 0xFFFF0000u);
+        }
+      }
+      Qb[j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if (QF32) Qbl[j] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+  // the store's keys are unscaled: their pages use the token factor 2^qe
+  // (with the compacted softmax, lanes n + 8 take head n's)
+  float store_st = ldexpf(1.0f, qe);
+  if (CMP) store_st = dpp_shr8_hi(store_st, store_st);
   // band norms: lane k holds bands (4k + jj) mod 8 of one half; halves are k, k^2
   float bfull[4];
 #pragma unroll
@@ -524,11 +587,13 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   if (SOFF) {
     const int64_t lph = c.num_pages * c.num_kv_heads;     // page-head blocks per layer
     const int64_t l0 = (int64_t)a.layer * lph;
-    lb.k = layer_rsrc(c.k_codes, l0 * 2048, (uint64_t)lph * 2048);
-    lb.v = layer_rsrc(c.v_codes, l0 * 2048, (uint64_t)lph * 2048);
+    constexpr int64_t PB = page_bytes<SCHEME>();
+    lb.k = layer_rsrc(c.k_codes, l0 * PB, (uint64_t)lph * PB);
+    lb.v = layer_rsrc(c.v_codes, l0 * PB, (uint64_t)lph * PB);
     lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
+    lb.o = lb.ks = lb.vs = lb.k;               // (unused unless set below)
     if (NO4 > 0) lb.o = layer_rsrc(c.k_outlier, l0 * (128 * NO4), (uint64_t)lph * (128 * NO4));
-    if (SCHEME == WC_DITHER_INT8) {
+    if (int8_codes<SCHEME>()) {
       lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
       lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
     }
@@ -592,12 +657,24 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       }
       sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
     };
-    if (!exact) {
+    if (!exact && SCHEME == WC_BF16_STORE) {
+      const uint4 kx[4] = {cur.k0, cur.k1, cur.k2, cur.k3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Dc = mfma_bf(kx[j], Qb[j], j == 0 ? zero4 : Dc);
+        if (QF32) Dc = mfma_bf(kx[j], Qbl[j], Dc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[r] = store_st;
+    } else if (!exact) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t hh[4], ll[4], c0, c1, c2, c3;
         if (SCHEME == WC_DITHER_INT8) {
           draws(j, hh, ll);
+          codes_to_h(kw[2 * j], c0, c1);
+          codes_to_h(kw[2 * j + 1], c2, c3);
+        } else if (SCHEME == WC_RTN_INT8) {
           codes_to_h(kw[2 * j], c0, c1);
           codes_to_h(kw[2 * j + 1], c2, c3);
         } else {
@@ -796,7 +873,24 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 
     // ---------------- PV: O^T += Vhat^T P^T
     h4 Bc;
-    if (CMP) {                                 // tokens 2, 3 come back from lane n + 8
+    uint4 Bp;
+    uint32_t ph0 = 0, ph1 = 0, pl0 = 0, pl1 = 0;   // 16-bit store: bf16 pairs of P_hi, P_lo
+    if (SCHEME == WC_BF16_STORE) {
+      // p = hi + lo with hi the truncated bf16 of p and lo the bf16 of the rest
+      auto split2 = [&](float x0, float x1, uint32_t& hi, uint32_t& lo) {
+        const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u, u1 = __float_as_uint(x1) & 0xFFFF0000u;
+        hi = (u0 >> 16) | u1;
+        lo = (__float_as_uint(x0 - __uint_as_float(u0)) >> 16) |
+             (__float_as_uint(x1 - __uint_as_float(u1)) & 0xFFFF0000u);
+      };
+      split2(p[0], p[1], ph0, pl0);
+      if (CMP) {                               // tokens 2, 3 come back from lane n + 8
+        ph1 = dpp_shl8_lo(ph0, ph0);
+        pl1 = dpp_shl8_lo(pl0, pl0);
+      } else {
+        split2(p[2], p[3], ph1, pl1);
+      }
+    } else if (CMP) {                          // tokens 2, 3 come back from lane n + 8
       const h2 own = {(_Float16)(p[0] * sv[0]), (_Float16)(p[1] * sv[1])};
       const uint32_t up = dpp_shl8_lo(as_u32(own), as_u32(own));
       Bc = make_h4(as_u32(own), up);
@@ -830,11 +924,33 @@ decode_kernel(wc_cache c, DecodeArgs a) {
         const uint32_t hb = as_u32(__builtin_elementwise_fma(as_h2(perm(h3w[w], h2w[w], sel)), km, kb));
         O[t] = mfma32(make_h8(c0, c1, ha, hb), B2, O[t]);
       }
+    } else if (SCHEME == WC_BF16_STORE) {
+      // [V|V] . [P_hi|P_lo]: tokens 4k..4k+3 of channel 8n + t twice, against
+      // the bf16 attention weights and their bf16 remainders
+      const uint4 vx[4] = {vl.v0, vl.v1, vl.v2, vl.v3};
+      Bp = make_uint4(ph0, ph1, pl0, pl1);
+      // past the end of the last page the store holds whatever was there:
+      // its values are masked to 0 (their weights are 0, a NaN would not be)
+      uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu;
+      if (!full) {
+        const int t0 = tok0 + 4 * kq;
+        mk0 = (t0 < S ? 0x0000FFFFu : 0u) | (t0 + 1 < S ? 0xFFFF0000u : 0u);
+        mk1 = (t0 + 2 < S ? 0x0000FFFFu : 0u) | (t0 + 3 < S ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint4 w = vx[t >> 1];
+        const uint32_t a0 = ((t & 1) ? w.z : w.x) & mk0, a1 = ((t & 1) ? w.w : w.y) & mk1;
+        O[t] = mfma_bf(make_uint4(a0, a1, a0, a1), Bp, O[t]);
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         uint32_t c0, c1;
-        fp8_to_h(vw[t], c0, c1);
+        if (SCHEME == WC_RTN_INT8)
+          codes_to_h(vw[t], c0, c1);
+        else
+          fp8_to_h(vw[t], c0, c1);
         O[t] = mfma16(make_h4(c0, c1), Bc, O[t]);
       }
     }
@@ -1038,7 +1154,8 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: need head_dim 128, 8 bands, 16-token pages");
     return WC_EUNSUPPORTED;
   }
-  if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3) {
+  if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3 && c.scheme != WC_RTN_INT8 &&
+      c.scheme != WC_BF16_STORE) {
     set_error("wc_decode_attn_meter: scheme %d has no decode path", c.scheme);
     return WC_EUNSUPPORTED;
   }
@@ -1075,6 +1192,10 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: INT8 cache needs seeds and scales");
     return WC_EINVAL;
   }
+  if (c.scheme == WC_RTN_INT8 && (!c.k_scale || !c.v_scale)) {
+    set_error("wc_decode_attn_meter: RTN INT8 cache needs scales");
+    return WC_EINVAL;
+  }
   if (!c.k_codes || !c.v_codes) {
     set_error("wc_decode_attn_meter: cache codes not set");
     return WC_EINVAL;
@@ -1109,7 +1230,8 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   hipStream_t st = (hipStream_t)stream;
   const bool cmp = a.G <= 8;
   // one buffer resource per layer array when its byte offsets fit 32 bits
-  const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * 2048u <= 0xFFFFFFFFull;
+  const uint64_t page_b = c.scheme == WC_BF16_STORE ? 4096u : 2048u;
+  const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * page_b <= 0xFFFFFFFFull;
 #define WC_LAUNCH_NO(SCH, QF, CM, NO)                                                                 \
   do {                                                                                               \
     if (soff)                                                                                        \
@@ -1132,11 +1254,23 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     } else {
       if (cmp) WC_LAUNCH(WC_DITHER_INT8, true, true); else WC_LAUNCH(WC_DITHER_INT8, true, false);
     }
-  } else {
+  } else if (c.scheme == WC_FP8_E4M3) {
     if (q_dtype == WC_BF16) {
       if (cmp) WC_LAUNCH(WC_FP8_E4M3, false, true); else WC_LAUNCH(WC_FP8_E4M3, false, false);
     } else {
       if (cmp) WC_LAUNCH(WC_FP8_E4M3, true, true); else WC_LAUNCH(WC_FP8_E4M3, true, false);
+    }
+  } else if (c.scheme == WC_RTN_INT8) {
+    if (q_dtype == WC_BF16) {
+      if (cmp) WC_LAUNCH(WC_RTN_INT8, false, true); else WC_LAUNCH(WC_RTN_INT8, false, false);
+    } else {
+      if (cmp) WC_LAUNCH(WC_RTN_INT8, true, true); else WC_LAUNCH(WC_RTN_INT8, true, false);
+    }
+  } else {
+    if (q_dtype == WC_BF16) {
+      if (cmp) WC_LAUNCH(WC_BF16_STORE, false, true); else WC_LAUNCH(WC_BF16_STORE, false, false);
+    } else {
+      if (cmp) WC_LAUNCH(WC_BF16_STORE, true, true); else WC_LAUNCH(WC_BF16_STORE, true, false);
     }
   }
 #undef WC_LAUNCH

@@ -96,6 +96,10 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
         xr = 0.0f;
       }
       code = (uint32_t)((int32_t)q + 128);
+    } else if (SCHEME == WC_RTN_INT8) {
+      const float q = s == 0.0f ? 0.0f : fminf(fmaxf(rintf(mul_rn(x[i], inv)), -128.0f), 127.0f);
+      code = (uint32_t)((int32_t)q + 128);
+      xr = fmaf(s, q, -x[i]);                   // one rounding
     } else {
       code = f32_to_e4m3(x[i]);
       xr = e4m3_to_f32(code) - x[i];
@@ -157,7 +161,7 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, shfl_xor(am, m));
     float s = 0.0f, inv = 0.0f;
-    if (SCHEME == WC_DITHER_INT8 && am > 0.0f) {
+    if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && am > 0.0f) {
       s = div_rn(am, 127.0f);
       inv = div_rn(127.0f, am);
     }
@@ -177,7 +181,7 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
                       (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
         *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
         if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = w;
-        if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.k_scale[pg * 16 + off] = s;
+        if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && lane16 == 0) c.k_scale[pg * 16 + off] = s;
         if (OUTL && ochan >= 0)
           c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] =
               reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
@@ -188,8 +192,69 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
       uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
 #pragma unroll
       for (int k = 0; k < 8; ++k) vc[(k >> 2) * 1024 + (k & 3) * 4] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
-      if (SCHEME == WC_DITHER_INT8 && lane16 == 0) c.v_scale[pg * 16 + off] = s;
+      if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && lane16 == 0) c.v_scale[pg * 16 + off] = s;
     }
+  }
+}
+
+// 16-bit store: the scheme's outputs (bf16) copied into the decode layouts,
+// witness 0 (wc_witness writes the scheme's own).  16 lanes per row, 8
+// channels each, as above.
+__global__ void __launch_bounds__(256) write_bf16_kernel(wc_cache c, const uint16_t* __restrict__ kin,
+                                                         const uint16_t* __restrict__ vin, RowArgs a) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
+  if (row >= rows) return;
+  const int g = (int)(row % a.hkv);
+  const int64_t i = (row / a.hkv) % a.n_tok;
+  const int l = (int)(row / ((int64_t)a.hkv * a.n_tok));
+  const int64_t slot = a.slot[i];
+  const int64_t page = slot / 16, off = slot % 16;
+  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
+  const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + page) * a.hkv + g;
+  const uint4 kv = *reinterpret_cast<const uint4*>(kin + in_off);
+  const uint4 vv = *reinterpret_cast<const uint4*>(vin + in_off);
+  // keys: channels 8 lane16 .. +7 of token off at [(c%32)/8][c/32][off][c%8]
+  uint8_t* kb = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 4096;
+  *reinterpret_cast<uint4*>(kb + (lane16 & 3) * 1024 + (lane16 >> 2) * 256 + off * 16) = kv;
+  // values: channel 8 lane16 + e at [e/2][off/4][lane16][e%2][off%4]
+  uint16_t* vb = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(c.v_codes) + pg * 4096);
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    vb[(e >> 1) * 512 + (off >> 2) * 128 + lane16 * 8 + (e & 1) * 4 + (off & 3)] =
+        (uint16_t)((e & 1) ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
+  if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = 0.0f;
+}
+
+// Witness of an arbitrary scheme's output: w_{t,b} = ||xhat - x|| over band b.
+template <typename T>
+__global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __restrict__ x, const T* __restrict__ xh,
+                                                      RowArgs a) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
+  const bool live = row < rows;
+  const int64_t rr = live ? row : 0;
+  const int g = (int)(rr % a.hkv);
+  const int64_t i = (rr / a.hkv) % a.n_tok;
+  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
+  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
+  float xv[8], hv[8];
+  load8<T>(x + in_off, xv);
+  load8<T>(xh + in_off, hv);
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float r = hv[k] - xv[k];
+    ss = fmaf(r, r, ss);
+  }
+  const float tot = ss + shfl_xor(ss, 8);
+  if (live && lane16 < 8) {
+    const int64_t slot = a.slot[i];
+    const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
+    c.witness[(pg * 16 + slot % 16) * 8 + lane16] = sqrtf(tot) * kWitnessGuard;
   }
 }
 
@@ -403,12 +468,22 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
   RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, pos, seed};
   hipStream_t st = (hipStream_t)stream;
   if (n_tok == 0) return WC_OK;
-  if (c.scheme == WC_DITHER_INT8 || c.scheme == WC_FP8_E4M3) {
+  if (c.scheme == WC_BF16_STORE) {
+    if (c.page_size != 16 || in_dtype != WC_BF16 || c.num_outliers != 0) {
+      set_error("wc_write_kv: the 16-bit store takes bf16 input and 16-token pages, no outlier bypass");
+      return WC_EUNSUPPORTED;
+    }
+    const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
+    hipLaunchKernelGGL(write_bf16_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, c,
+                       (const uint16_t*)k, (const uint16_t*)v, a);
+    return check_launch("wc_write_kv");
+  }
+  if (c.scheme == WC_DITHER_INT8 || c.scheme == WC_FP8_E4M3 || c.scheme == WC_RTN_INT8) {
     if (c.page_size != 16) {
       set_error("wc_write_kv: INT8 and fp8 caches use 16-token pages");
       return WC_EUNSUPPORTED;
     }
-    if (c.scheme == WC_DITHER_INT8 && (!c.k_scale || !c.v_scale)) {
+    if ((c.scheme == WC_DITHER_INT8 || c.scheme == WC_RTN_INT8) && (!c.k_scale || !c.v_scale)) {
       set_error("wc_write_kv: INT8 cache needs k_scale and v_scale");
       return WC_EINVAL;
     }
@@ -437,6 +512,13 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
                            (const uint16_t*)k, (const uint16_t*)v, a);
       else
         hipLaunchKernelGGL((write_rows_kernel<float, WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c,
+                           (const float*)k, (const float*)v, a);
+    } else if (c.scheme == WC_RTN_INT8) {
+      if (in_dtype == WC_BF16)
+        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_RTN_INT8, false>), grid, dim3(256), 0, st, c,
+                           (const uint16_t*)k, (const uint16_t*)v, a);
+      else
+        hipLaunchKernelGGL((write_rows_kernel<float, WC_RTN_INT8, false>), grid, dim3(256), 0, st, c,
                            (const float*)k, (const float*)v, a);
     } else {
       if (in_dtype == WC_BF16)
@@ -468,6 +550,43 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
   }
   set_error("wc_write_kv: unknown scheme %d", c.scheme);
   return WC_EUNSUPPORTED;
+}
+
+extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat,
+                          int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot, void* stream) {
+  if (!cache || !x || !xhat || !slot) {
+    set_error("wc_witness: null pointer");
+    return WC_EINVAL;
+  }
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1 || c.num_pages < 1) {
+    set_error("wc_witness: need head_dim 128, 8 bands, 16-token pages");
+    return WC_EUNSUPPORTED;
+  }
+  if (!c.witness) {
+    set_error("wc_witness: cache witness not set");
+    return WC_EINVAL;
+  }
+  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_tok < 0 ||
+      (n_layers > 1 && layer_stride < n_tok * c.num_kv_heads * 128)) {
+    set_error("wc_witness: layer range, token count or layer stride out of range");
+    return WC_EINVAL;
+  }
+  if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
+    set_error("wc_witness: in_dtype must be WC_F32 or WC_BF16");
+    return WC_EUNSUPPORTED;
+  }
+  if (n_tok == 0) return WC_OK;
+  RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, nullptr, nullptr};
+  const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
+  dim3 grid((unsigned)((rows + 15) / 16));
+  if (in_dtype == WC_BF16)
+    hipLaunchKernelGGL((witness_kernel<uint16_t>), grid, dim3(256), 0, (hipStream_t)stream, c, (const uint16_t*)x,
+                       (const uint16_t*)xhat, a);
+  else
+    hipLaunchKernelGGL((witness_kernel<float>), grid, dim3(256), 0, (hipStream_t)stream, c, (const float*)x,
+                       (const float*)xhat, a);
+  return check_launch("wc_witness");
 }
 
 extern "C" int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, int num_kv_heads,

@@ -34,15 +34,21 @@
  *  k_codes   INT8/fp8: [L][P][Hkv][2][4][16][16] bytes per page-head
  *            block: token t, channel c at [(c%32)/16][c/32][t][c%16] (each
  *            1 KB half holds, for every token, 16 channels of each 32-channel
- *            group).  INT8 codes are stored as offset binary (code + 128).
+ *            group).  INT8 codes (dithered and RTN) are stored as offset
+ *            binary (code + 128).
+ *            16-bit store: bf16 [L][P][Hkv][4][4][16][8]: token t, channel c
+ *            at [(c%32)/8][c/32][t][c%8] (4 KB per page-head block).
  *            2-bit:    [L][P][Hkv][128][8] bytes (32 tokens of one channel,
  *                      4 codes per byte, token i in bits 2(i%4)).
  *  v_codes   INT8/fp8: [L][P][Hkv][2][4][16][4][4] bytes: token t, channel c
  *                      at [(c%8)/4][t/4][c/8][c%4][t%4] (four tokens of one
  *                      channel are one 32-bit word).
  *            2-bit:    [L][P][Hkv][32][32] bytes (token-major, 4 codes/byte).
+ *            16-bit store: bf16 [L][P][Hkv][4][4][16][2][4]: token t,
+ *                      channel c at [(c%8)/2][t/4][c/8][c%2][t%4].
  *  k_scale,
- *  v_scale   INT8: fp32 [L][P][Hkv][16], s = absmax/127 of the row.
+ *  v_scale   INT8 (dithered and RTN): fp32 [L][P][Hkv][16], s = absmax/127
+ *            of the row.
  *  k_aux     2-bit: fp32 [L][P][Hkv][128][2] (scale, min) per channel group.
  *  v_aux     2-bit: fp32 [L][P][Hkv][32][4][2] (scale, min) per token group.
  *  witness   fp32 [L][P][Hkv][page][8]: w_{t,b} = ||r_{t,b}||, keys only.
@@ -87,6 +93,9 @@ extern "C" {
 #define WC_DITHER_INT8 0 /* subtractively-dithered INT8 (Tier A + Tier B) */
 #define WC_FP8_E4M3 1    /* fp8 e4m3fn raw cast, black box (Tier A)       */
 #define WC_KIVI2 2       /* 2-bit asymmetric, group 32 (write path only)  */
+#define WC_RTN_INT8 3    /* round-to-nearest INT8, black box (Tier A)     */
+#define WC_BF16_STORE 4  /* 16-bit store of any scheme's output x^ (Tier A,
+                            witness through wc_witness)                   */
 
 /* Input dtypes. */
 #define WC_F32 0
@@ -143,11 +152,35 @@ typedef struct {
  *  seed       device uint64 [n_tok]: dither seed of the token's sequence.
  * Writes k_codes, v_codes, scales (or aux) and the key witness; with the
  * outlier bypass (num_outliers > 0, bf16 input only) also k_outlier, reading
- * the channels of each layer from outlier_ch.
+ * the channels of each layer from outlier_ch.  RTN INT8: code =
+ * clamp(rint(x * (127/absmax)), -128, 127), x^ = s code.  16-bit store
+ * (bf16 input only): k and v are stored as given (they are the scheme's
+ * outputs x^) and the witness is set to 0; wc_witness then stores the
+ * witness of the scheme's residual.
  */
 int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
                 int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
                 const int32_t* pos, const uint64_t* seed, void* stream);
+
+/*
+ * wc_witness -- the black-box hook: store the witness of any scheme.
+ *
+ * The summary's implementation paragraph and the abstract register any
+ * scheme as one tensor function x^ = f(x) and meter it through the witness
+ * of its residual: w_{t,b} = ||x^_t - x_t|| over band b (witness-theorem
+ * paragraph), written at the tokens' slots in cache->witness (Tier A then
+ * bounds the scheme in wc_decode_attn_meter).  With the 16-bit store the
+ * caller writes x^ with wc_write_kv first, then calls this with the exact
+ * keys x and the same x^.
+ *
+ *  x, xhat    device, dtype in_dtype (WC_F32 | WC_BF16), [n_layers][n_tok][Hkv][128],
+ *             layer l at l * layer_stride elements; x = exact post-RoPE keys.
+ *  slot       device int64 [n_tok]: page * 16 + offset (16-token pages).
+ * The stored value is rounded up (by a factor 1 + 2^-17) so that it never
+ * falls below the exact norm.
+ */
+int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat, int in_dtype,
+               int64_t n_tok, int64_t layer_stride, const int64_t* slot, void* stream);
 
 /*
  * wc_outlier_select -- the outlier-bypass channels of each (layer, KV head).
@@ -186,6 +219,8 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *  ctx_len    device int32 [B]: tokens cached per sequence (<= max_pages*16).
  *  seed       device uint64 [B]: dither seed of each sequence.
  *  meter_mask 0, WC_METER_A or WC_METER_A|WC_METER_B (B needs dithered INT8).
+ *  Schemes: dithered INT8, fp8, RTN INT8 and the 16-bit store (2-bit has
+ *             no decode path).
  *             With 0 the witness is not read; output and LSE bits are the same
  *             as with the meter on.
  *  n_split    1..1024 KV splits per (sequence, KV head): split i covers blocks

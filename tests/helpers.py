@@ -60,6 +60,22 @@ def gather_v_codes(vc, layer, pt_row, S, g):
     return vc[layer, pt_row[t // 16], g, (c % 8) // 4, (t % 16) // 4, c // 8, c % 4, t % 4]
 
 
+def gather_k_bf16(kc, layer, pt_row, S, g):
+    """[S, 128] bf16 bits of the 16-bit store's keys from [L][P][Hkv][4][4][16][8]:
+    token t, channel c at [(c % 32) // 8][c // 32][t % 16][c % 8]."""
+    t = np.arange(S)[:, None]
+    c = np.arange(128)[None, :]
+    return kc[layer, pt_row[t // 16], g, (c % 32) // 8, c // 32, t % 16, c % 8]
+
+
+def gather_v_bf16(vc, layer, pt_row, S, g):
+    """[S, 128] bf16 bits of the 16-bit store's values from [L][P][Hkv][4][4][16][2][4]:
+    token t, channel c at [(c % 8) // 2][(t % 16) // 4][c // 8][c % 2][t % 4]."""
+    t = np.arange(S)[:, None]
+    c = np.arange(128)[None, :]
+    return vc[layer, pt_row[t // 16], g, (c % 8) // 2, (t % 16) // 4, c // 8, c % 2, t % 4]
+
+
 def gather_rows(arr, layer, pt_row, S, g):
     """[S, ...] per-token rows (scales, witness) from [L][P][Hkv][16][...]."""
     t = np.arange(S)
@@ -82,6 +98,14 @@ def oracle_int8_cache(k32, v32, seed, layer, g, S, bypass=None):
     cv, sv, _ = quant.dither_int8(v32, xv)
     vhat = quant.dequant_dither_int8(cv, sv, xv)
     return dict(ck=ck, sk=sk, cv=cv, sv=sv, khat=khat, vhat=vhat, w=quant.witness(k32, khat), side=side)
+
+
+def oracle_rtn_cache(k32, v32):
+    ck, sk, _ = quant.rtn_int8(k32)
+    cv, sv, _ = quant.rtn_int8(v32)
+    khat = quant.dequant_rtn_int8(ck, sk)
+    return dict(ck=ck, sk=sk, cv=cv, sv=sv, khat=khat, vhat=quant.dequant_rtn_int8(cv, sv),
+                w=quant.witness(k32, khat))
 
 
 def oracle_fp8_cache(k32, v32):

@@ -10,13 +10,13 @@ import numpy as np
 import torch
 
 from certified_kv_cache_amd import inputs
-from oracle import meter, outlier
+from oracle import meter, outlier, quant
 from tests import helpers as H
 
 
 class Scenario:
     def __init__(self, scheme, k, v, q, ctx_lens, dtype, Hkv, layer=1, num_layers=2, seed=5, pool_capacity=0,
-                 extra_pages=3, delta=(1e-2, 28, 28, 256), num_outliers=0):
+                 extra_pages=3, delta=(1e-2, 28, 28, 256), num_outliers=0, khat=None, vhat=None):
         from certified_kv_cache_amd import _lib as L
         self.L = L
         self.scheme, self.dtype, self.Hkv = scheme, dtype, Hkv
@@ -43,9 +43,18 @@ class Scenario:
             seed=torch.from_numpy(self.seeds.view(np.int64)).cuda(),
             tab=torch.from_numpy(self.tab).cuda(), ctx=torch.from_numpy(self.ctx.astype(np.int32)).cuda(),
             q=H.dev_tensor(q, dtype))
+        # 16-bit store: a black-box scheme's outputs khat, vhat (bf16 bits) are
+        # stored, and the witness of khat against k comes from wc_witness
+        self.khat, self.vhat = khat, vhat
         if len(slot):
-            L.wc_write_kv(self.cache, H.dev_tensor(k, dtype), H.dev_tensor(v, dtype), self.dev["slot"],
-                          self.dev["pos"], self.dev["tseed"], layer0=layer)
+            if scheme == L.WC_BF16_STORE:
+                L.wc_write_kv(self.cache, H.dev_tensor(khat, dtype), H.dev_tensor(vhat, dtype), self.dev["slot"],
+                              self.dev["pos"], self.dev["tseed"], layer0=layer)
+                L.wc_witness(self.cache, H.dev_tensor(k, dtype), H.dev_tensor(khat, dtype), self.dev["slot"],
+                             layer0=layer)
+            else:
+                L.wc_write_kv(self.cache, H.dev_tensor(k, dtype), H.dev_tensor(v, dtype), self.dev["slot"],
+                              self.dev["pos"], self.dev["tseed"], layer0=layer)
         self.offsets = np.concatenate([[0], np.cumsum(self.ctx)])
 
     def decode(self, n_split=4, mask=3, risk=False, sm=H.SM, cmax=False):
@@ -86,6 +95,15 @@ class Scenario:
             lt = math.log(2 * S / dl) if S > 0 else 0.0
             res = meter.decode_group(q, k32, oc["khat"], v32, oc["vhat"], oc["w"], sm, k_scale=oc["sk"],
                                      log_term=lt, repaired=repaired, bypass=O)
+        elif self.scheme == self.L.WC_RTN_INT8:
+            oc = H.oracle_rtn_cache(k32, v32)
+            res = meter.decode_group(q, k32, oc["khat"], v32, oc["vhat"], oc["w"], sm, repaired=repaired)
+        elif self.scheme == self.L.WC_BF16_STORE:
+            s0, s1 = self.offsets[b], self.offsets[b + 1]
+            kh = H.to_f32(self.khat[s0:s1, g], self.dtype)
+            vh = H.to_f32(self.vhat[s0:s1, g], self.dtype)
+            oc = dict(khat=kh, vhat=vh, w=quant.witness(k32, kh))
+            res = meter.decode_group(q, k32, kh, v32, vh, oc["w"], sm, repaired=repaired)
         else:
             oc = H.oracle_fp8_cache(k32, v32)
             res = meter.decode_group(q, k32, oc["khat"], v32, oc["vhat"], oc["w"], sm, repaired=repaired)

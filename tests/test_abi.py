@@ -162,3 +162,30 @@ def test_tanh_gate_and_cmax_reject_bad_arguments():
     cc = ctypes.byref(_cache(L))
     assert d(cc, 0, p, 1, 2, 28, p, 8, p, p, 0.088, 3 | L.WC_BLOCK_CMAX, 1e-2, 28, 28, 256, 4, p, ws, None,
              None) == L.WC_EINVAL                      # block maxima need the block output
+
+
+def test_blackbox_schemes_reject_bad_arguments():
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    w = L.lib.wc_witness
+    ok = ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE))
+    assert w(None, 0, 1, p, p, 1, 4, 0, p, None) == L.WC_EINVAL
+    assert w(ok, 0, 1, p, None, 1, 4, 0, p, None) == L.WC_EINVAL
+    assert w(ok, 1, 2, p, p, 1, 4, 0, p, None) == L.WC_EINVAL              # layer range
+    assert w(ok, 0, 1, p, p, 9, 4, 0, p, None) == L.WC_EUNSUPPORTED        # dtype
+    assert w(ctypes.byref(_cache(L, witness=None)), 0, 1, p, p, 1, 4, 0, p, None) == L.WC_EINVAL
+    assert w(ok, 0, 1, p, p, 1, 0, 0, p, None) == L.WC_OK                  # nothing to do
+    wr = L.lib.wc_write_kv
+    assert wr(ok, 0, 1, p, p, 0, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED  # the store takes bf16
+    assert wr(ctypes.byref(_cache(L, scheme=L.WC_RTN_INT8, k_scale=None)), 0, 1, p, p, 1, 4, 0, p, p, p,
+              None) == L.WC_EINVAL
+    d = L.lib.wc_decode_attn_meter
+    ws = L.wc_decode_workspace_bytes(2, 28, 4)
+
+    def call(cache, mask=1):
+        return d(ctypes.byref(cache), 0, p, 1, 2, 28, p, 8, p, p, 0.088, mask, 1e-2, 28, 28, 256, 4, p, ws, None, None)
+
+    assert call(_cache(L, scheme=L.WC_RTN_INT8), mask=3) == L.WC_EINVAL      # Tier B needs the dither
+    assert call(_cache(L, scheme=L.WC_BF16_STORE), mask=3) == L.WC_EINVAL
+    assert call(_cache(L, scheme=L.WC_RTN_INT8, v_scale=None)) == L.WC_EINVAL
+    assert call(_cache(L, scheme=L.WC_RTN_INT8, num_outliers=8, outlier_ch=16, k_outlier=16)) == L.WC_EUNSUPPORTED
