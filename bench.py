@@ -116,6 +116,38 @@ def fp8_variant(w, B, S, iters):
             "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
+def scheme_variant(w, B, S, iters, scheme):
+    """The same workload on a black-box scheme with Tier A: RTN INT8, or the
+    16-bit store (x^ = x here; its witness comes from wc_witness)."""
+    import torch
+    L = w["L"]
+    sch = {"rtn": L.WC_RTN_INT8, "store16": L.WC_BF16_STORE}[scheme]
+    cache = L.KVCache(sch, 1, w["npages"], HKV)
+    L.wc_write_kv(cache, w["k"], w["v"], w["slot"], w["pos"], w["seed"].repeat_interleave(S))
+    if scheme == "store16":
+        L.wc_witness(cache, w["k"], w["k"], w["slot"])
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    sm = 1.0 / math.sqrt(D)
+
+    def decode(mask=1, with_risk=True):
+        L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    t_risk = min(time_decode(decode, iters, mask=1, with_risk=True), time_decode(decode, iters, mask=1, with_risk=True))
+    t_on = time_decode(decode, iters, mask=1, with_risk=False)
+    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    if scheme == "store16":
+        nb = B * S * HKV * (2 * 2 * D + 32) + B * (-(-S // 16)) * 4 + B * HQ * D * 2 + B * 12
+    else:
+        nb = decode_bytes(B, S, True)
+    del cache
+    return {"decode_us": round(t_risk, 2), "decode_meter_on_us": round(t_on, 2), "decode_meter_off_us": round(t_off, 2),
+            "meter_overhead": round(t_on / t_off - 1, 4), "decode_bytes": nb,
+            "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
 def outlier_variant(w, B, S, iters, m):
     """The same workload with the outlier bypass of the keys (m exact bf16
     channels per KV head, chosen by key energy over the first 4096 cached
@@ -474,6 +506,8 @@ def main():
     }
     out["fp8_variant"] = fp8_variant(w, B, S, iters)
     out["outlier_variant"] = [outlier_variant(w, B, S, iters, m) for m in (8, 16)]
+    out["rtn_variant"] = scheme_variant(w, B, S, iters, "rtn")
+    out["store16_variant"] = scheme_variant(w, B, S, iters, "store16")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
     if args.copy_ref:
