@@ -40,6 +40,13 @@ Readings (the design doc lists them):
   sequence's full context length, H = query heads; with the outlier bypass
   (oracle/outlier.py) s_{c,t} = 0 on the bypassed channels.
 * Repaired (exact) tokens have c_t = 0 in both tiers and k^ = k.
+* The value-side certificate (the pages report joint K+V coverage but
+  define no value bound): with the value witness w^V_t = ||v^_t - v_t||,
+  ||sum_t p~_t v^_t - sum_t p~_t v_t|| <= E_V = sum_t p~_t w^V_t by the
+  triangle inequality (deterministic, any value quantizer).  With the key
+  side's TV it bounds the whole output error:
+  ||o~ - o|| <= E_V + 2 TV max_t ||v_t||, since sum_t (p~_t - p_t) v_t has norm
+  at most 2 TV max ||v_t||.
 * The block risk used by the gate is rho_{h,j} = sum_{t in block j}
   p~_t expm1(c_t) for the gate's tier, so that sum_j rho_{h,j} = E_h.
 """
@@ -105,6 +112,11 @@ def tv(p, p_tilde):
     return 0.5 * np.sum(np.abs(p - p_tilde), axis=-1)
 
 
+def v_certificate(p_tilde, wv):
+    """E_V = sum_t p~_t w^V_t (value witness wv [S])."""
+    return np.asarray(p_tilde, dtype=np.float64) @ np.asarray(wv, dtype=np.float64)
+
+
 def tanh_bound(c):
     """TV <= tanh(max_t c_t / 2) for per-token logit bounds c [..., S] (0 if S = 0)."""
     c = np.asarray(c, dtype=np.float64)
@@ -113,7 +125,7 @@ def tanh_bound(c):
 
 
 def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
-                 repaired=None, page_size=16, gate_tier="auto", num_bands=8, bypass=None):
+                 repaired=None, page_size=16, gate_tier="auto", num_bands=8, bypass=None, wv=None):
     """Decode of the query heads sharing one KV head, over S cached tokens.
 
     q [G, d]; k, khat, v, vhat [S, d]; w [S, B]; k_scale [S] (dithered INT8,
@@ -125,6 +137,8 @@ def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
       E_A, R_A [G]    Tier A meter;  E_B, R_B [G] Tier B (NaN if no k_scale)
       T_A, T_B [G]    tanh bounds tanh(max_t c_t / 2) of each tier (T_B NaN if no k_scale)
       block_cmax [G, P]  per page max of the gate tier's c (the tanh gate's input)
+      E_V [G]         value certificate sum_t p~_t w^V_t (wv given; else from vhat - v)
+      dv_true [G]     ||sum_t p~_t (v^_t - v_t)||, what E_V bounds
       tv_true [G]     TV between exact and compressed attention
       o_exact [G, d]  exact attention output
       a, u [G, S]     per-token bounds; eps [G, S] = |l~ - l|
@@ -160,7 +174,10 @@ def decode_group(q, k, khat, v, vhat, w, sm_scale, k_scale=None, log_term=None,
     block_risk = contrib.reshape(q.shape[0], P, page_size).sum(-1)
     cpad = np.concatenate([cg, np.zeros((q.shape[0], pad))], axis=1)
     block_cmax = cpad.reshape(q.shape[0], P, page_size).max(-1)
+    rv = np.asarray(vhat, dtype=np.float64) - np.asarray(v, dtype=np.float64)
+    wv_ = np.sqrt(np.sum(rv * rv, axis=-1)) if wv is None else np.asarray(wv, dtype=np.float64)
     return dict(o_tilde=pt @ np.asarray(vhat, dtype=np.float64), lse=lse,
+                E_V=pt @ wv_, dv_true=np.linalg.norm(pt @ rv, axis=-1),
                 E_A=E_A, R_A=R_A, E_B=E_B, R_B=R_B, tv_true=tv(p, pt),
                 T_A=tanh_bound(a), T_B=tanh_bound(u) if use_b else np.full(q.shape[0], np.nan),
                 block_cmax=block_cmax,
@@ -174,16 +191,18 @@ def split_ranges(num_pages, n_split):
     return [(i * num_pages // n_split, (i + 1) * num_pages // n_split) for i in range(n_split)]
 
 
-def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16):
+def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16, wv=None):
     """Per-split partials (m, l, o, N_A, N_B, C_A, C_B) of one KV head's query group.
 
     m = max l~ in the split, l = sum exp(l~ - m), o = sum exp(l~ - m) v^,
-    N_X = sum exp(l~ - m) expm1(c_X), C_X = max c_X over the split's tokens.
-    Empty splits have m = -inf, l = 0, C_X = 0.
+    N_X = sum exp(l~ - m) expm1(c_X), C_X = max c_X over the split's tokens,
+    N_V = sum exp(l~ - m) w^V (value witness wv, zeros if not given).
+    Empty splits have m = -inf, l = 0, C_X = 0, N_V = 0.
     c_a, c_b: [G, S] per-token bounds (already zero on repaired tokens).
     """
     q = np.asarray(q, dtype=np.float64)
     S = khat.shape[0]
+    wv = np.zeros(S) if wv is None else np.asarray(wv, dtype=np.float64)
     l_tilde = sm_scale * q @ np.asarray(khat, dtype=np.float64).T
     P = -(-S // page_size)
     parts = []
@@ -192,7 +211,8 @@ def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16):
         G = q.shape[0]
         if t1 <= t0:
             parts.append(dict(m=np.full(G, -np.inf), l=np.zeros(G), o=np.zeros((G, vhat.shape[1])),
-                              N_A=np.zeros(G), N_B=np.zeros(G), C_A=np.zeros(G), C_B=np.zeros(G)))
+                              N_A=np.zeros(G), N_B=np.zeros(G), C_A=np.zeros(G), C_B=np.zeros(G),
+                              N_V=np.zeros(G)))
             continue
         ls = l_tilde[:, t0:t1]
         m = np.max(ls, axis=-1)
@@ -200,7 +220,8 @@ def split_partials(q, khat, vhat, c_a, c_b, sm_scale, n_split, page_size=16):
         parts.append(dict(m=m, l=e.sum(-1), o=e @ np.asarray(vhat[t0:t1], dtype=np.float64),
                           N_A=np.sum(e * np.expm1(c_a[:, t0:t1]), -1),
                           N_B=np.sum(e * np.expm1(c_b[:, t0:t1]), -1),
-                          C_A=np.max(c_a[:, t0:t1], -1), C_B=np.max(c_b[:, t0:t1], -1)))
+                          C_A=np.max(c_a[:, t0:t1], -1), C_B=np.max(c_b[:, t0:t1], -1),
+                          N_V=e @ wv[t0:t1]))
     return parts
 
 
@@ -209,7 +230,7 @@ def lse_merge(parts):
 
     M = max_s m_s, w_s = exp(m_s - M), L = sum w_s l_s, o = sum w_s o_s / L,
     E_X = sum w_s N_X,s / L, LSE = M + log L, R_X = E_X (1 + E_X / 2),
-    T_X = tanh(max_s C_X,s / 2).
+    T_X = tanh(max_s C_X,s / 2), E_V = sum w_s N_V,s / L.
     """
     m = np.stack([p["m"] for p in parts])
     M = np.max(m, axis=0)
@@ -220,6 +241,7 @@ def lse_merge(parts):
     o = np.sum(wts[..., None] * np.stack([p["o"] for p in parts]), axis=0)
     NA = np.sum(wts * np.stack([p["N_A"] for p in parts]), axis=0)
     NB = np.sum(wts * np.stack([p["N_B"] for p in parts]), axis=0)
+    NV = np.sum(wts * np.stack([p["N_V"] for p in parts]), axis=0)
     Ls = np.where(L > 0, L, 1.0)
     E_A = np.where(L > 0, NA / Ls, 0.0)
     E_B = np.where(L > 0, NB / Ls, 0.0)
@@ -228,4 +250,4 @@ def lse_merge(parts):
     return dict(o=np.where((L > 0)[:, None], o / Ls[:, None], 0.0),
                 lse=np.where(L > 0, M + np.log(Ls), -np.inf),
                 E_A=E_A, R_A=E_A * (1 + 0.5 * E_A), E_B=E_B, R_B=E_B * (1 + 0.5 * E_B),
-                T_A=np.tanh(0.5 * CA), T_B=np.tanh(0.5 * CB))
+                T_A=np.tanh(0.5 * CA), T_B=np.tanh(0.5 * CB), E_V=np.where(L > 0, NV / Ls, 0.0))

@@ -173,6 +173,17 @@ def kivi2_values(v):
     return code.reshape(n, d), scale, mn, xhat.reshape(n, d)
 
 
+def witness_v(v, vhat):
+    """Value witness w^V_t = ||v^_t - v_t|| over all channels, float64 [n].
+
+    Reading (the pages define witnesses for keys only): the value side of the
+    certificate needs the size of each value's residual; values are not
+    rotated by RoPE, so one norm per token suffices.
+    """
+    r = np.asarray(vhat, dtype=np.float64) - np.asarray(v, dtype=np.float64)
+    return np.sqrt(np.sum(r * r, axis=-1))
+
+
 def witness(x, xhat, num_bands=8):
     """w_{t,b} = ||xhat_t - x_t|| over band b, float64 [n, num_bands]."""
     r = np.asarray(xhat, dtype=np.float64) - np.asarray(x, dtype=np.float64)
