@@ -16,7 +16,7 @@ LIB_PATH = os.environ.get("WITCERT_LIB") or os.path.join(_HERE, "libwitcert.so")
 WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
 WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2, WC_RTN_INT8, WC_BF16_STORE = 0, 1, 2, 3, 4
 WC_F32, WC_BF16 = 0, 1
-WC_METER_A, WC_METER_B, WC_BLOCK_CMAX = 1, 2, 4
+WC_METER_A, WC_METER_B, WC_BLOCK_CMAX, WC_METER_V = 1, 2, 4, 8
 PARTIAL = 136
 
 _c_void_p = ctypes.c_void_p
@@ -30,7 +30,7 @@ class WcCache(ctypes.Structure):
                 ("v_scale", _c_void_p), ("k_aux", _c_void_p), ("v_aux", _c_void_p),
                 ("witness", _c_void_p), ("exact_slot", _c_void_p), ("exact_pool", _c_void_p),
                 ("exact_scale", _c_void_p), ("pool_capacity", _i64), ("num_outliers", _i32),
-                ("reserved", _i32), ("outlier_ch", _c_void_p), ("k_outlier", _c_void_p)]
+                ("reserved", _i32), ("outlier_ch", _c_void_p), ("k_outlier", _c_void_p), ("v_witness", _c_void_p)]
 
 
 class WitcertError(RuntimeError):
@@ -49,12 +49,12 @@ def _load():
         "wc_decode_attn_meter": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
                                  P, P, ctypes.c_float, ctypes.c_uint, ctypes.c_double, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P, P],
-        "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P],
+        "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P],
         "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
         "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
-        "wc_witness": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, P],
+        "wc_witness": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, ctypes.c_int, P],
         "wc_gate_pagein_tanh": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_double,
                                 _i64, P, P, P, P, P, ctypes.c_size_t, P],
     }
@@ -108,7 +108,7 @@ class KVCache:
     """Device tensors of one paged cache (all layers) plus its C descriptor."""
 
     def __init__(self, scheme, num_layers, num_pages, num_kv_heads, device="cuda", pool_capacity=0,
-                 page_size=None, num_outliers=0):
+                 page_size=None, num_outliers=0, v_witness=False):
         self.scheme = scheme
         self.L, self.P, self.H = num_layers, num_pages, num_kv_heads
         ps = page_size or (32 if scheme == WC_KIVI2 else 16)
@@ -141,6 +141,8 @@ class KVCache:
             else:
                 self.k_scale = self.v_scale = None
         self.witness = torch.zeros(shp + (ps, 8), **f32)
+        # value witness ||v^ - v|| per token (the value certificate), optional
+        self.v_witness = torch.zeros(shp + (ps,), **f32) if v_witness else None
         self.pool_capacity = pool_capacity
         if pool_capacity > 0:
             self.exact_slot = torch.full(shp, -1, dtype=torch.int32, device=device)
@@ -162,7 +164,8 @@ class KVCache:
                               (self.k_codes, self.v_codes, self.k_scale, self.v_scale, self.k_aux,
                                self.v_aux, self.witness, self.exact_slot, self.exact_pool, self.exact_scale)],
                             pool_capacity, num_outliers, 0,
-                            *[t.data_ptr() if t is not None else None for t in (self.outlier_ch, self.k_outlier)])
+                            *[t.data_ptr() if t is not None else None for t in
+                              (self.outlier_ch, self.k_outlier, self.v_witness)])
 
     def ref(self):
         return ctypes.byref(self.desc)
@@ -180,14 +183,16 @@ def wc_write_kv(cache, k, v, slot, pos, seed, layer0=0, stream=None):
                                           _stream(stream)))
 
 
-def wc_witness(cache, x, xhat, slot, layer0=0, stream=None):
-    """x, xhat: [n_layers, n_tok, Hkv, 128] or [n_tok, Hkv, 128] (same dtype, contiguous)."""
+def wc_witness(cache, x, xhat, slot, layer0=0, values=False, stream=None):
+    """x, xhat: [n_layers, n_tok, Hkv, 128] or [n_tok, Hkv, 128] (same dtype, contiguous);
+    values=True stores the value witness instead of the banded key witness."""
     if x.dim() == 3:
         x, xhat = x[None], xhat[None]
     assert x.is_contiguous() and xhat.is_contiguous() and x.shape == xhat.shape and x.dtype == xhat.dtype
     n_layers, n_tok = x.shape[0], x.shape[1]
     _check("wc_witness", lib.wc_witness(cache.ref(), layer0, n_layers, _ptr(x), _ptr(xhat), _dtype_code(x), n_tok,
-                                        n_tok * x.shape[2] * x.shape[3], _ptr(slot), _stream(stream)))
+                                        n_tok * x.shape[2] * x.shape[3], _ptr(slot), int(bool(values)),
+                                        _stream(stream)))
 
 
 def wc_decode_workspace_bytes(B, Hq, n_split):
@@ -205,9 +210,10 @@ def wc_decode_attn_meter(cache, layer, q, page_table, ctx_len, seed, partials, s
 
 
 def wc_lse_merge(partials, B, Hq, n_split, o, lse, meter_a=None, meter_b=None, tanh_a=None, tanh_b=None,
-                 stream=None):
+                 meter_v=None, stream=None):
     _check("wc_lse_merge", lib.wc_lse_merge(_ptr(partials), B, Hq, n_split, _ptr(o), _ptr(lse), _ptr(meter_a),
-                                            _ptr(meter_b), _ptr(tanh_a), _ptr(tanh_b), _stream(stream)))
+                                            _ptr(meter_b), _ptr(tanh_a), _ptr(tanh_b), _ptr(meter_v),
+                                            _stream(stream)))
 
 
 def wc_gate_workspace_bytes(B, Hkv, max_pages):

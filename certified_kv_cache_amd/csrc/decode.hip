@@ -58,7 +58,7 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 #endif
 constexpr int kNW = WC_DECODE_WAVES;
 constexpr int kThreads = 64 * kNW;
-// floats per (b, h, split) partial: m, l, N_A, N_B, o[128], C_A, C_B, 0, 0
+// floats per (b, h, split) partial: m, l, N_A, N_B, o[128], C_A, C_B, N_V, 0
 constexpr int kPartial = 136;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -193,6 +193,7 @@ struct KLoad {
   float4 ks;
   float2 w;
   uint2 xo;               // outlier bypass: the lane's bf16 side-store entries
+  float4 wv;              // value certificate: the value witnesses of the lane's tokens
   int slot;               // exact-pool slot (-1 = quantized), wave-uniform
 };
 // Values: 8 channels x 4 tokens of codes and the value scales of the lane's
@@ -237,9 +238,18 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
 // The load count and order never depend on run-time flags, and the lane
 // offsets stay in fixed registers, so the wait for one page's data never
 // waits on the page prefetched after it.
-template <int SCHEME, bool PAIR, int NO4>
+template <int SCHEME, bool PAIR, int NO4, bool MV>
 __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const LaneOff& lo, bool meterA, KLoad& d,
                                           VLoad& e) {
+  if (MV) {                                    // value witnesses: 16 floats per page-head block
+    const __amdgpu_buffer_rsrc_t wvr = page_rsrc(c.v_witness, pg * 64, 64);
+    if (PAIR) {
+      const float2 t = bload8(wvr, lo.s);
+      d.wv = make_float4(t.x, t.y, 0.f, 0.f);
+    } else {
+      d.wv = __builtin_bit_cast(float4, bload16(wvr, lo.s));
+    }
+  }
   if (NO4 > 0) {                               // side store: 32 m bytes per page-head block
     const __amdgpu_buffer_rsrc_t orr = page_rsrc(c.k_outlier, pg * (128 * NO4), 128 * NO4);
     if (NO4 == 4)
@@ -285,7 +295,7 @@ __device__ __forceinline__ void load_page(const wc_cache& c, int64_t pg, const L
 // serves every page: the page enters as a 32-bit scalar offset, which saves
 // the per-page resource set-up.
 struct LayerBufs {
-  __amdgpu_buffer_rsrc_t k, v, w, ks, vs, o;
+  __amdgpu_buffer_rsrc_t k, v, w, ks, vs, o, wv;
 };
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t layer_rsrc(const void* base, int64_t off, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + off), (short)0,
@@ -301,9 +311,17 @@ __device__ __forceinline__ uint32_t bload4s(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
 }
 // pg: page-head block index within the layer (phys * Hkv + g)
-template <int SCHEME, bool PAIR, int NO4>
+template <int SCHEME, bool PAIR, int NO4, bool MV>
 __device__ __forceinline__ void load_page_soff(const LayerBufs& lb, uint32_t pg, const LaneOff& lo, bool meterA,
                                                KLoad& d, VLoad& e) {
+  if (MV) {
+    if (PAIR) {
+      const float2 t = bload8s(lb.wv, lo.s, pg * 64u);
+      d.wv = make_float4(t.x, t.y, 0.f, 0.f);
+    } else {
+      d.wv = __builtin_bit_cast(float4, bload16s(lb.wv, lo.s, pg * 64u));
+    }
+  }
   if (NO4 > 0) {
     if (NO4 == 4)
       d.xo = __builtin_bit_cast(uint2, bload8s(lb.o, lo.o, pg * (128u * NO4)));
@@ -378,7 +396,8 @@ constexpr int decode_waves_per_simd() {
 // CMP: the query group has at most 8 heads, so the softmax and meter run
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 // NO4: outlier bypass with m = 4 NO4 exact key channels (0 = none).
-template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4>
+// MV: the value certificate (reads the value witnesses).
+template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4, bool MV>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<SCHEME, QF32, NO4>())))
 decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -567,6 +586,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   // ---------------------------------------------------------------- state
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
   float ca_max = 0.0f, cb_max = 0.0f;          // largest per-token bound of each tier (tanh bound)
+  float nvv = 0.0f;                            // value certificate: sum 2^(l2 - m) ||v^ - v||
   f4 O[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) O[t] = f4{0.f, 0.f, 0.f, 0.f};
@@ -591,7 +611,8 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     lb.k = layer_rsrc(c.k_codes, l0 * PB, (uint64_t)lph * PB);
     lb.v = layer_rsrc(c.v_codes, l0 * PB, (uint64_t)lph * PB);
     lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
-    lb.o = lb.ks = lb.vs = lb.k;               // (unused unless set below)
+    lb.o = lb.ks = lb.vs = lb.wv = lb.k;       // (unused unless set below)
+    if (MV) lb.wv = layer_rsrc(c.v_witness, l0 * 64, (uint64_t)lph * 64);
     if (NO4 > 0) lb.o = layer_rsrc(c.k_outlier, l0 * (128 * NO4), (uint64_t)lph * (128 * NO4));
     if (int8_codes<SCHEME>()) {
       lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
@@ -611,9 +632,9 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
     d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
     if (SOFF)
-      load_page_soff<SCHEME, CMP, NO4>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
+      load_page_soff<SCHEME, CMP, NO4, MV>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
     else
-      load_page<SCHEME, CMP, NO4>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
+      load_page<SCHEME, CMP, NO4, MV>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
   };
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
     // the page kDepth ahead; past the end the last page loads itself again
@@ -767,6 +788,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     float l2[4], cB[4];
     const float kapB = (meterB && !exact) ? kappac : 0.0f;
     float sv[4] = {vl.vs.x, vl.vs.y, vl.vs.z, vl.vs.w};
+    float wvv[4] = {cur.wv.x, cur.wv.y, cur.wv.z, cur.wv.w};
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       l2[r] = qs2c * st[r] * raw[r];
@@ -781,6 +803,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
         cA[r] = ok ? cA[r] : 0.0f;
         cB[r] = ok ? cB[r] : 0.0f;
         sv[r] = ok ? sv[r] : 0.0f;
+        if (MV) wvv[r] = ok ? wvv[r] : 0.0f;
       }
     }
 
@@ -806,6 +829,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       const float alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
       l_run *= alpha;
       na *= alpha;
+      if (MV) nvv *= alpha;
       nb *= alpha;
       vsum *= alpha;
 #pragma unroll
@@ -820,6 +844,10 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       psum += p[r];
     }
     l_run += psum;
+    if (MV) {                                  // repaired blocks too: their values stay quantized
+#pragma unroll
+      for (int r = 0; r < NV; ++r) nvv = fmaf(p[r], wvv[r], nvv);
+    }
     // meter terms p (e^c - 1) = 2^(l2 - m + c log2 e) - p: one exp per token, and
     // a bound large enough to overflow saturates the meter at +inf.  A bound in
     // (0, 2^-6) would lose relative precision to the subtraction: then the
@@ -1006,17 +1034,19 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     l_run += dpp_ror8(l_run);
     na += dpp_ror8(na);
     nb += dpp_ror8(nb);
+    if (MV) nvv += dpp_ror8(nvv);
     ca_max = vmax(ca_max, dpp_ror8(ca_max));
     cb_max = vmax(cb_max, dpp_ror8(cb_max));
   }
   l_run = sum4k(l_run);
   na = sum4k(na);
   nb = sum4k(nb);
+  if (MV) nvv = sum4k(nvv);
   ca_max = max4k(ca_max);
   cb_max = max4k(cb_max);
   __syncthreads();                             // the dither tiles are reused below
   float (*sO)[16][128] = reinterpret_cast<float (*)[16][128]>(smem);
-  __shared__ float sM[kNW][16][6];
+  __shared__ float sM[kNW][16][7];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -1028,6 +1058,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     sM[wave][n][3] = nb;
     sM[wave][n][4] = ca_max;
     sM[wave][n][5] = cb_max;
+    sM[wave][n][6] = nvv;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < G * kPartial; e += kThreads) {
@@ -1038,10 +1069,18 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     float val = 0.0f;
     if (f == 0) {
       val = M;
-    } else if (f >= 132) {                     // largest bounds: max over the waves
+    } else if (f >= 132 && f != 134) {         // largest bounds: max over the waves
       if (f < 134) {
 #pragma unroll
         for (int w = 0; w < kNW; ++w) val = fmaxf(val, sM[w][hn][f - 128]);
+      }
+    } else if (f == 134) {                     // value certificate sum, rescaled like l
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+          const float mw = sM[w][hn][0];
+          val = fmaf(mw == -INFINITY ? 0.0f : exp2f(mw - M), sM[w][hn][6], val);
+        }
       }
     } else if (M != -INFINITY) {
 #pragma unroll
@@ -1073,27 +1112,29 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ part, int n_split, float* o,
                                                    float* lse, float* meter_a, float* meter_b, float* tanh_a,
-                                                   float* tanh_b) {
+                                                   float* tanh_b, float* meter_v) {
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* pp = part + (int64_t)bh * n_split * kPartial;
   float M = -INFINITY;
   for (int s = lane; s < n_split; s += 64) M = fmaxf(M, pp[s * kPartial]);
   M = wave_max(M);
   auto weight = [&](float ms) { return (ms == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(ms - M); };
-  float L = 0.f, NA = 0.f, NB = 0.f, CA = 0.f, CB = 0.f;
+  float L = 0.f, NA = 0.f, NB = 0.f, CA = 0.f, CB = 0.f, NV = 0.f;
   for (int s = lane; s < n_split; s += 64) {
     const float4 q = *reinterpret_cast<const float4*>(pp + s * kPartial);
-    const float2 cm = *reinterpret_cast<const float2*>(pp + s * kPartial + 132);
+    const float4 cm = *reinterpret_cast<const float4*>(pp + s * kPartial + 132);
     const float w = weight(q.x);
     L = fmaf(w, q.y, L);
     NA = fmaf(w, q.z, NA);
     NB = fmaf(w, q.w, NB);
     CA = fmaxf(CA, cm.x);
     CB = fmaxf(CB, cm.y);
+    NV = fmaf(w, cm.z, NV);
   }
   L = wave_sum(L);
   NA = wave_sum(NA);
   NB = wave_sum(NB);
+  NV = wave_sum(NV);
   CA = wave_max(CA);
   CB = wave_max(CB);
   float o0 = 0.f, o1 = 0.f;
@@ -1128,6 +1169,7 @@ __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ par
     if (meter_b) meter_b[bh] = eb * (1.0f + 0.5f * eb);
     if (tanh_a) tanh_a[bh] = tanhf(0.5f * CA);
     if (tanh_b) tanh_b[bh] = tanhf(0.5f * CB);
+    if (meter_v) meter_v[bh] = NV * inv;
   }
 }
 
@@ -1138,6 +1180,42 @@ using namespace wc;
 extern "C" size_t wc_decode_workspace_bytes(int B, int Hq, int n_split) {
   if (B < 0 || Hq < 0 || n_split < 0) return 0;
   return (size_t)B * Hq * n_split * kPartial * sizeof(float);
+}
+
+// Host dispatch from the run-time shape to the template instance.
+template <int SCH, bool QF, bool CM, bool SO, int NO>
+static void launch_mv(bool mv, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
+  if (mv)
+    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, true>), grid, dim3(kThreads), 0, st, c, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false>), grid, dim3(kThreads), 0, st, c, a);
+}
+template <int SCH, bool QF, bool CM, bool SO>
+static void launch_no(int no4, bool mv, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
+  if constexpr (SCH == WC_DITHER_INT8) {
+    if (no4 == 2) return launch_mv<SCH, QF, CM, SO, 2>(mv, grid, st, c, a);
+    if (no4 == 4) return launch_mv<SCH, QF, CM, SO, 4>(mv, grid, st, c, a);
+  }
+  launch_mv<SCH, QF, CM, SO, 0>(mv, grid, st, c, a);
+}
+template <int SCH, bool QF>
+static void launch_shape(bool cm, bool so, int no4, bool mv, dim3 grid, hipStream_t st, const wc_cache& c,
+                         const DecodeArgs& a) {
+  if (cm) {
+    if (so) launch_no<SCH, QF, true, true>(no4, mv, grid, st, c, a); else launch_no<SCH, QF, true, false>(no4, mv, grid, st, c, a);
+  } else {
+    if (so) launch_no<SCH, QF, false, true>(no4, mv, grid, st, c, a); else launch_no<SCH, QF, false, false>(no4, mv, grid, st, c, a);
+  }
+}
+template <bool QF>
+static void launch_scheme(int scheme, bool cm, bool so, int no4, bool mv, dim3 grid, hipStream_t st,
+                          const wc_cache& c, const DecodeArgs& a) {
+  switch (scheme) {
+    case WC_DITHER_INT8: launch_shape<WC_DITHER_INT8, QF>(cm, so, no4, mv, grid, st, c, a); break;
+    case WC_FP8_E4M3: launch_shape<WC_FP8_E4M3, QF>(cm, so, no4, mv, grid, st, c, a); break;
+    case WC_RTN_INT8: launch_shape<WC_RTN_INT8, QF>(cm, so, no4, mv, grid, st, c, a); break;
+    default: launch_shape<WC_BF16_STORE, QF>(cm, so, no4, mv, grid, st, c, a); break;
+  }
 }
 
 extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_dtype, int B, int Hq,
@@ -1168,7 +1246,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: bad B/Hq/max_pages/n_split/layer");
     return WC_EINVAL;
   }
-  if (meter_mask & ~(WC_METER_A | WC_METER_B | WC_BLOCK_CMAX)) {
+  if (meter_mask & ~(WC_METER_A | WC_METER_B | WC_BLOCK_CMAX | WC_METER_V)) {
     set_error("wc_decode_attn_meter: unknown meter_mask bits");
     return WC_EINVAL;
   }
@@ -1182,6 +1260,10 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   }
   if (block_logrisk && !(meter_mask & WC_METER_A)) {
     set_error("wc_decode_attn_meter: block risks need the meter on");
+    return WC_EINVAL;
+  }
+  if ((meter_mask & WC_METER_V) && !c.v_witness) {
+    set_error("wc_decode_attn_meter: the value certificate needs the value witness");
     return WC_EINVAL;
   }
   if ((meter_mask & WC_BLOCK_CMAX) && !block_logrisk) {
@@ -1232,60 +1314,24 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   // one buffer resource per layer array when its byte offsets fit 32 bits
   const uint64_t page_b = c.scheme == WC_BF16_STORE ? 4096u : 2048u;
   const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * page_b <= 0xFFFFFFFFull;
-#define WC_LAUNCH_NO(SCH, QF, CM, NO)                                                                 \
-  do {                                                                                               \
-    if (soff)                                                                                        \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, true, NO>), grid, dim3(kThreads), 0, st, c, a); \
-    else                                                                                             \
-      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, false, NO>), grid, dim3(kThreads), 0, st, c, a); \
-  } while (0)
-#define WC_LAUNCH(SCH, QF, CM)                                               \
-  do {                                                                       \
-    if (SCH != WC_DITHER_INT8 || c.num_outliers == 0)                        \
-      WC_LAUNCH_NO(SCH, QF, CM, 0);                                          \
-    else if (c.num_outliers == 8)                                            \
-      WC_LAUNCH_NO(SCH, QF, CM, (SCH == WC_DITHER_INT8 ? 2 : 0));            \
-    else                                                                     \
-      WC_LAUNCH_NO(SCH, QF, CM, (SCH == WC_DITHER_INT8 ? 4 : 0));            \
-  } while (0)
-  if (c.scheme == WC_DITHER_INT8) {
-    if (q_dtype == WC_BF16) {
-      if (cmp) WC_LAUNCH(WC_DITHER_INT8, false, true); else WC_LAUNCH(WC_DITHER_INT8, false, false);
-    } else {
-      if (cmp) WC_LAUNCH(WC_DITHER_INT8, true, true); else WC_LAUNCH(WC_DITHER_INT8, true, false);
-    }
-  } else if (c.scheme == WC_FP8_E4M3) {
-    if (q_dtype == WC_BF16) {
-      if (cmp) WC_LAUNCH(WC_FP8_E4M3, false, true); else WC_LAUNCH(WC_FP8_E4M3, false, false);
-    } else {
-      if (cmp) WC_LAUNCH(WC_FP8_E4M3, true, true); else WC_LAUNCH(WC_FP8_E4M3, true, false);
-    }
-  } else if (c.scheme == WC_RTN_INT8) {
-    if (q_dtype == WC_BF16) {
-      if (cmp) WC_LAUNCH(WC_RTN_INT8, false, true); else WC_LAUNCH(WC_RTN_INT8, false, false);
-    } else {
-      if (cmp) WC_LAUNCH(WC_RTN_INT8, true, true); else WC_LAUNCH(WC_RTN_INT8, true, false);
-    }
-  } else {
-    if (q_dtype == WC_BF16) {
-      if (cmp) WC_LAUNCH(WC_BF16_STORE, false, true); else WC_LAUNCH(WC_BF16_STORE, false, false);
-    } else {
-      if (cmp) WC_LAUNCH(WC_BF16_STORE, true, true); else WC_LAUNCH(WC_BF16_STORE, true, false);
-    }
-  }
-#undef WC_LAUNCH
-#undef WC_LAUNCH_NO
+  const int no4 = c.scheme == WC_DITHER_INT8 ? c.num_outliers / 4 : 0;
+  const bool mv = (meter_mask & WC_METER_V) != 0;
+  if (q_dtype == WC_BF16)
+    launch_scheme<false>(c.scheme, cmp, soff, no4, mv, grid, st, c, a);
+  else
+    launch_scheme<true>(c.scheme, cmp, soff, no4, mv, grid, st, c, a);
   return check_launch("wc_decode_attn_meter");
 }
 
 extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
-                            float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, void* stream) {
+                            float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, float* meter_v,
+                            void* stream) {
   if (!partials || !o || !lse || B < 0 || Hq < 1 || n_split < 1 || n_split > 1024) {
     set_error("wc_lse_merge: bad arguments");
     return WC_EINVAL;
   }
   if (B == 0) return WC_OK;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split, o,
-                     lse, meter_a, meter_b, tanh_a, tanh_b);
+                     lse, meter_a, meter_b, tanh_a, tanh_b, meter_v);
   return check_launch("wc_lse_merge");
 }

@@ -186,7 +186,15 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
           c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] =
               reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
       }
-    } else if (live) {
+    } else {
+      // value witness ||v^ - v|| over the row's 128 channels (16-lane sum)
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) ss += shfl_xor(ss, m);
+      if (!live) continue;
+      if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = sqrtf(ss) * kWitnessGuard;
       // channel 8 lane16 + k of token off: half k / 4, token group off / 4,
       // channel group lane16, word k % 4, byte off % 4
       uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
@@ -226,10 +234,12 @@ __global__ void __launch_bounds__(256) write_bf16_kernel(wc_cache c, const uint1
     vb[(e >> 1) * 512 + (off >> 2) * 128 + lane16 * 8 + (e & 1) * 4 + (off & 3)] =
         (uint16_t)((e & 1) ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
   if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = 0.0f;
+  if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = 0.0f;
 }
 
-// Witness of an arbitrary scheme's output: w_{t,b} = ||xhat - x|| over band b.
-template <typename T>
+// Witness of an arbitrary scheme's output: keys w_{t,b} = ||xhat - x|| over
+// band b; values (VAL) ||xhat - x|| over the whole row.
+template <typename T, bool VAL>
 __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __restrict__ x, const T* __restrict__ xh,
                                                       RowArgs a) {
   const int lane16 = threadIdx.x & 15;
@@ -249,6 +259,16 @@ __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __res
   for (int k = 0; k < 8; ++k) {
     const float r = hv[k] - xv[k];
     ss = fmaf(r, r, ss);
+  }
+  if (VAL) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) ss += shfl_xor(ss, m);
+    if (live && lane16 == 0) {
+      const int64_t slot = a.slot[i];
+      const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
+      c.v_witness[pg * 16 + slot % 16] = sqrtf(ss) * kWitnessGuard;
+    }
+    return;
   }
   const float tot = ss + shfl_xor(ss, 8);
   if (live && lane16 < 8) {
@@ -361,12 +381,20 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
     const float vs = div_rn(vmx - vmn, 3.0f);
     const float vinv = vs != 0.0f ? div_rn(1.0f, vs) : 0.0f;
     uint32_t pk = 0;
+    float vss = 0.0f;
     for (int k = 0; k < 16; ++k) {
       uint32_t code;
       float xh;
       quant2(x[k], vmn, vs, vinv, code, xh);
       pk |= code << (2 * k);
+      const float rv = xh - x[k];
+      vss = fmaf(rv, rv, vss);
     }
+    // value witness of the token: its 8 threads (t & 7) hold 16 channels each
+    vss += __shfl_xor(vss, 1, 64);
+    vss += __shfl_xor(vss, 2, 64);
+    vss += __shfl_xor(vss, 4, 64);
+    if (c.v_witness && part == 0) c.v_witness[pg * 32 + tok] = sqrtf(vss) * kWitnessGuard;
     uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 1024 + tok * 32 + 4 * part;
     *reinterpret_cast<uint32_t*>(vc) = pk;
     if ((part & 1) == 0) {
@@ -553,7 +581,8 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
 }
 
 extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat,
-                          int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot, void* stream) {
+                          int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot, int values,
+                          void* stream) {
   if (!cache || !x || !xhat || !slot) {
     set_error("wc_witness: null pointer");
     return WC_EINVAL;
@@ -563,8 +592,12 @@ extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const
     set_error("wc_witness: need head_dim 128, 8 bands, 16-token pages");
     return WC_EUNSUPPORTED;
   }
-  if (!c.witness) {
-    set_error("wc_witness: cache witness not set");
+  if (values != 0 && values != 1) {
+    set_error("wc_witness: values must be 0 (keys) or 1 (values)");
+    return WC_EINVAL;
+  }
+  if (values ? !c.v_witness : !c.witness) {
+    set_error("wc_witness: cache %s witness not set", values ? "value" : "key");
     return WC_EINVAL;
   }
   if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_tok < 0 ||
@@ -580,12 +613,22 @@ extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const
   RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, nullptr, nullptr};
   const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
   dim3 grid((unsigned)((rows + 15) / 16));
-  if (in_dtype == WC_BF16)
-    hipLaunchKernelGGL((witness_kernel<uint16_t>), grid, dim3(256), 0, (hipStream_t)stream, c, (const uint16_t*)x,
-                       (const uint16_t*)xhat, a);
-  else
-    hipLaunchKernelGGL((witness_kernel<float>), grid, dim3(256), 0, (hipStream_t)stream, c, (const float*)x,
-                       (const float*)xhat, a);
+  hipStream_t st = (hipStream_t)stream;
+  if (in_dtype == WC_BF16) {
+    if (values)
+      hipLaunchKernelGGL((witness_kernel<uint16_t, true>), grid, dim3(256), 0, st, c, (const uint16_t*)x,
+                         (const uint16_t*)xhat, a);
+    else
+      hipLaunchKernelGGL((witness_kernel<uint16_t, false>), grid, dim3(256), 0, st, c, (const uint16_t*)x,
+                         (const uint16_t*)xhat, a);
+  } else {
+    if (values)
+      hipLaunchKernelGGL((witness_kernel<float, true>), grid, dim3(256), 0, st, c, (const float*)x,
+                         (const float*)xhat, a);
+    else
+      hipLaunchKernelGGL((witness_kernel<float, false>), grid, dim3(256), 0, st, c, (const float*)x,
+                         (const float*)xhat, a);
+  }
   return check_launch("wc_witness");
 }
 

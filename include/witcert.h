@@ -61,6 +61,15 @@
  *            channels O of each layer and KV head, ascending and distinct.
  *  k_outlier bf16 [L][P][Hkv][16][m]: entry i of a token is its exact key on
  *            channel O[i].
+ *  v_witness fp32 [L][P][Hkv][page]: the value witness w^V_t = ||v^_t - v_t||
+ *            over all 128 channels (written when the pointer is set).
+ *
+ * Value certificate (WC_METER_V).  The summary reports joint K+V coverage but
+ * defines witnesses for keys only.  Reading implemented here: the value
+ * witness above, and E_V = sum_t p~_t w^V_t, which bounds the value part of
+ * the output error, ||sum_t p~_t (v^_t - v_t)||, by the triangle inequality
+ * for any value quantizer; with the key side's TV,
+ * ||o~ - o|| <= E_V + 2 TV max_t ||v_t||.
  *
  * Outlier bypass (dithered INT8 keys, m = 8 or 16).  The summary reports the
  * capacity of the certified INT8 cache with an outlier bypass too, and
@@ -105,6 +114,7 @@ extern "C" {
 #define WC_METER_A 1u
 #define WC_METER_B 2u
 #define WC_BLOCK_CMAX 4u /* block output = largest per-token bound (tanh gate) */
+#define WC_METER_V 8u    /* value certificate (needs cache->v_witness)       */
 
 typedef struct {
   int32_t scheme;       /* WC_DITHER_INT8 | WC_FP8_E4M3 | WC_KIVI2          */
@@ -129,6 +139,7 @@ typedef struct {
   int32_t reserved;     /* 0                                                 */
   int32_t* outlier_ch;  /* [L][Hkv][m] when m > 0                            */
   uint16_t* k_outlier;  /* bf16 [L][P][Hkv][16][m] when m > 0                */
+  float* v_witness;     /* fp32 [L][P][Hkv][page]: ||v^_t - v_t|| (nullable) */
 } wc_cache;
 
 /*
@@ -150,13 +161,14 @@ typedef struct {
  *  pos        device int32 [n_tok]: the token's 0-based position in its
  *             sequence (dither counter).
  *  seed       device uint64 [n_tok]: dither seed of the token's sequence.
- * Writes k_codes, v_codes, scales (or aux) and the key witness; with the
+ * Writes k_codes, v_codes, scales (or aux), the key witness and, when
+ * cache->v_witness is set, the value witness; with the
  * outlier bypass (num_outliers > 0, bf16 input only) also k_outlier, reading
  * the channels of each layer from outlier_ch.  RTN INT8: code =
  * clamp(rint(x * (127/absmax)), -128, 127), x^ = s code.  16-bit store
  * (bf16 input only): k and v are stored as given (they are the scheme's
- * outputs x^) and the witness is set to 0; wc_witness then stores the
- * witness of the scheme's residual.
+ * outputs x^) and the witnesses are set to 0; wc_witness then stores the
+ * witnesses of the scheme's residuals.
  */
 int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
                 int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
@@ -176,11 +188,13 @@ int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, 
  *  x, xhat    device, dtype in_dtype (WC_F32 | WC_BF16), [n_layers][n_tok][Hkv][128],
  *             layer l at l * layer_stride elements; x = exact post-RoPE keys.
  *  slot       device int64 [n_tok]: page * 16 + offset (16-token pages).
+ *  values     0: x are keys, the banded key witness goes to cache->witness;
+ *             1: x are values, ||x^ - x|| goes to cache->v_witness.
  * The stored value is rounded up (by a factor 1 + 2^-17) so that it never
  * falls below the exact norm.
  */
 int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat, int in_dtype,
-               int64_t n_tok, int64_t layer_stride, const int64_t* slot, void* stream);
+               int64_t n_tok, int64_t layer_stride, const int64_t* slot, int values, void* stream);
 
 /*
  * wc_outlier_select -- the outlier-bypass channels of each (layer, KV head).
@@ -218,7 +232,9 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *  page_table device int32 [B][max_pages] physical page of each logical block.
  *  ctx_len    device int32 [B]: tokens cached per sequence (<= max_pages*16).
  *  seed       device uint64 [B]: dither seed of each sequence.
- *  meter_mask 0, WC_METER_A or WC_METER_A|WC_METER_B (B needs dithered INT8).
+ *  meter_mask 0, WC_METER_A or WC_METER_A|WC_METER_B (B needs dithered INT8),
+ *             plus WC_METER_V for the value certificate (any scheme; needs
+ *             cache->v_witness) and WC_BLOCK_CMAX for the block output mode.
  *  Schemes: dithered INT8, fp8, RTN INT8 and the 16-bit store (2-bit has
  *             no decode path).
  *             With 0 the witness is not read; output and LSE bits are the same
@@ -226,10 +242,11 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *  n_split    1..1024 KV splits per (sequence, KV head): split i covers blocks
  *             [i*P_b/n_split, (i+1)*P_b/n_split) of the sequence's P_b blocks.
  *  partials   device fp32 workspace [B][Hq][n_split][136]: per split
- *             (m, l, N_A, N_B, o[128], C_A, C_B, 0, 0) with m the running max
- *             of the logits in log2 units, l = sum 2^(l2 - m),
- *             N_X = sum 2^(l2 - m) expm1(c_X), o = sum 2^(l2 - m) v^ and
- *             C_X = max_t c_X (for the tanh bound).
+ *             (m, l, N_A, N_B, o[128], C_A, C_B, N_V, 0) with m the running
+ *             max of the logits in log2 units, l = sum 2^(l2 - m),
+ *             N_X = sum 2^(l2 - m) expm1(c_X), o = sum 2^(l2 - m) v^,
+ *             C_X = max_t c_X (for the tanh bound) and N_V = sum 2^(l2 - m) w^V
+ *             (WC_METER_V, else 0).
  *             ws_bytes >= wc_decode_workspace_bytes().
  *  block_logrisk  nullable device fp32 [B][Hq][max_pages]: natural log of
  *             sum_{t in block} exp(l_t) expm1(c_t) for the gate's tier (B if
@@ -264,9 +281,11 @@ size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
  *           most c_t: the log-ratio of the two softmaxes then spans at most
  *           2 max c, and a span D gives TV <= tanh(D/4)).  0 when the tier
  *           is off or the sequence is empty.
+ *  meter_v  nullable device fp32 [B][Hq]: the value certificate E_V (0 when
+ *           WC_METER_V was off).
  */
 int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
-                 float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, void* stream);
+                 float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, float* meter_v, void* stream);
 
 /*
  * wc_gate_pagein -- meter-driven repair from the exact backing store.

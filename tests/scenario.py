@@ -16,7 +16,7 @@ from tests import helpers as H
 
 class Scenario:
     def __init__(self, scheme, k, v, q, ctx_lens, dtype, Hkv, layer=1, num_layers=2, seed=5, pool_capacity=0,
-                 extra_pages=3, delta=(1e-2, 28, 28, 256), num_outliers=0, khat=None, vhat=None):
+                 extra_pages=3, delta=(1e-2, 28, 28, 256), num_outliers=0, khat=None, vhat=None, v_witness=False):
         from certified_kv_cache_amd import _lib as L
         self.L = L
         self.scheme, self.dtype, self.Hkv = scheme, dtype, Hkv
@@ -29,7 +29,7 @@ class Scenario:
         self.seeds = inputs.seeds(self.B, base=1000 + seed)
         self.k, self.v, self.q = k, v, q
         self.cache = L.KVCache(scheme, num_layers, self.num_pages, Hkv, pool_capacity=pool_capacity,
-                               num_outliers=num_outliers)
+                               num_outliers=num_outliers, v_witness=v_witness)
         # outlier bypass: the oracle's top-energy channels over all cached keys of each head
         self.bypass = None
         if num_outliers:
@@ -52,26 +52,30 @@ class Scenario:
                               self.dev["pos"], self.dev["tseed"], layer0=layer)
                 L.wc_witness(self.cache, H.dev_tensor(k, dtype), H.dev_tensor(khat, dtype), self.dev["slot"],
                              layer0=layer)
+                if v_witness:
+                    L.wc_witness(self.cache, H.dev_tensor(v, dtype), H.dev_tensor(vhat, dtype), self.dev["slot"],
+                                 layer0=layer, values=True)
             else:
                 L.wc_write_kv(self.cache, H.dev_tensor(k, dtype), H.dev_tensor(v, dtype), self.dev["slot"],
                               self.dev["pos"], self.dev["tseed"], layer0=layer)
         self.offsets = np.concatenate([[0], np.cumsum(self.ctx)])
 
-    def decode(self, n_split=4, mask=3, risk=False, sm=H.SM, cmax=False):
+    def decode(self, n_split=4, mask=3, risk=False, sm=H.SM, cmax=False, vcert=False):
         L = self.L
         B, Hq = self.B, self.Hq
         part = torch.empty(L.wc_decode_workspace_bytes(B, Hq, n_split) // 4, dtype=torch.float32, device="cuda")
         br = torch.full((B, Hq, self.tab.shape[1]), float("nan"), device="cuda") if (risk or cmax) else None
         L.wc_decode_attn_meter(self.cache, self.layer, self.dev["q"], self.dev["tab"], self.dev["ctx"],
-                               self.dev["seed"], part, sm, mask | (L.WC_BLOCK_CMAX if cmax else 0), self.delta[0],
+                               self.dev["seed"], part, sm,
+                               mask | (L.WC_BLOCK_CMAX if cmax else 0) | (L.WC_METER_V if vcert else 0), self.delta[0],
                                *self.delta[1:], n_split, block_logrisk=br)
         o = torch.empty((B, Hq, 128), device="cuda")
         lse = torch.empty((B, Hq), device="cuda")
-        ra, rb, ta, tb = (torch.empty((B, Hq), device="cuda") for _ in range(4))
-        L.wc_lse_merge(part, B, Hq, n_split, o, lse, ra, rb, ta, tb)
+        ra, rb, ta, tb, ev = (torch.empty((B, Hq), device="cuda") for _ in range(5))
+        L.wc_lse_merge(part, B, Hq, n_split, o, lse, ra, rb, ta, tb, ev)
         torch.cuda.synchronize()
         out = dict(o=o.cpu().numpy(), lse=lse.cpu().numpy(), R_A=ra.cpu().numpy(), R_B=rb.cpu().numpy(),
-                   T_A=ta.cpu().numpy(), T_B=tb.cpu().numpy(), part=part.cpu().numpy())
+                   T_A=ta.cpu().numpy(), T_B=tb.cpu().numpy(), E_V=ev.cpu().numpy(), part=part.cpu().numpy())
         if risk:
             out["logrisk"] = br.cpu().numpy()
         if cmax:

@@ -97,8 +97,8 @@ def test_decode_rejects_bad_arguments():
 def test_merge_and_gate_reject_bad_arguments():
     L = _lib()
     p = ctypes.c_void_p(16)
-    assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None, None, None) == L.WC_EINVAL
-    assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None, None, None) == L.WC_EINVAL
+    assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None, None, None, None) == L.WC_EINVAL
+    assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None, None, None, None) == L.WC_EINVAL
     g = L.lib.wc_gate_pagein
     c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
     wsb = L.wc_gate_workspace_bytes(2, 4, 8)
@@ -169,12 +169,14 @@ def test_blackbox_schemes_reject_bad_arguments():
     p = ctypes.c_void_p(16)
     w = L.lib.wc_witness
     ok = ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE))
-    assert w(None, 0, 1, p, p, 1, 4, 0, p, None) == L.WC_EINVAL
-    assert w(ok, 0, 1, p, None, 1, 4, 0, p, None) == L.WC_EINVAL
-    assert w(ok, 1, 2, p, p, 1, 4, 0, p, None) == L.WC_EINVAL              # layer range
-    assert w(ok, 0, 1, p, p, 9, 4, 0, p, None) == L.WC_EUNSUPPORTED        # dtype
-    assert w(ctypes.byref(_cache(L, witness=None)), 0, 1, p, p, 1, 4, 0, p, None) == L.WC_EINVAL
-    assert w(ok, 0, 1, p, p, 1, 0, 0, p, None) == L.WC_OK                  # nothing to do
+    assert w(None, 0, 1, p, p, 1, 4, 0, p, 0, None) == L.WC_EINVAL
+    assert w(ok, 0, 1, p, None, 1, 4, 0, p, 0, None) == L.WC_EINVAL
+    assert w(ok, 1, 2, p, p, 1, 4, 0, p, 0, None) == L.WC_EINVAL              # layer range
+    assert w(ok, 0, 1, p, p, 9, 4, 0, p, 0, None) == L.WC_EUNSUPPORTED        # dtype
+    assert w(ctypes.byref(_cache(L, witness=None)), 0, 1, p, p, 1, 4, 0, p, 0, None) == L.WC_EINVAL
+    assert w(ok, 0, 1, p, p, 1, 4, 0, p, 1, None) == L.WC_EINVAL              # no value witness array
+    assert w(ok, 0, 1, p, p, 1, 4, 0, p, 2, None) == L.WC_EINVAL
+    assert w(ok, 0, 1, p, p, 1, 0, 0, p, 0, None) == L.WC_OK                  # nothing to do
     wr = L.lib.wc_write_kv
     assert wr(ok, 0, 1, p, p, 0, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED  # the store takes bf16
     assert wr(ctypes.byref(_cache(L, scheme=L.WC_RTN_INT8, k_scale=None)), 0, 1, p, p, 1, 4, 0, p, p, p,
@@ -189,3 +191,4 @@ def test_blackbox_schemes_reject_bad_arguments():
     assert call(_cache(L, scheme=L.WC_BF16_STORE), mask=3) == L.WC_EINVAL
     assert call(_cache(L, scheme=L.WC_RTN_INT8, v_scale=None)) == L.WC_EINVAL
     assert call(_cache(L, scheme=L.WC_RTN_INT8, num_outliers=8, outlier_ch=16, k_outlier=16)) == L.WC_EUNSUPPORTED
+    assert call(_cache(L), mask=1 | L.WC_METER_V) == L.WC_EINVAL              # no value witness array
