@@ -148,6 +148,31 @@ def scheme_variant(w, B, S, iters, scheme):
             "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
+def vcert_variant(w, B, S, iters):
+    """The headline decode with the value certificate added (value witness
+    stored at write time, E_V in the same pass)."""
+    import torch
+    L = w["L"]
+    cache = L.KVCache(L.WC_DITHER_INT8, 1, w["npages"], HKV, v_witness=True)
+    L.wc_write_kv(cache, w["k"], w["v"], w["slot"], w["pos"], w["seed"].repeat_interleave(S))
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    sm = 1.0 / math.sqrt(D)
+
+    def decode(mask=3, with_risk=True):
+        L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    t_v = min(time_decode(decode, iters, mask=3 | L.WC_METER_V), time_decode(decode, iters, mask=3 | L.WC_METER_V))
+    t_kv = min(time_decode(decode, iters, mask=3), time_decode(decode, iters, mask=3))
+    nb = decode_bytes(B, S, True) + B * S * HKV * 4
+    del cache
+    return {"decode_us": round(t_v, 2), "decode_without_v_us": round(t_kv, 2),
+            "v_overhead": round(t_v / t_kv - 1, 4), "decode_bytes": nb,
+            "achieved_GBps": round(nb / (t_v * 1e-6) / 1e9, 1), "frac": round(nb / (t_v * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
 def outlier_variant(w, B, S, iters, m):
     """The same workload with the outlier bypass of the keys (m exact bf16
     channels per KV head, chosen by key energy over the first 4096 cached
@@ -508,6 +533,7 @@ def main():
     out["outlier_variant"] = [outlier_variant(w, B, S, iters, m) for m in (8, 16)]
     out["rtn_variant"] = scheme_variant(w, B, S, iters, "rtn")
     out["store16_variant"] = scheme_variant(w, B, S, iters, "store16")
+    out["vcert_variant"] = vcert_variant(w, B, S, iters)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
     if args.copy_ref:
