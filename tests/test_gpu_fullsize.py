@@ -2,8 +2,10 @@
 
 * decode: batch 32 x 32768 tokens, 28 query / 4 KV heads, 16 KV splits, block
   risks on -- the launch configuration bench.py times -- for the dithered INT8
-  cache (Tier A + B) and the fp8 raw-cast cache (Tier A); codes, scales,
-  witnesses, outputs, meters and block risks of sampled (sequence, KV head)
+  cache (Tier A + B), the fp8 raw-cast cache (Tier A), and the variants bench.py
+  reports beside them (outlier bypass m = 8, RTN INT8, the 16-bit store of a
+  4-bit-mantissa scheme, the value certificate); codes, scales, witnesses,
+  outputs, meters, tanh bounds and block risks of sampled (sequence, KV head)
   pairs against the oracle, and size-independent properties on every head;
 * write: the 28-layer prefill (4096 tokens, 4 KV heads, per-channel variance
   log-uniform in [0.1, 10]) for all three schemes, sampled (layer, head) rows
@@ -20,7 +22,7 @@ import pytest
 import torch
 
 from certified_kv_cache_amd import inputs
-from oracle import gate, meter, quant
+from oracle import gate, meter, outlier, quant
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -56,48 +58,71 @@ def _rows_of(arr, layer, pages, g):
 
 
 # ---------------------------------------------------------------- decode, bench configuration
+def _mantissa4_t(x):
+    """The 16-bit store's scheme under test (torch, on the device): bf16 with 4
+    of its 8 significant bits, rounded half up on the magnitude."""
+    b = x.view(torch.int16).to(torch.int32) & 0xFFFF
+    return (((b + 4) & 0xFFF8) & 0xFFFF).to(torch.int16).view(torch.bfloat16)
+
+
 def _decode_full(scheme_name, seed=3):
     L = H.need_gpu()
-    scheme = L.WC_DITHER_INT8 if scheme_name == "int8" else L.WC_FP8_E4M3
-    mask = 3 if scheme_name == "int8" else 1
+    scheme = {"int8": L.WC_DITHER_INT8, "fp8": L.WC_FP8_E4M3, "int8-bypass8": L.WC_DITHER_INT8,
+              "rtn": L.WC_RTN_INT8, "store16": L.WC_BF16_STORE, "int8-vcert": L.WC_DITHER_INT8}[scheme_name]
+    mask = 3 if scheme_name.startswith("int8") else 1
+    vcert = scheme_name == "int8-vcert"
     k, v = inputs.decode_kv_torch(seed, B, S, Hkv=HKV)
     q = inputs.query_torch(seed, B, Hq=HQ)
     ctx = np.full(B, S)
     tab, npages = inputs.page_table(seed, ctx)
     seeds = inputs.seeds(B, base=1000 + seed)
-    cache = L.KVCache(scheme, 1, npages, HKV)
+    cache = L.KVCache(scheme, 1, npages, HKV, num_outliers=8 if scheme_name == "int8-bypass8" else 0,
+                      v_witness=vcert)
+    if scheme_name == "int8-bypass8":                 # calibration: the first 4096 cached tokens
+        L.wc_outlier_select(k[:4096].contiguous(), 8, cache.outlier_ch)
     tab_d = torch.from_numpy(tab).cuda()
     t = torch.arange(S, device="cuda")
     slot = (tab_d[:, t // 16].long() * 16 + (t % 16)[None]).reshape(-1)
     pos = t.int().repeat(B)
     sd = torch.from_numpy(seeds.view(np.int64)).cuda()
-    L.wc_write_kv(cache, k, v, slot, pos, sd.repeat_interleave(S))
+    if scheme_name == "store16":
+        kh, vh = _mantissa4_t(k), _mantissa4_t(v)
+        L.wc_write_kv(cache, kh, vh, slot, pos, sd.repeat_interleave(S))
+        L.wc_witness(cache, k, kh, slot)
+        del kh, vh
+    else:
+        L.wc_write_kv(cache, k, v, slot, pos, sd.repeat_interleave(S))
     part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
     risk = torch.full((B, HQ, tab.shape[1]), float("nan"), device="cuda")
     ctx_d = torch.full((B,), S, dtype=torch.int32, device="cuda")
-    L.wc_decode_attn_meter(cache, 0, q, tab_d, ctx_d, sd, part, H.SM, mask, DELTA[0], *DELTA[1:], NSPLIT,
-                           block_logrisk=risk)
+    L.wc_decode_attn_meter(cache, 0, q, tab_d, ctx_d, sd, part, H.SM, mask | (L.WC_METER_V if vcert else 0),
+                           DELTA[0], *DELTA[1:], NSPLIT, block_logrisk=risk)
     o = torch.empty((B, HQ, 128), device="cuda")
     lse = torch.empty((B, HQ), device="cuda")
-    ra = torch.empty((B, HQ), device="cuda")
-    rb = torch.empty((B, HQ), device="cuda")
-    L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb)
+    ra, rb, ta, tb, ev = (torch.empty((B, HQ), device="cuda") for _ in range(5))
+    L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb, ta, tb, ev)
     torch.cuda.synchronize()
     out = dict(o=o.cpu().numpy(), lse=lse.cpu().numpy(), R_A=ra.cpu().numpy(), R_B=rb.cpu().numpy(),
-               logrisk=risk.cpu().numpy())
+               T_A=ta.cpu().numpy(), T_B=tb.cpu().numpy(), E_V=ev.cpu().numpy(), logrisk=risk.cpu().numpy())
     return L, cache, k, v, q, tab, seeds, out
 
 
-@pytest.mark.parametrize("scheme", ["int8", "fp8"])
+@pytest.mark.parametrize("scheme", ["int8", "fp8", "int8-bypass8", "rtn", "store16", "int8-vcert"])
 def test_decode_bench_size_sampled_against_oracle(scheme):
     _flush(f"full-size decode {scheme}: B={B} S={S} splits={NSPLIT}")
     L, cache, k, v, q, tab, seeds, out = _decode_full(scheme)
     P = S // 16
+    dither = scheme.startswith("int8")
+    O = None
+    if scheme == "int8-bypass8":                     # the selection, bit-exact, from the oracle's energies
+        calib = k[:4096].float().cpu().numpy()
+        O = np.stack([outlier.top_energy_channels(calib[:, g], 8) for g in range(HKV)])
+        assert np.array_equal(cache.outlier_ch[0].cpu().numpy(), O)
     # every head: finite outputs, nonnegative meters, and the block risks sum
     # to the gate tier's E (R = E (1 + E/2)) -- properties of any size
     assert np.all(np.isfinite(out["o"])) and np.all(np.isfinite(out["lse"]))
     assert np.all(out["R_A"] >= 0)
-    r_gate = out["R_B"] if scheme == "int8" else out["R_A"]
+    r_gate = out["R_B"] if dither else out["R_A"]
     e_gate = np.sqrt(1.0 + 2.0 * r_gate.astype(np.float64)) - 1.0
     rho_sum = np.exp(out["logrisk"][:, :, :P].astype(np.float64) - out["lse"][:, :, None]).sum(-1)
     assert np.all(np.abs(rho_sum - e_gate) <= 1e-4 * e_gate + 1e-30)
@@ -109,29 +134,51 @@ def test_decode_bench_size_sampled_against_oracle(scheme):
         k32 = k[b * S:(b + 1) * S, g].float().cpu().numpy()
         v32 = v[b * S:(b + 1) * S, g].float().cpu().numpy()
         qg = q[b, g * G:(g + 1) * G].float().cpu().numpy().astype(np.float64)
-        gk, gv = _codes_of(cache, 0, tab[b, :P], g)
         wt = _rows_of(cache.witness, 0, tab[b, :P], g)
-        if scheme == "int8":
-            oc = H.oracle_int8_cache(k32, v32, int(seeds[b]), 0, g, S)
-            gk = (gk.astype(np.int16) - 128).astype(np.int8)
-            gv = (gv.astype(np.int16) - 128).astype(np.int8)
-            assert np.array_equal(_rows_of(cache.k_scale, 0, tab[b, :P], g), oc["sk"])
-            assert np.array_equal(_rows_of(cache.v_scale, 0, tab[b, :P], g), oc["sv"])
+        if dither:
+            oc = H.oracle_int8_cache(k32, v32, int(seeds[b]), 0, g, S, bypass=None if O is None else O[g])
             r = meter.decode_group(qg, k32, oc["khat"], v32, oc["vhat"], oc["w"], H.SM, k_scale=oc["sk"],
-                                   log_term=lt)
+                                   log_term=lt, bypass=None if O is None else O[g])
+        elif scheme == "rtn":
+            oc = H.oracle_rtn_cache(k32, v32)
+            r = meter.decode_group(qg, k32, oc["khat"], v32, oc["vhat"], oc["w"], H.SM)
+        elif scheme == "store16":
+            kh = _mantissa4_t(k[b * S:(b + 1) * S, g]).float().cpu().numpy()
+            vh = _mantissa4_t(v[b * S:(b + 1) * S, g]).float().cpu().numpy()
+            oc = dict(khat=kh, vhat=vh, w=quant.witness(k32, kh))
+            r = meter.decode_group(qg, k32, kh, v32, vh, oc["w"], H.SM)
         else:
             oc = H.oracle_fp8_cache(k32, v32)
             r = meter.decode_group(qg, k32, oc["khat"], v32, oc["vhat"], oc["w"], H.SM)
-        assert np.array_equal(gk.view(oc["ck"].dtype), oc["ck"]), (b, g)
-        assert np.array_equal(gv.view(oc["cv"].dtype), oc["cv"]), (b, g)
+        if scheme != "store16":
+            gk, gv = _codes_of(cache, 0, tab[b, :P], g)
+            if scheme != "fp8":                          # offset binary in HBM
+                gk = (gk.astype(np.int16) - 128).astype(np.int8)
+                gv = (gv.astype(np.int16) - 128).astype(np.int8)
+                assert np.array_equal(_rows_of(cache.k_scale, 0, tab[b, :P], g), oc["sk"])
+                assert np.array_equal(_rows_of(cache.v_scale, 0, tab[b, :P], g), oc["sv"])
+            assert np.array_equal(gk.view(oc["ck"].dtype), oc["ck"]), (b, g)
+            assert np.array_equal(gv.view(oc["cv"].dtype), oc["cv"]), (b, g)
+        if O is not None:
+            side = _rows_of(cache.k_outlier, 0, tab[b, :P], g).view(np.uint16)
+            assert np.array_equal(inputs.bf16_bits_to_f32(side), oc["side"]), (b, g)
         assert np.all(np.abs(wt - oc["w"]) <= MET_TOL * oc["w"] + 1e-30) and np.all(wt >= oc["w"])
         hs = slice(g * G, (g + 1) * G)
         assert np.all(H.rel_l2(out["o"][b, hs], r["o_tilde"]) <= OUT_TOL), (b, g)
         assert np.all(np.abs(out["lse"][b, hs] - r["lse"]) <= 1e-4 * np.maximum(1, np.abs(r["lse"])))
         assert np.all(np.abs(out["R_A"][b, hs] - r["R_A"]) <= MET_TOL * r["R_A"]), (b, g)
         assert np.all(out["R_A"][b, hs] >= r["tv_true"])
-        if scheme == "int8":
+        assert np.all(np.abs(out["T_A"][b, hs] - r["T_A"]) <= MET_TOL * r["T_A"] + 1e-7), (b, g)
+        assert np.all(out["T_A"][b, hs] >= r["tv_true"] * (1 - 1e-6))
+        if dither:
             assert np.all(np.abs(out["R_B"][b, hs] - r["R_B"]) <= MET_TOL * r["R_B"]), (b, g)
+            assert np.all(np.abs(out["T_B"][b, hs] - r["T_B"]) <= MET_TOL * r["T_B"] + 1e-7), (b, g)
+        if scheme == "int8-vcert":
+            wv = _rows_of(cache.v_witness, 0, tab[b, :P], g)
+            want = quant.witness_v(v32, oc["vhat"])
+            assert np.all(np.abs(wv - want) <= MET_TOL * want + 1e-30) and np.all(wv >= want)
+            assert np.all(np.abs(out["E_V"][b, hs] - r["E_V"]) <= MET_TOL * r["E_V"]), (b, g)
+            assert np.all(out["E_V"][b, hs] >= r["dv_true"])
         rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
         assert np.all(np.abs(rho - r["block_risk"]) <= 2e-4 * r["block_risk"] + 1e-30), (b, g)
     del cache, k, v
