@@ -666,13 +666,15 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     f4 Dc = zero4, Dh = zero4, Dl = zero4;
     float st[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
-    const uint32_t base = key + (uint32_t)(64 * (tok0 + n) + 16 * kq);
+    // LCG state of the lane's first counter, key + 64 token + 16 k; the
+    // other 15 counters are consecutive (their states differ by constants)
+    const uint32_t st0 = (key + (uint32_t)(64 * (tok0 + n) + 16 * kq)) * kPcgMul + kPcgInc;
     // draws of token n, channels 32k + 8j .. +7, as fp16 pairs 1024 + high byte
     // (= 1152 + h) and 1024 + low byte; published to LDS for the values
     auto draws = [&](int j, uint32_t (&hh)[4], uint32_t (&ll)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t wd = pcg(base + (uint32_t)(4 * j + e));
+        const uint32_t wd = pcg_out(st0 + (uint32_t)(4 * j + e) * kPcgMul);
         hh[e] = perm(kMagic, wd, 0x04030401u);
         ll[e] = perm(kMagic, wd, 0x04020400u);
       }

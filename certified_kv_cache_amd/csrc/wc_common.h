@@ -15,11 +15,15 @@ int check_launch(const char* what);
 // ---------------------------------------------------------------- dither
 // pcg hash of Jarzynski and Olano, "Hash Functions for GPU Rendering",
 // JCGT 9(3), 2020: one LCG step followed by the RXS-M-XS output permutation.
-__host__ __device__ __forceinline__ uint32_t pcg(uint32_t v) {
-  uint32_t state = v * 747796405u + 2891336453u;
+constexpr uint32_t kPcgMul = 747796405u, kPcgInc = 2891336453u;
+// the output permutation of one LCG state
+__host__ __device__ __forceinline__ uint32_t pcg_out(uint32_t state) {
   uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
   return (word >> 22u) ^ word;
 }
+__host__ __device__ __forceinline__ uint32_t pcg(uint32_t v) { return pcg_out(v * kPcgMul + kPcgInc); }
+// The LCG step is linear: the state of counter v + i is the state of v plus
+// i * kPcgMul, so runs of consecutive counters need one multiply in all.
 
 // 32-bit key of the dither of one (sequence, layer, KV head), chained from
 // the 64-bit sequence seed, the layer and the KV head.
