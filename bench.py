@@ -287,7 +287,8 @@ def cpu_baseline(w, B, S, budget_s=12.0):
 def prefill_write(iters, seed=4, NL=28, NT=4096):
     """Write path at prefill scale: 28 layers x 4 KV heads x 4096 tokens, bf16
     K/V with per-(layer, head, channel) variance log-uniform in [0.1, 10]; one
-    wc_write_kv call per scheme writes all layers."""
+    call per scheme writes all layers, per token (wc_write_kv) and in whole
+    pages (wc_write_kv_pages, suffix _pages)."""
     import numpy as np
     import torch
 
@@ -313,19 +314,26 @@ def prefill_write(iters, seed=4, NL=28, NT=4096):
             written = n_tok_heads * (2 * D + 32)
         else:                                   # 2-bit codes (2 x d/4 B per token-head), group params, witness
             written = n_tok_heads * (2 * D // 4 + 32) + NL * HKV * (NT // 32) * (D * 2 * 4 + 32 * 4 * 2 * 4)
-        L.wc_write_kv(cache, k, v, slot, pos, sd)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(iters):
-            L.wc_write_kv(cache, k, v, slot, pos, sd)
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / iters * 1e3
-        tot = in_bytes + written
-        out["schemes"][name] = {"us": round(us, 2), "bytes_written": written, "bytes_total": tot,
-                                "written_GBps": round(written / (us * 1e-6) / 1e9, 1),
-                                "total_GBps": round(tot / (us * 1e-6) / 1e9, 1),
-                                "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
+        calls = [("", lambda: L.wc_write_kv(cache, k, v, slot, pos, sd))]
+        if sch != L.WC_KIVI2:                   # whole pages: one workgroup per page-head block
+            pg = torch.from_numpy(tab[0, :NT // 16].astype(np.int32)).cuda()
+            p0 = torch.arange(0, NT, 16, dtype=torch.int32, device="cuda")
+            psd = torch.full((NT // 16,), 777, dtype=torch.int64, device="cuda")
+            calls.append(("_pages", lambda: L.wc_write_kv_pages(cache, k, v, pg, p0, psd)))
+        for suffix, call in calls:
+            call()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / iters * 1e3
+            tot = in_bytes + written
+            out["schemes"][name + suffix] = {"us": round(us, 2), "bytes_written": written, "bytes_total": tot,
+                                             "written_GBps": round(written / (us * 1e-6) / 1e9, 1),
+                                             "total_GBps": round(tot / (us * 1e-6) / 1e9, 1),
+                                             "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
         del cache
     return out
 

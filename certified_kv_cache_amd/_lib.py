@@ -55,6 +55,7 @@ def _load():
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
         "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
         "wc_witness": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, ctypes.c_int, P],
+        "wc_write_kv_pages": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, P, P, P],
         "wc_gate_pagein_tanh": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_double,
                                 _i64, P, P, P, P, P, ctypes.c_size_t, P],
     }
@@ -75,7 +76,7 @@ lib = _load()
 
 EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
            "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select",
-           "wc_witness", "wc_last_error", "wc_version"]
+           "wc_witness", "wc_write_kv_pages", "wc_last_error", "wc_version"]
 
 
 def _check(fn, code):
@@ -181,6 +182,19 @@ def wc_write_kv(cache, k, v, slot, pos, seed, layer0=0, stream=None):
     _check("wc_write_kv", lib.wc_write_kv(cache.ref(), layer0, n_layers, _ptr(k), _ptr(v), _dtype_code(k), n_tok,
                                           n_tok * k.shape[2] * k.shape[3], _ptr(slot), _ptr(pos), _ptr(seed),
                                           _stream(stream)))
+
+
+def wc_write_kv_pages(cache, k, v, pages, pos0, seed, layer0=0, stream=None):
+    """k, v: [n_layers, 16 * n_pages, Hkv, 128] or [16 * n_pages, Hkv, 128]; pages, pos0 int32 [n_pages],
+    seed int64 [n_pages]."""
+    if k.dim() == 3:
+        k, v = k[None], v[None]
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+    n_layers, n_tok = k.shape[0], k.shape[1]
+    assert n_tok % 16 == 0 and pages.numel() == n_tok // 16
+    _check("wc_write_kv_pages", lib.wc_write_kv_pages(cache.ref(), layer0, n_layers, _ptr(k), _ptr(v), _dtype_code(k),
+                                                      n_tok // 16, n_tok * k.shape[2] * k.shape[3], _ptr(pages),
+                                                      _ptr(pos0), _ptr(seed), _stream(stream)))
 
 
 def wc_witness(cache, x, xhat, slot, layer0=0, values=False, stream=None):

@@ -109,46 +109,21 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
   }
 }
 
-// OUTL: dithered INT8 keys with the outlier bypass (bf16 input): the
-// channels of outlier_ch are excluded from the key absmax, coded 0 with a
-// zero residual, and their exact bf16 keys go to k_outlier.
-template <typename T, int SCHEME, bool OUTL>
-__global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
-                                                         const T* __restrict__ vin, RowArgs a) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
-  const bool live = row < rows;
-  const int64_t rr = live ? row : 0;
-  const int g = (int)(rr % a.hkv);
-  const int64_t i = (rr / a.hkv) % a.n_tok;
-  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
-  const int layer = a.layer0 + l;
-  const int64_t slot = a.slot[i];
-  const int64_t page = slot / 16, off = slot % 16;
-  const int32_t p = a.pos[i];
-  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
-  const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
+// One (token, KV head) row, both tensors, on 16 lanes of 8 channels: codes
+// (packed little-endian, INT8 as offset binary), row scales, the key's band
+// witness (lanes 0..7 hold bands 0..7) and the value witness.
+struct RowQ {
+  uint32_t kp[2], vp[2];
+  float ks, vs, w, wv;
+};
 
-  // bypassed channels among the lane's 8 (bit i = channel 8 lane16 + i); the
-  // row's lane16 < m also copies entry lane16 of the side store
-  uint32_t omask = 0;
-  int ochan = -1;
-  if (OUTL) {
-    const int m = c.num_outliers;
-    const int32_t* oc = c.outlier_ch + ((int64_t)layer * a.hkv + g) * m;
-    for (int e = 0; e < m; ++e) {
-      const int ch = oc[e];
-      omask |= (ch >> 3) == lane16 ? 1u << (ch & 7) : 0u;
-    }
-    if (lane16 < m) ochan = oc[lane16] & 127;    // (in range even for a corrupt list)
-  }
-  uint32_t words[4] = {0u, 0u, 0u, 0u};
-  if (SCHEME == WC_DITHER_INT8) {
-    const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
-  }
+// OUTL: dithered INT8 keys with the outlier bypass (bf16 input): the
+// channels in omask are excluded from the key absmax, coded 0 with a zero
+// residual (their exact keys go to the side store, written by the caller).
+template <typename T, int SCHEME>
+__device__ __forceinline__ RowQ quant_row(const T* kin, const T* vin, int64_t in_off, const uint32_t (&words)[4],
+                                          uint32_t omask) {
+  RowQ o;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const bool isv = which == 1;
@@ -168,41 +143,148 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
     uint32_t packed[2];
     float r[8];
     quant8<SCHEME>(x, s, inv, words, ex, packed, r);
-    if (!isv) {
-      float ss = 0.0f;
+    float ss = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
+    for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
+    if (!isv) {
       const float tot = ss + shfl_xor(ss, 8);
-      const float w = sqrtf(tot) * kWitnessGuard;
-      if (live) {
-        // channels 8 lane16 .. +7 of token off: half (lane16 % 4) / 2, 32-channel
-        // group lane16 / 4, bytes 8 (lane16 % 2) .. of the token's 16-byte chunk
-        uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 2048 + ((lane16 & 3) >> 1) * 1024 +
-                      (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
-        *reinterpret_cast<uint2*>(kc) = make_uint2(packed[0], packed[1]);
-        if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = w;
-        if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && lane16 == 0) c.k_scale[pg * 16 + off] = s;
-        if (OUTL && ochan >= 0)
-          c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] =
-              reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
-      }
+      o.w = sqrtf(tot) * kWitnessGuard;
+      o.kp[0] = packed[0];
+      o.kp[1] = packed[1];
+      o.ks = s;
     } else {
       // value witness ||v^ - v|| over the row's 128 channels (16-lane sum)
-      float ss = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) ss += shfl_xor(ss, m);
-      if (!live) continue;
-      if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = sqrtf(ss) * kWitnessGuard;
-      // channel 8 lane16 + k of token off: half k / 4, token group off / 4,
-      // channel group lane16, word k % 4, byte off % 4
-      uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) vc[(k >> 2) * 1024 + (k & 3) * 4] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
-      if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && lane16 == 0) c.v_scale[pg * 16 + off] = s;
+      o.wv = sqrtf(ss) * kWitnessGuard;
+      o.vp[0] = packed[0];
+      o.vp[1] = packed[1];
+      o.vs = s;
     }
   }
+  return o;
+}
+
+// Bypassed channels among lane16's 8 (bit i = channel 8 lane16 + i), and the
+// channel whose exact key lane16 copies into the side store (-1: none).
+__device__ __forceinline__ void bypass_lanes(const wc_cache& c, int layer, int hkv, int g, int lane16,
+                                             uint32_t& omask, int& ochan) {
+  const int m = c.num_outliers;
+  const int32_t* oc = c.outlier_ch + ((int64_t)layer * hkv + g) * m;
+  omask = 0;
+  for (int e = 0; e < m; ++e) {
+    const int ch = oc[e];
+    omask |= (ch >> 3) == lane16 ? 1u << (ch & 7) : 0u;
+  }
+  ochan = lane16 < m ? (oc[lane16] & 127) : -1;   // (in range even for a corrupt list)
+}
+
+template <typename T, int SCHEME, bool OUTL>
+__global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
+                                                         const T* __restrict__ vin, RowArgs a) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
+  const bool live = row < rows;
+  const int64_t rr = live ? row : 0;
+  const int g = (int)(rr % a.hkv);
+  const int64_t i = (rr / a.hkv) % a.n_tok;
+  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
+  const int layer = a.layer0 + l;
+  const int64_t slot = a.slot[i];
+  const int64_t page = slot / 16, off = slot % 16;
+  const int32_t p = a.pos[i];
+  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
+  const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
+
+  uint32_t omask = 0;
+  int ochan = -1;
+  if (OUTL) bypass_lanes(c, layer, a.hkv, g, lane16, omask, ochan);
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  if (SCHEME == WC_DITHER_INT8) {
+    const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
+  }
+  const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
+  if (!live) return;
+  constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
+  // keys: channels 8 lane16 .. +7 of token off: half (lane16 % 4) / 2, 32-channel
+  // group lane16 / 4, bytes 8 (lane16 % 2) .. of the token's 16-byte chunk
+  uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 2048 + ((lane16 & 3) >> 1) * 1024 +
+                (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
+  *reinterpret_cast<uint2*>(kc) = make_uint2(o.kp[0], o.kp[1]);
+  if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = o.w;
+  if (SC && lane16 == 0) c.k_scale[pg * 16 + off] = o.ks;
+  if (OUTL && ochan >= 0)
+    c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] = reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
+  // values: channel 8 lane16 + k of token off: half k / 4, token group off / 4,
+  // channel group lane16, word k % 4, byte off % 4
+  if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = o.wv;
+  uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vc[(k >> 2) * 1024 + (k & 3) * 4] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+  if (SC && lane16 == 0) c.v_scale[pg * 16 + off] = o.vs;
+}
+
+// Whole pages (prefill): one workgroup per (layer, page, KV head) block, row
+// = token j of the page.  The same arithmetic as write_rows_kernel; the code
+// blocks are assembled in LDS and leave as 2 KB of 16-byte stores each.
+struct PageArgs {
+  int64_t n_pages;
+  int64_t layer_stride;
+  int64_t num_pages;
+  int hkv;
+  int layer0;
+  const int32_t* pages;
+  const int32_t* pos0;
+  const uint64_t* seed;
+};
+
+template <typename T, int SCHEME, bool OUTL>
+__global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* __restrict__ kin,
+                                                          const T* __restrict__ vin, PageArgs a) {
+  __shared__ __align__(16) uint8_t sK[2048];
+  __shared__ __align__(16) uint8_t sV[2048];
+  const int lane16 = threadIdx.x & 15, j = threadIdx.x >> 4;
+  const int64_t blk = blockIdx.x;
+  const int g = (int)(blk % a.hkv);
+  const int64_t pi = (blk / a.hkv) % a.n_pages;
+  const int l = (int)(blk / ((int64_t)a.hkv * a.n_pages));
+  const int layer = a.layer0 + l;
+  const int64_t i = pi * 16 + j;                  // input token
+  const int32_t p = a.pos0[pi] + j;
+  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
+  const int64_t pg = ((int64_t)layer * a.num_pages + a.pages[pi]) * a.hkv + g;
+
+  uint32_t omask = 0;
+  int ochan = -1;
+  if (OUTL) bypass_lanes(c, layer, a.hkv, g, lane16, omask, ochan);
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  if (SCHEME == WC_DITHER_INT8) {
+    const uint32_t key = stream_key(a.seed[pi], (uint32_t)layer, (uint32_t)g);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
+  }
+  const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
+  constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
+  *reinterpret_cast<uint2*>(sK + ((lane16 & 3) >> 1) * 1024 + (lane16 >> 2) * 256 + j * 16 + 8 * (lane16 & 1)) =
+      make_uint2(o.kp[0], o.kp[1]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    sV[(k >> 2) * 1024 + (j >> 2) * 256 + lane16 * 16 + (k & 3) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+  if (lane16 < 8) c.witness[(pg * 16 + j) * 8 + lane16] = o.w;
+  if (SC && lane16 == 0) {
+    c.k_scale[pg * 16 + j] = o.ks;
+    c.v_scale[pg * 16 + j] = o.vs;
+  }
+  if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + j] = o.wv;
+  if (OUTL && ochan >= 0)
+    c.k_outlier[(pg * 16 + j) * c.num_outliers + lane16] = reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
+  __syncthreads();
+  const int t = threadIdx.x & 127;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(threadIdx.x < 128 ? c.k_codes : c.v_codes) + pg * 2048 + 16 * t;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((threadIdx.x < 128 ? sK : sV) + 16 * t);
 }
 
 // 16-bit store: the scheme's outputs (bf16) copied into the decode layouts,
@@ -578,6 +660,75 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
   }
   set_error("wc_write_kv: unknown scheme %d", c.scheme);
   return WC_EUNSUPPORTED;
+}
+
+extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
+                                 int in_dtype, int64_t n_pages, int64_t layer_stride, const int32_t* pages,
+                                 const int32_t* pos0, const uint64_t* seed, void* stream) {
+  if (!cache || !k || !v || !pages || !pos0 || !seed) {
+    set_error("wc_write_kv_pages: null pointer");
+    return WC_EINVAL;
+  }
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.num_bands != 8 || c.num_kv_heads < 1 || c.num_layers < 1 || c.num_pages < 1 ||
+      c.page_size != 16) {
+    set_error("wc_write_kv_pages: need head_dim 128, 8 bands, 16-token pages");
+    return WC_EUNSUPPORTED;
+  }
+  if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3 && c.scheme != WC_RTN_INT8) {
+    set_error("wc_write_kv_pages: scheme %d writes through wc_write_kv", c.scheme);
+    return WC_EUNSUPPORTED;
+  }
+  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_pages < 0 ||
+      n_pages * 16 > (int64_t(1) << 26)) {
+    set_error("wc_write_kv_pages: layer range or page count out of range");
+    return WC_EINVAL;
+  }
+  if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
+    set_error("wc_write_kv_pages: in_dtype must be WC_F32 or WC_BF16");
+    return WC_EUNSUPPORTED;
+  }
+  if (n_layers > 1 && layer_stride < n_pages * 16 * c.num_kv_heads * 128) {
+    set_error("wc_write_kv_pages: layer_stride smaller than one layer");
+    return WC_EINVAL;
+  }
+  if (!c.k_codes || !c.v_codes || !c.witness ||
+      ((c.scheme == WC_DITHER_INT8 || c.scheme == WC_RTN_INT8) && (!c.k_scale || !c.v_scale))) {
+    set_error("wc_write_kv_pages: cache codes, scales and witness must be set");
+    return WC_EINVAL;
+  }
+  if (c.num_outliers != 0) {
+    if (c.scheme != WC_DITHER_INT8 || (c.num_outliers != 8 && c.num_outliers != 16)) {
+      set_error("wc_write_kv_pages: the outlier bypass needs the dithered INT8 scheme and m = 8 or 16");
+      return WC_EUNSUPPORTED;
+    }
+    if (in_dtype != WC_BF16) {
+      set_error("wc_write_kv_pages: the outlier bypass stores bf16 keys: input must be WC_BF16");
+      return WC_EUNSUPPORTED;
+    }
+    if (!c.outlier_ch || !c.k_outlier) {
+      set_error("wc_write_kv_pages: outlier bypass needs outlier_ch and k_outlier");
+      return WC_EINVAL;
+    }
+  }
+  if (n_pages == 0) return WC_OK;
+  PageArgs a{n_pages, layer_stride, c.num_pages, c.num_kv_heads, layer0, pages, pos0, seed};
+  dim3 grid((unsigned)((int64_t)n_layers * n_pages * c.num_kv_heads));
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = in_dtype == WC_BF16;
+#define WC_PAGES(T, SCH, OU) hipLaunchKernelGGL((write_pages_kernel<T, SCH, OU>), grid, dim3(256), 0, st, c, \
+                                                (const T*)k, (const T*)v, a)
+  if (c.scheme == WC_DITHER_INT8) {
+    if (c.num_outliers != 0) WC_PAGES(uint16_t, WC_DITHER_INT8, true);
+    else if (bf) WC_PAGES(uint16_t, WC_DITHER_INT8, false);
+    else WC_PAGES(float, WC_DITHER_INT8, false);
+  } else if (c.scheme == WC_RTN_INT8) {
+    if (bf) WC_PAGES(uint16_t, WC_RTN_INT8, false); else WC_PAGES(float, WC_RTN_INT8, false);
+  } else {
+    if (bf) WC_PAGES(uint16_t, WC_FP8_E4M3, false); else WC_PAGES(float, WC_FP8_E4M3, false);
+  }
+#undef WC_PAGES
+  return check_launch("wc_write_kv_pages");
 }
 
 extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat,

@@ -175,6 +175,24 @@ int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, 
                 const int32_t* pos, const uint64_t* seed, void* stream);
 
 /*
+ * wc_write_kv_pages -- wc_write_kv for whole 16-token pages (the prefill).
+ *
+ * The same arithmetic and outputs as wc_write_kv (dithered INT8, fp8, RTN
+ * INT8; the outlier bypass and the value witness as there), for tokens that
+ * fill whole pages: input token 16 i + j goes to page pages[i], offset j, at
+ * position pos0[i] + j with the dither seed seed[i].  One workgroup writes a
+ * whole page-head block, so every code block leaves as full-line stores.
+ *
+ *  k, v     device, in_dtype, [n_layers][16 n_pages][Hkv][128]; layer l at
+ *           l * layer_stride elements.
+ *  pages, pos0  device int32 [n_pages];  seed  device uint64 [n_pages].
+ * Other schemes return WC_EUNSUPPORTED (write them with wc_write_kv).
+ */
+int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
+                      int in_dtype, int64_t n_pages, int64_t layer_stride, const int32_t* pages,
+                      const int32_t* pos0, const uint64_t* seed, void* stream);
+
+/*
  * wc_witness -- the black-box hook: store the witness of any scheme.
  *
  * The summary's implementation paragraph and the abstract register any

@@ -192,3 +192,20 @@ def test_blackbox_schemes_reject_bad_arguments():
     assert call(_cache(L, scheme=L.WC_RTN_INT8, v_scale=None)) == L.WC_EINVAL
     assert call(_cache(L, scheme=L.WC_RTN_INT8, num_outliers=8, outlier_ch=16, k_outlier=16)) == L.WC_EUNSUPPORTED
     assert call(_cache(L), mask=1 | L.WC_METER_V) == L.WC_EINVAL              # no value witness array
+
+
+def test_write_pages_rejects_bad_arguments():
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    f = L.lib.wc_write_kv_pages
+    ok = ctypes.byref(_cache(L))
+    assert f(None, 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
+    assert f(ok, 0, 1, p, p, 1, 4, 0, None, p, p, None) == L.WC_EINVAL
+    assert f(ok, 1, 2, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL              # layer range
+    assert f(ok, 0, 1, p, p, 5, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED        # dtype
+    assert f(ok, 0, 2, p, p, 1, 4, 10, p, p, p, None) == L.WC_EINVAL             # layer stride
+    assert f(ctypes.byref(_cache(L, scheme=L.WC_KIVI2, page_size=32)), 0, 1, p, p, 1, 4, 0, p, p, p,
+             None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, k_scale=None)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
+    assert f(ok, 0, 1, p, p, 1, 0, 0, p, p, p, None) == L.WC_OK                  # nothing to do
