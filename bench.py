@@ -106,7 +106,7 @@ def fp8_variant(w, B, S, iters):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = time_decode(decode, iters, mask=1, with_risk=True)
+    t_risk = time_decode(decode, iters, warm=100, mask=1, with_risk=True)
     t_on = time_decode(decode, iters, mask=1, with_risk=False)
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
     nb = decode_bytes(B, S, True, scales=False)
@@ -135,7 +135,7 @@ def scheme_variant(w, B, S, iters, scheme):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = min(time_decode(decode, iters, mask=1, with_risk=True), time_decode(decode, iters, mask=1, with_risk=True))
+    t_risk = min(time_decode(decode, iters, warm=100, mask=1, with_risk=True), time_decode(decode, iters, mask=1, with_risk=True))
     t_on = time_decode(decode, iters, mask=1, with_risk=False)
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
     if scheme == "store16":
@@ -164,13 +164,49 @@ def vcert_variant(w, B, S, iters):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_v = min(time_decode(decode, iters, mask=3 | L.WC_METER_V), time_decode(decode, iters, mask=3 | L.WC_METER_V))
+    t_v = min(time_decode(decode, iters, warm=100, mask=3 | L.WC_METER_V), time_decode(decode, iters, mask=3 | L.WC_METER_V))
     t_kv = min(time_decode(decode, iters, mask=3), time_decode(decode, iters, mask=3))
     nb = decode_bytes(B, S, True) + B * S * HKV * 4
     del cache
     return {"decode_us": round(t_v, 2), "decode_without_v_us": round(t_kv, 2),
             "v_overhead": round(t_v / t_kv - 1, 4), "decode_bytes": nb,
             "achieved_GBps": round(nb / (t_v * 1e-6) / 1e9, 1), "frac": round(nb / (t_v * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
+def needle_variant(w, B, S, iters, outs):
+    """The structured stand-in for concentrated attention: the same workload
+    with a sink key at position 0 (+8 on the mean query's logit) and 4 seeded
+    needle keys (+6) per (sequence, KV head).  Decode time, and the meters of
+    both workloads side by side (median over heads)."""
+    import numpy as np
+    import torch
+    from certified_kv_cache_amd import inputs
+    L = w["L"]
+    kn = inputs.plant_needles_torch(w["k"], w["q"], B, S, Hkv=HKV, seed=3)
+    cache = L.KVCache(L.WC_DITHER_INT8, 1, w["npages"], HKV)
+    L.wc_write_kv(cache, kn, w["v"], w["slot"], w["pos"], w["seed"].repeat_interleave(S))
+    del kn
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    sm = 1.0 / math.sqrt(D)
+
+    def decode(mask=3, with_risk=True):
+        L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
+                               *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
+
+    t = min(time_decode(decode, iters, warm=100), time_decode(decode, iters))
+    decode()
+    o = torch.empty((B, HQ, D), device="cuda")
+    lse = torch.empty((B, HQ), device="cuda")
+    ra, rb, ta = (torch.empty((B, HQ), device="cuda") for _ in range(3))
+    L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb, ta)
+    torch.cuda.synchronize()
+    med = lambda x: float(np.median(x.cpu().numpy()))
+    res = {"decode_us": round(t, 2), "R_A_median": med(ra), "R_B_median": med(rb), "tanh_A_median": med(ta),
+           "uniform_R_A_median": med(outs["ra"]), "uniform_R_B_median": med(outs["rb"])}
+    del cache
+    return res
 
 
 def outlier_variant(w, B, S, iters, m):
@@ -191,7 +227,7 @@ def outlier_variant(w, B, S, iters, m):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = min(time_decode(decode, iters, mask=3, with_risk=True), time_decode(decode, iters, mask=3, with_risk=True))
+    t_risk = min(time_decode(decode, iters, warm=100, mask=3, with_risk=True), time_decode(decode, iters, mask=3, with_risk=True))
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
     nb = decode_bytes(B, S, True) + B * S * HKV * 2 * m
     del cache
@@ -228,12 +264,14 @@ def make_step(w, B, S):
     return step, decode, dict(o=o, lse=lse, ra=ra, rb=rb, paged=paged)
 
 
-def time_decode(decode, iters, **kw):
+def time_decode(decode, iters, warm=1, **kw):
     """Mean duration (us) of one decode launch: `iters` back-to-back launches
-    between one pair of HIP events on the launch stream."""
+    between one pair of HIP events on the launch stream, after `warm` untimed
+    launches."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    decode(**kw)
+    for _ in range(warm):
+        decode(**kw)
     a.record()
     for _ in range(iters):
         decode(**kw)
@@ -279,7 +317,10 @@ def cpu_baseline(w, B, S, budget_s=12.0):
             if total >= budget_s:
                 break
     sample_bytes = done * decode_bytes(B, S, True) / (B * HKV)
+    from threadpoolctl import threadpool_info
+    blas = sorted({i.get("internal_api", "?") + ":" + str(i.get("num_threads")) for i in threadpool_info()})
     return dict(value=round(sample_bytes / total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                host_cores=len(os.sched_getaffinity(0)), blas_threads_default=blas,
                 sample=f"{done} of {B * HKV} (sequence, KV head) pairs, all {S} tokens each, "
                        f"{total:.1f} s single-threaded float64 numpy")
 
@@ -453,6 +494,55 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
     return res
 
 
+def latency(iters=200):
+    """Decode + merge latency of the two parity-size workloads: one head with
+    256 fp32 tokens (dithered INT8, Tier A+B), and one layer of 28 q / 4 KV
+    heads with 4096 bf16 tokens (x20 outlier channels), 4 splits."""
+    import numpy as np
+    import torch
+
+    from certified_kv_cache_amd import _lib as L
+    from certified_kv_cache_amd import inputs
+    res = {"metric": "decode + merge latency at the parity sizes", "unit": "us", "data": "synthetic", "configs": {}}
+    for name, d, hkv, n_split, delta in (("tiny S=256 1q/1kv fp32", inputs.tiny(seed=1), 1, 1, (1e-2, 1, 1, 1)),
+                                         ("layer S=4096 28q/4kv bf16", inputs.layer(seed=2), 4, 4, DELTA)):
+        dt = torch.float32 if d["dtype"] == "f32" else torch.bfloat16
+        conv = (lambda a: torch.from_numpy(a).cuda()) if dt == torch.float32 else \
+            (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16))
+        k, v, q = conv(d["k"]), conv(d["v"]), conv(d["q"])
+        S = k.shape[0]
+        tab, npages = inputs.page_table(1, [S])
+        cache = L.KVCache(L.WC_DITHER_INT8, 1, npages, hkv)
+        t = np.arange(S)
+        slot = torch.from_numpy(tab[0, t // 16].astype(np.int64) * 16 + t % 16).cuda()
+        L.wc_write_kv(cache, k, v, slot, torch.arange(S, dtype=torch.int32, device="cuda"),
+                      torch.full((S,), 5, dtype=torch.int64, device="cuda"))
+        Hq = q.shape[1]
+        part = torch.empty(L.wc_decode_workspace_bytes(1, Hq, n_split) // 4, device="cuda")
+        o = torch.empty((1, Hq, D), device="cuda")
+        lse, ra, rb = (torch.empty((1, Hq), device="cuda") for _ in range(3))
+        tab_d = torch.from_numpy(tab).cuda()
+        ctx = torch.tensor([S], dtype=torch.int32, device="cuda")
+        sd = torch.tensor([5], dtype=torch.int64, device="cuda")
+
+        def call():
+            L.wc_decode_attn_meter(cache, 0, q, tab_d, ctx, sd, part, 1.0 / math.sqrt(D), 3, delta[0], *delta[1:],
+                                   n_split)
+            L.wc_lse_merge(part, 1, Hq, n_split, o, lse, ra, rb)
+
+        for _ in range(20):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        res["configs"][name] = {"us_per_decode_and_merge": round(a.elapsed_time(b) / iters * 1e3, 2),
+                                "n_split": n_split}
+    return res
+
+
 def decode_bytes_ragged(lens, scales=True):
     """Algorithmic decode bytes of one layer over a ragged batch (meter on)."""
     per_tok = 128 + 128 + (8 if scales else 0) + 32
@@ -470,22 +560,28 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill-write", "gate-flow", "gate-compare"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill-write", "gate-flow", "gate-compare", "latency"],
                     help="decode: the headline line (default); prefill-write: the 28-layer write path per scheme; "
                          "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps; "
-                         "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate")
+                         "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate; "
+                         "latency: decode + merge latency at the two parity sizes")
     ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; the path shards without communication "
               "(see the design notes), so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     if args.workload == "prefill-write":
         print(json.dumps(prefill_write(args.steps)), flush=True)
         return
     if args.workload == "gate-flow":
         print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)))), flush=True)
+        return
+    if args.workload == "latency":
+        print(json.dumps(latency()), flush=True)
         return
     if args.workload == "gate-compare":
         print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)), taus=(0.1, 0.05, 0.02), scheme="int8")),
@@ -503,15 +599,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    # the step's decode (meter on, block risks) timed on its own, then the same
-    # kernel with the meter off for the overhead
+    # the step's decode (meter on, block risks) timed on its own over 10 loops
+    # of back-to-back launches (median and p10-p90 of the loop means), then the
+    # same kernel without block risks and with the meter off for the overhead
     iters = max(args.steps, 10)
-    t_risk = time_decode(decode, iters, mask=3, with_risk=True)
-    t_on = time_decode(decode, iters, mask=3, with_risk=False)
+    loops = sorted(time_decode(decode, iters, mask=3, with_risk=True) for _ in range(10))
+    t_risk = float(np.median(loops))
+    t_on = min(time_decode(decode, iters, mask=3, with_risk=False), time_decode(decode, iters, mask=3, with_risk=False))
     t_off = time_decode(decode, iters, mask=0, with_risk=False)
-    t_risk2 = time_decode(decode, iters, mask=3, with_risk=True)
-    t_on2 = time_decode(decode, iters, mask=3, with_risk=False)
-    t_risk, t_on = min(t_risk, t_risk2), min(t_on, t_on2)
     dec_step_us = t_risk
     bytes_on = decode_bytes(B, S, True)
     ach = bytes_on / (dec_step_us * 1e-6) / 1e9
@@ -521,6 +616,20 @@ def main():
         if cnt.get("source_sha") == decode_source_sha() and cnt.get("batch") == B and cnt.get("ctx") == S:
             traffic = cnt.get("hbm_bytes_per_launch")
     value = step_bytes(B, S) / (ms_step * 1e-3) / 1e9
+    # measured device copy peak (1 GiB read + 1 GiB written per copy)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(10):
+        dst.copy_(src)
+    cb.record()
+    torch.cuda.synchronize()
+    copy_peak = 2 * src.numel() * 4 / (ca.elapsed_time(cb) / 10 * 1e-3) / 1e9
+    del src, dst
+    props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -530,10 +639,16 @@ def main():
                    "batch": B, "ctx": S, "n_split": NSPLIT, "tau": TAU},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_GBS, 4), "traffic": traffic},
-        "decode_us": round(dec_step_us, 2), "decode_meter_on_us": round(t_on, 2),
+        "decode_us": round(dec_step_us, 2), "decode_us_p10": round(loops[1], 2), "decode_us_p90": round(loops[8], 2),
+        "decode_loops": f"10 loops of {iters} back-to-back launches (median; p10, p90 of the loop means)",
+        "decode_meter_on_us": round(t_on, 2),
         "decode_meter_off_us": round(t_off, 2), "meter_overhead": round(t_on / t_off - 1, 4),
         "pct_peak": round(100 * ach / PEAK_GBS, 2),
         "kv_tokens_per_s": round(B * S / (dec_step_us * 1e-6), 1),
+        "decode_steps_per_s_per_layer": round(1e6 / dec_step_us, 1),
+        "copy_peak_GBps": round(copy_peak, 1), "pct_copy_peak": round(100 * ach / copy_peak, 2),
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count},
         "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),
         "pages_paged_in": int(outs["paged"].item()) // 4096,
     }
@@ -542,6 +657,7 @@ def main():
     out["rtn_variant"] = scheme_variant(w, B, S, iters, "rtn")
     out["store16_variant"] = scheme_variant(w, B, S, iters, "store16")
     out["vcert_variant"] = vcert_variant(w, B, S, iters)
+    out["needle_variant"] = needle_variant(w, B, S, iters, outs)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, B, S)
     if args.copy_ref:

@@ -188,3 +188,28 @@ def prefill_kv_torch(seed, layers=28, n_tok=4096, Hkv=4, d=128, device="cuda"):
     k = (torch.randn((layers, n_tok, Hkv, d), generator=gen, device=device) * sd[0]).to(torch.bfloat16)
     v = (torch.randn((layers, n_tok, Hkv, d), generator=gen, device=device) * sd[1]).to(torch.bfloat16)
     return k, v
+
+
+def plant_needles_torch(k, q, batch, S, Hkv=4, sm=1.0 / np.sqrt(128), sink=8.0, needle=6.0, n_needles=4, seed=0):
+    """Structured variant of a decode workload: per (sequence, KV head) the key
+    at position 0 becomes a sink and `n_needles` seeded positions become
+    needles, by adding a multiple of u, the unit vector of the mean of the
+    group's queries, sized so that the mean query's logit rises by `sink`
+    (`needle`).  k: bf16 [batch*S, Hkv, d] (returned modified copy); q: [batch, Hq, d]."""
+    import torch
+    G = q.shape[1] // Hkv
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed) + 31337)
+    out = k.clone()
+    for b in range(batch):
+        pos = torch.randperm(S - 1, generator=gen)[:n_needles] + 1
+        for g in range(Hkv):
+            qm = q[b, g * G:(g + 1) * G].float().mean(0)
+            nrm = float(qm.norm())
+            if nrm == 0.0:
+                continue
+            u = qm / nrm
+            for t, gain in [(0, sink)] + [(int(p), needle) for p in pos]:
+                row = b * S + t
+                out[row, g] = (out[row, g].float() + (gain / (sm * nrm)) * u).to(out.dtype)
+    return out
