@@ -179,17 +179,16 @@ __device__ __forceinline__ void bypass_lanes(const wc_cache& c, int layer, int h
   ochan = lane16 < m ? (oc[lane16] & 127) : -1;   // (in range even for a corrupt list)
 }
 
+// Grid (ceil(n_tok / 16), Hkv, n_layers): 16 consecutive tokens of one KV
+// head per workgroup (no index division).
 template <typename T, int SCHEME, bool OUTL>
 __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
                                                          const T* __restrict__ vin, RowArgs a) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
-  const bool live = row < rows;
-  const int64_t rr = live ? row : 0;
-  const int g = (int)(rr % a.hkv);
-  const int64_t i = (rr / a.hkv) % a.n_tok;
-  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = tok < a.n_tok;
+  const int64_t i = live ? tok : 0;
+  const int g = blockIdx.y, l = blockIdx.z;
   const int layer = a.layer0 + l;
   const int64_t slot = a.slot[i];
   const int64_t page = slot / 16, off = slot % 16;
@@ -247,10 +246,8 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
   __shared__ __align__(16) uint8_t sK[2048];
   __shared__ __align__(16) uint8_t sV[2048];
   const int lane16 = threadIdx.x & 15, j = threadIdx.x >> 4;
-  const int64_t blk = blockIdx.x;
-  const int g = (int)(blk % a.hkv);
-  const int64_t pi = (blk / a.hkv) % a.n_pages;
-  const int l = (int)(blk / ((int64_t)a.hkv * a.n_pages));
+  const int64_t pi = blockIdx.x;                  // grid (n_pages, Hkv, n_layers)
+  const int g = blockIdx.y, l = blockIdx.z;
   const int layer = a.layer0 + l;
   const int64_t i = pi * 16 + j;                  // input token
   const int32_t p = a.pos0[pi] + j;
@@ -293,12 +290,9 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
 __global__ void __launch_bounds__(256) write_bf16_kernel(wc_cache c, const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin, RowArgs a) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
-  if (row >= rows) return;
-  const int g = (int)(row % a.hkv);
-  const int64_t i = (row / a.hkv) % a.n_tok;
-  const int l = (int)(row / ((int64_t)a.hkv * a.n_tok));
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);     // grid as write_rows_kernel
+  if (i >= a.n_tok) return;
+  const int g = blockIdx.y, l = blockIdx.z;
   const int64_t slot = a.slot[i];
   const int64_t page = slot / 16, off = slot % 16;
   const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
@@ -325,13 +319,10 @@ template <typename T, bool VAL>
 __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __restrict__ x, const T* __restrict__ xh,
                                                       RowArgs a) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int64_t rows = (int64_t)a.n_layers * a.n_tok * a.hkv;
-  const bool live = row < rows;
-  const int64_t rr = live ? row : 0;
-  const int g = (int)(rr % a.hkv);
-  const int64_t i = (rr / a.hkv) % a.n_tok;
-  const int l = (int)(rr / ((int64_t)a.hkv * a.n_tok));
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // grid as write_rows_kernel
+  const bool live = tok < a.n_tok;
+  const int64_t i = live ? tok : 0;
+  const int g = blockIdx.y, l = blockIdx.z;
   const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
   float xv[8], hv[8];
   load8<T>(x + in_off, xv);
@@ -383,11 +374,8 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
   __shared__ float xs[32][129];
   __shared__ float red[2][2][128];
   const int t = threadIdx.x;
-  const int64_t ngrp = a.n_tok / 32;
-  const int64_t blk = blockIdx.x;
-  const int g = (int)(blk % a.hkv);
-  const int64_t grp = (blk / a.hkv) % ngrp;
-  const int l = (int)(blk / ((int64_t)a.hkv * ngrp));
+  const int64_t grp = blockIdx.x;                // grid (n_tok / 32, Hkv, n_layers)
+  const int g = blockIdx.y, l = blockIdx.z;
   const int layer = a.layer0 + l;
   const int64_t i0 = grp * 32;
   const int64_t page = a.slot[i0] / 32;
@@ -555,8 +543,9 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
     set_error("wc_write_kv: need head_dim 128, 8 bands, >= 1 KV head, layer and page");
     return WC_EUNSUPPORTED;
   }
-  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_tok < 0) {
-    set_error("wc_write_kv: layer range or token count out of range");
+  if (layer0 < 0 || n_layers < 1 || n_layers > 65535 || layer0 + n_layers > c.num_layers || n_tok < 0 ||
+      c.num_kv_heads > 65535) {
+    set_error("wc_write_kv: layer range, head count or token count out of range");
     return WC_EINVAL;
   }
   if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
@@ -583,9 +572,8 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
       set_error("wc_write_kv: the 16-bit store takes bf16 input and 16-token pages, no outlier bypass");
       return WC_EUNSUPPORTED;
     }
-    const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
-    hipLaunchKernelGGL(write_bf16_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, c,
-                       (const uint16_t*)k, (const uint16_t*)v, a);
+    hipLaunchKernelGGL(write_bf16_kernel, dim3((unsigned)((n_tok + 15) / 16), (unsigned)c.num_kv_heads,
+                       (unsigned)n_layers), dim3(256), 0, st, c, (const uint16_t*)k, (const uint16_t*)v, a);
     return check_launch("wc_write_kv");
   }
   if (c.scheme == WC_DITHER_INT8 || c.scheme == WC_FP8_E4M3 || c.scheme == WC_RTN_INT8) {
@@ -611,8 +599,7 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
         return WC_EINVAL;
       }
     }
-    const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
-    dim3 grid((unsigned)((rows + 15) / 16));
+    dim3 grid((unsigned)((n_tok + 15) / 16), (unsigned)c.num_kv_heads, (unsigned)n_layers);
     if (c.scheme == WC_DITHER_INT8) {
       if (c.num_outliers != 0)
         hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8, true>), grid, dim3(256), 0, st, c,
@@ -649,7 +636,7 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
       set_error("wc_write_kv: 2-bit cache needs k_aux and v_aux");
       return WC_EINVAL;
     }
-    dim3 grid((unsigned)((int64_t)n_layers * (n_tok / 32) * c.num_kv_heads));
+    dim3 grid((unsigned)(n_tok / 32), (unsigned)c.num_kv_heads, (unsigned)n_layers);
     if (in_dtype == WC_BF16)
       hipLaunchKernelGGL((write_kivi2_kernel<uint16_t>), grid, dim3(256), 0, st, c, (const uint16_t*)k,
                          (const uint16_t*)v, a);
@@ -679,8 +666,8 @@ extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers
     set_error("wc_write_kv_pages: scheme %d writes through wc_write_kv", c.scheme);
     return WC_EUNSUPPORTED;
   }
-  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_pages < 0 ||
-      n_pages * 16 > (int64_t(1) << 26)) {
+  if (layer0 < 0 || n_layers < 1 || n_layers > 65535 || layer0 + n_layers > c.num_layers || n_pages < 0 ||
+      n_pages * 16 > (int64_t(1) << 26) || c.num_kv_heads > 65535) {
     set_error("wc_write_kv_pages: layer range or page count out of range");
     return WC_EINVAL;
   }
@@ -713,7 +700,7 @@ extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers
   }
   if (n_pages == 0) return WC_OK;
   PageArgs a{n_pages, layer_stride, c.num_pages, c.num_kv_heads, layer0, pages, pos0, seed};
-  dim3 grid((unsigned)((int64_t)n_layers * n_pages * c.num_kv_heads));
+  dim3 grid((unsigned)n_pages, (unsigned)c.num_kv_heads, (unsigned)n_layers);
   hipStream_t st = (hipStream_t)stream;
   const bool bf = in_dtype == WC_BF16;
 #define WC_PAGES(T, SCH, OU) hipLaunchKernelGGL((write_pages_kernel<T, SCH, OU>), grid, dim3(256), 0, st, c, \
@@ -751,7 +738,8 @@ extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const
     set_error("wc_witness: cache %s witness not set", values ? "value" : "key");
     return WC_EINVAL;
   }
-  if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.num_layers || n_tok < 0 ||
+  if (layer0 < 0 || n_layers < 1 || n_layers > 65535 || c.num_kv_heads > 65535 ||
+      layer0 + n_layers > c.num_layers || n_tok < 0 || n_tok > (int64_t(1) << 30) ||
       (n_layers > 1 && layer_stride < n_tok * c.num_kv_heads * 128)) {
     set_error("wc_witness: layer range, token count or layer stride out of range");
     return WC_EINVAL;
@@ -762,8 +750,7 @@ extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const
   }
   if (n_tok == 0) return WC_OK;
   RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, nullptr, nullptr};
-  const int64_t rows = (int64_t)n_layers * n_tok * c.num_kv_heads;
-  dim3 grid((unsigned)((rows + 15) / 16));
+  dim3 grid((unsigned)((n_tok + 15) / 16), (unsigned)c.num_kv_heads, (unsigned)n_layers);
   hipStream_t st = (hipStream_t)stream;
   if (in_dtype == WC_BF16) {
     if (values)
