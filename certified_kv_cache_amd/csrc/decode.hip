@@ -674,7 +674,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     auto draws = [&](int j, uint32_t (&hh)[4], uint32_t (&ll)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t wd = pcg_out(st0 + (uint32_t)(4 * j + e) * kPcgMul);
+        const uint32_t wd = pcg_out_sdwa(st0 + (uint32_t)(4 * j + e) * kPcgMul);
         hh[e] = perm(kMagic, wd, 0x04030401u);
         ll[e] = perm(kMagic, wd, 0x04020400u);
       }

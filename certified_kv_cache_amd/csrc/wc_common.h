@@ -22,6 +22,18 @@ __host__ __device__ __forceinline__ uint32_t pcg_out(uint32_t state) {
   return (word >> 22u) ^ word;
 }
 __host__ __device__ __forceinline__ uint32_t pcg(uint32_t v) { return pcg_out(v * kPcgMul + kPcgInc); }
+// The same permutation in six VALU instructions instead of eight: the shift
+// s >> ((s >> 28) + 4) is (s >> 4) >> (s >> 28), and s >> 28 is byte 3 of
+// s >> 4, which an SDWA operand select of the shift amount reads directly.
+__device__ __forceinline__ uint32_t pcg_out_sdwa(uint32_t state) {
+  const uint32_t u = state >> 4u;
+  uint32_t r;
+  asm("v_lshrrev_b32_sdwa %0, %1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(u));
+  const uint32_t word = (r ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
 // The LCG step is linear: the state of counter v + i is the state of v plus
 // i * kPcgMul, so runs of consecutive counters need one multiply in all.
 
