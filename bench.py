@@ -106,9 +106,9 @@ def fp8_variant(w, B, S, iters):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = time_decode(decode, iters, warm=100, mask=1, with_risk=True)
-    t_on = time_decode(decode, iters, mask=1, with_risk=False)
-    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    t = time_modes(decode, iters, {"risk": dict(mask=1, with_risk=True), "on": dict(mask=1, with_risk=False),
+                                   "off": dict(mask=0, with_risk=False)}, warm=60)
+    t_risk, t_on, t_off = t["risk"], t["on"], t["off"]
     nb = decode_bytes(B, S, True, scales=False)
     del cache
     return {"decode_us": round(t_risk, 2), "decode_meter_on_us": round(t_on, 2), "decode_meter_off_us": round(t_off, 2),
@@ -135,9 +135,9 @@ def scheme_variant(w, B, S, iters, scheme):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = min(time_decode(decode, iters, warm=100, mask=1, with_risk=True), time_decode(decode, iters, mask=1, with_risk=True))
-    t_on = time_decode(decode, iters, mask=1, with_risk=False)
-    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    t = time_modes(decode, iters, {"risk": dict(mask=1, with_risk=True), "on": dict(mask=1, with_risk=False),
+                                   "off": dict(mask=0, with_risk=False)}, warm=60)
+    t_risk, t_on, t_off = t["risk"], t["on"], t["off"]
     if scheme == "store16":
         nb = B * S * HKV * (2 * 2 * D + 32) + B * (-(-S // 16)) * 4 + B * HQ * D * 2 + B * 12
     else:
@@ -164,8 +164,8 @@ def vcert_variant(w, B, S, iters):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_v = min(time_decode(decode, iters, warm=100, mask=3 | L.WC_METER_V), time_decode(decode, iters, mask=3 | L.WC_METER_V))
-    t_kv = min(time_decode(decode, iters, mask=3), time_decode(decode, iters, mask=3))
+    t = time_modes(decode, iters, {"v": dict(mask=3 | L.WC_METER_V), "kv": dict(mask=3)}, warm=60)
+    t_v, t_kv = t["v"], t["kv"]
     nb = decode_bytes(B, S, True) + B * S * HKV * 4
     del cache
     return {"decode_us": round(t_v, 2), "decode_without_v_us": round(t_kv, 2),
@@ -227,8 +227,8 @@ def outlier_variant(w, B, S, iters, m):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t_risk = min(time_decode(decode, iters, warm=100, mask=3, with_risk=True), time_decode(decode, iters, mask=3, with_risk=True))
-    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    t = time_modes(decode, iters, {"risk": dict(mask=3, with_risk=True), "off": dict(mask=0, with_risk=False)}, warm=60)
+    t_risk, t_off = t["risk"], t["off"]
     nb = decode_bytes(B, S, True) + B * S * HKV * 2 * m
     del cache
     return {"m": m, "decode_us": round(t_risk, 2), "decode_meter_off_us": round(t_off, 2), "decode_bytes": nb,
@@ -262,6 +262,21 @@ def make_step(w, B, S):
         L.wc_gate_pagein(w["cache"], 0, risk, lse, w["tab"], w["ctx"], TAU, w["host"], pool_used, paged, gws)
 
     return step, decode, dict(o=o, lse=lse, ra=ra, rb=rb, paged=paged)
+
+
+def time_modes(decode, iters, modes, rounds=3, warm=20):
+    """Median loop time (us) of each decode mode in `modes` (name -> keyword
+    arguments of `decode`), the modes' loops taken in turn for `rounds`
+    rounds after `warm` launches of each."""
+    import numpy as np
+    for kw in modes.values():
+        for _ in range(warm):
+            decode(**kw)
+    got = {m: [] for m in modes}
+    for _ in range(rounds):
+        for m, kw in modes.items():
+            got[m].append(time_decode(decode, iters, **kw))
+    return {m: float(np.median(v)) for m, v in got.items()}
 
 
 def time_decode(decode, iters, warm=1, **kw):
@@ -494,6 +509,41 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
     return res
 
 
+def decode_bounds(B, S, iters=20):
+    """What bounds the decode: the headline launch (dithered INT8 with block
+    risks, and meter off; fp8 raw cast the same) with its random page table,
+    and again with every page-table entry folded into 64 physical pages, so
+    that the cache the launch reads stays in L2 and the time is the kernel's
+    compute alone."""
+    import torch
+    w = setup(B, S)
+    L = w["L"]
+    mp = w["tab"].shape[1]
+    part = torch.empty(L.wc_decode_workspace_bytes(B, HQ, NSPLIT) // 4, device="cuda")
+    risk = torch.empty((B, HQ, mp), device="cuda")
+    c8 = L.KVCache(L.WC_FP8_E4M3, 1, w["npages"], HKV)
+    L.wc_write_kv(c8, w["k"], w["v"], w["slot"], w["pos"], torch.zeros_like(w["pos"], dtype=torch.int64))
+    folded = (w["tab"] % 64).contiguous()
+    sm = 1.0 / math.sqrt(D)
+    res = {"metric": "decode time with the cache in HBM and with it L2-resident (compute alone)", "unit": "us",
+           "data": "synthetic", "config": {"workload": f"decode B={B} S={S} Hq={HQ} Hkv={HKV} d={D}, {NSPLIT} splits"},
+           "hbm": {}, "l2_resident": {}}
+    for tname, tab in (("hbm", w["tab"]), ("l2_resident", folded)):
+        modes = {}
+        for name, cache, mask, r in (("int8_risk", w["cache"], 3, True), ("int8_off", w["cache"], 0, False),
+                                     ("fp8_risk", c8, 1, True), ("fp8_off", c8, 0, False)):
+            modes[name] = (cache, mask, r)
+
+        def decode(name):
+            cache, mask, r = modes[name]
+            L.wc_decode_attn_meter(cache, 0, w["q"], tab, w["ctx"], w["seed"], part, sm, mask, DELTA[0], *DELTA[1:],
+                                   NSPLIT, block_logrisk=risk if r else None)
+
+        t = time_modes(decode, iters, {n: dict(name=n) for n in modes}, warm=60)
+        res[tname] = {n: round(v, 2) for n, v in t.items()}
+    return res
+
+
 def latency(iters=200):
     """Decode + merge latency of the two parity-size workloads: one head with
     256 fp32 tokens (dithered INT8, Tier A+B), and one layer of 28 q / 4 KV
@@ -561,11 +611,12 @@ def main():
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill-write", "gate-flow", "gate-compare", "latency"],
+                    choices=["decode", "prefill-write", "gate-flow", "gate-compare", "latency", "decode-bounds"],
                     help="decode: the headline line (default); prefill-write: the 28-layer write path per scheme; "
                          "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps; "
                          "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate; "
-                         "latency: decode + merge latency at the two parity sizes")
+                         "latency: decode + merge latency at the two parity sizes; "
+                         "decode-bounds: the decode with its cache in HBM and L2-resident (compute alone)")
     ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -583,6 +634,9 @@ def main():
     if args.workload == "latency":
         print(json.dumps(latency()), flush=True)
         return
+    if args.workload == "decode-bounds":
+        print(json.dumps(decode_bounds(args.batch, args.ctx)), flush=True)
+        return
     if args.workload == "gate-compare":
         print(json.dumps(gate_flow(args.layers, max(2, min(args.steps, 8)), taus=(0.1, 0.05, 0.02), scheme="int8")),
               flush=True)
@@ -599,14 +653,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    # the step's decode (meter on, block risks) timed on its own over 10 loops
-    # of back-to-back launches (median and p10-p90 of the loop means), then the
-    # same kernel without block risks and with the meter off for the overhead
+    # the step's decode (meter on, block risks), the same kernel without block
+    # risks, and with the meter off, each timed as 10 loops of back-to-back
+    # launches taken in turn (risk, on, off, risk, ...) so that a drift of the
+    # GPU's clocks over the run falls on all three alike; median and p10-p90
+    # of the loop means
     iters = max(args.steps, 10)
-    loops = sorted(time_decode(decode, iters, mask=3, with_risk=True) for _ in range(10))
+    loops, on_loops, off_loops = [], [], []
+    for _ in range(10):
+        loops.append(time_decode(decode, iters, mask=3, with_risk=True))
+        on_loops.append(time_decode(decode, iters, mask=3, with_risk=False))
+        off_loops.append(time_decode(decode, iters, mask=0, with_risk=False))
+    loops.sort()
     t_risk = float(np.median(loops))
-    t_on = min(time_decode(decode, iters, mask=3, with_risk=False), time_decode(decode, iters, mask=3, with_risk=False))
-    t_off = time_decode(decode, iters, mask=0, with_risk=False)
+    t_on = float(np.median(on_loops))
+    t_off = float(np.median(off_loops))
     dec_step_us = t_risk
     bytes_on = decode_bytes(B, S, True)
     ach = bytes_on / (dec_step_us * 1e-6) / 1e9
@@ -640,9 +701,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_GBS, 4), "traffic": traffic},
         "decode_us": round(dec_step_us, 2), "decode_us_p10": round(loops[1], 2), "decode_us_p90": round(loops[8], 2),
-        "decode_loops": f"10 loops of {iters} back-to-back launches (median; p10, p90 of the loop means)",
+        "decode_loops": f"10 rounds of three loops of {iters} back-to-back launches (block risks, meter on, meter "
+                        f"off, in turn); median, and p10, p90 of the loop means with block risks",
         "decode_meter_on_us": round(t_on, 2),
         "decode_meter_off_us": round(t_off, 2), "meter_overhead": round(t_on / t_off - 1, 4),
+        "meter_overhead_with_risks": round(t_risk / t_off - 1, 4),
         "pct_peak": round(100 * ach / PEAK_GBS, 2),
         "kv_tokens_per_s": round(B * S / (dec_step_us * 1e-6), 1),
         "decode_steps_per_s_per_layer": round(1e6 / dec_step_us, 1),
