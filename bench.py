@@ -541,7 +541,55 @@ def decode_bounds(B, S, iters=20):
 
         t = time_modes(decode, iters, {n: dict(name=n) for n in modes}, warm=60)
         res[tname] = {n: round(v, 2) for n, v in t.items()}
+        if tname == "hbm":
+            # board power and shader clock while each mode runs back to back
+            # for about four seconds (amd-smi sampled once in the middle)
+            res["power_clock"] = {n: power_clock(lambda: decode(n)) for n in modes}
     return res
+
+
+def power_clock(launch, seconds=4.0):
+    """Socket power (W) and current shader clock (MHz) read by amd-smi while
+    `launch` runs back to back on the device; None where amd-smi is absent."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    smi = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if smi is None:
+        return None
+    stop = [False]
+
+    def run():
+        while not stop[0]:
+            for _ in range(20):
+                launch()
+            torch.cuda.synchronize()
+
+    th = threading.Thread(target=run)
+    th.start()
+    time.sleep(seconds / 2)
+    try:
+        out = subprocess.run([smi, "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
+                             timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        out = ""
+    time.sleep(seconds / 2)
+    stop[0] = True
+    th.join()
+    try:
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = g["clock"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+        out = {"socket_power_W": g["power"]["socket_power"]["value"],
+               "gfx_clock_MHz_mean": round(sum(gfx) / len(gfx), 1), "gfx_clock_MHz_min": min(gfx),
+               "gfx_clock_MHz_max": max(gfx)}
+        if isinstance(clk.get("mem_0"), dict):
+            out["mem_clock_MHz"] = clk["mem_0"]["clk"]["value"]
+        return out
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
 
 
 def latency(iters=200):
