@@ -259,7 +259,8 @@ def make_step(w, B, S):
         L.wc_write_kv(w["cache"], n["k"], n["v"], n["slot"], n["pos"], n["seed"])
         decode()
         L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb)
-        L.wc_gate_pagein(w["cache"], 0, risk, lse, w["tab"], w["ctx"], TAU, w["host"], pool_used, paged, gws)
+        L.wc_gate_pagein(w["cache"], 0, risk, lse, w["tab"], w["ctx"], TAU, w["host"], pool_used, paged, gws,
+                         meter=rb)
 
     return step, decode, dict(o=o, lse=lse, ra=ra, rb=rb, paged=paged)
 
@@ -453,6 +454,7 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
     o = torch.empty((NB, HQ, D), device=dev)
     lse = torch.empty((NB, HQ), device=dev)
     ra = torch.empty((NB, HQ), device=dev)
+    rb = torch.empty((NB, HQ), device=dev)
     gws = torch.empty(L.wc_gate_workspace_bytes(NB, HKV, mp), dtype=torch.uint8, device=dev)
     cname = "fp8 raw-cast" if scheme == "fp8" else "dithered INT8"
     res = {"metric": "gated ragged decode: page-in bytes per step and attention throughput", "data": "synthetic",
@@ -483,11 +485,12 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
                                        mask | (L.WC_BLOCK_CMAX if kind == "tanh" else 0), DELTA[0], *DELTA[1:],
                                        NSPLIT, block_logrisk=risk)
                 b.record()
-                L.wc_lse_merge(part, NB, HQ, NSPLIT, o, lse, ra)
+                L.wc_lse_merge(part, NB, HQ, NSPLIT, o, lse, ra, rb)
                 if kind == "tanh":
                     L.wc_gate_pagein_tanh(cache, layer, risk, tab_d, ctx, tau, host, pool_used, paged, gws)
                 else:
-                    L.wc_gate_pagein(cache, layer, risk, lse, tab_d, ctx, tau, host, pool_used, paged, gws)
+                    L.wc_gate_pagein(cache, layer, risk, lse, tab_d, ctx, tau, host, pool_used, paged, gws,
+                                     meter=rb if mask & 2 else ra)
                 torch.cuda.synchronize()
                 t_dec += a.elapsed_time(b) * 1e3
             per_step.append(int(paged.item()) - before)

@@ -50,7 +50,7 @@ def _load():
                                  P, P, ctypes.c_float, ctypes.c_uint, ctypes.c_double, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P, P],
         "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P],
-        "wc_gate_pagein": [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
+        "wc_gate_pagein": [P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
         "wc_outlier_select": [P, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _i64, ctypes.c_int, P, P],
@@ -235,10 +235,11 @@ def wc_gate_workspace_bytes(B, Hkv, max_pages):
 
 
 def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, host_exact_k, pool_used,
-                   bytes_paged, workspace, budget_blocks=-1, selected=None, rho_fx=None, stream=None):
+                   bytes_paged, workspace, budget_blocks=-1, selected=None, rho_fx=None, meter=None, stream=None):
     B, Hq, max_pages = block_logrisk.shape
     _check("wc_gate_pagein", lib.wc_gate_pagein(
-        cache.ref(), layer, _ptr(block_logrisk), _ptr(lse), B, Hq, _ptr(page_table), max_pages, _ptr(ctx_len),
+        cache.ref(), layer, _ptr(block_logrisk), _ptr(lse), _ptr(meter), B, Hq, _ptr(page_table), max_pages,
+        _ptr(ctx_len),
         float(tau), int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged), _ptr(selected),
         _ptr(rho_fx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 

@@ -11,20 +11,23 @@
 // turned into 40-bit fixed point so every decision is integer arithmetic
 // and does not depend on summation order.
 //
-// Kernels: (1) per (sequence, KV head, 256-block chunk): fixed-point risks
-// of all the group's query heads and their chunk sums; (2) per (sequence, KV
-// head): trigger test on the sums, then (rarely) bitonic sort of the
-// candidates by risk in LDS and per-head scans for the shortest sufficient
-// prefix; (3) one workgroup: exclusive scan of the counts in (sequence, head)
-// order hands out exact-pool slots deterministically; (4) copy each selected
-// block from pinned host memory (zero-copy reads), store it as fp16 with a
-// per-token power of two, zero its witness, mark it.
+// Kernels: (1) per (sequence, KV head): fixed-point risks of all the group's
+// query heads summed in the workgroup, the trigger test on the sums, then
+// (rarely) bitonic sort of the candidates by risk in LDS and per-head scans
+// for the shortest sufficient prefix; (2) per (sequence, KV head) and copy
+// lane: the pool slots of the pair from the exclusive prefix of the counts in
+// (sequence, head) order (deterministic, no atomics), the pool counters
+// updated by one workgroup, then each selected block copied from pinned host
+// memory (zero-copy reads), stored as fp16 with a per-token power of two, its
+// witness zeroed and the block marked.  Kernel (1) keeps the pool counter's
+// value from before the call in the workspace, which is all kernel (2) reads
+// of it, so the one write of the counter races with no read.
 //
 // The tanh gate (the page-in comparison of the summary): the bound
 // tanh(max_t c_t / 2) is <= tau for every head exactly when no unrepaired
 // token has c_t > c* = 2 artanh(tau), so kernel (2) is replaced by one that
 // takes every unrepaired block whose largest bound over the group's heads
-// exceeds c*, ranked by that bound; (3) and (4) are shared.
+// exceeds c*, ranked by that bound; (2) is shared.
 #include <math.h>
 
 #include "wc_common.h"
@@ -38,16 +41,16 @@ constexpr int kMaxSortPages = 4096;
 struct GateArgs {
   const float* logrisk;
   const float* lse;
+  const float* meter;     // nullable: merged meter R of the gate's tier, [B][Hq]
   const int32_t* page_table;
   const int32_t* ctx_len;
   uint64_t* fx;           // [B][Hq][max_pages], optional copy for the caller
-  uint64_t* xpart;        // [B][Hq][nchunk]: per 256-block chunk sums of rho_fx
   int32_t* sel;           // [B][Hkv][max_pages]
   int32_t* count;         // [B][Hkv]
-  int32_t* base;          // [B][Hkv]
-  int32_t* take;          // [B][Hkv]
-  int B, Hq, G, max_pages, layer, nchunk;
+  int64_t* pool_old;      // the pool counter before this call
+  int B, Hq, G, max_pages, layer;
   uint64_t T;
+  float e_tau;            // E_tau rounded down to float (the quiet test)
   int64_t budget;
 };
 
@@ -72,49 +75,6 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// Fixed-point risks of one 256-block chunk of one (sequence, KV head), all
-// its query heads: chunk sums for the trigger test (and the optional copy).
-__global__ void __launch_bounds__(256) gate_risk_kernel(wc_cache c, GateArgs a) {
-  __shared__ uint64_t wsum[4][16];
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int hkv = c.num_kv_heads;
-  const int P = (a.ctx_len[b] + 15) >> 4;
-  const int G = a.G;
-  const int j = chunk * 256 + t;
-  const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;
-  // every load is issued unconditionally (indices clamped into range) so that
-  // they are all in flight together
-  const int jc = min(j, a.max_pages - 1);
-  float lr[16], ls[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    const int nc = min(n, G - 1);
-    lr[n] = a.logrisk[row0 + (int64_t)nc * a.max_pages + jc];
-    ls[n] = a.lse[b * a.Hq + g * G + nc];
-  }
-  const int phys = a.page_table[(int64_t)b * a.max_pages + min(j, max(P - 1, 0))];
-  // repaired blocks (exact keys in the pool) carry no risk
-  const bool live = j < P && c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] < 0;
-  uint64_t part[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) part[n] = (n < G && live) ? risk_fx(lr[n], ls[n]) : 0;
-  if (a.fx && j < a.max_pages) {
-#pragma unroll
-    for (int n = 0; n < 16; ++n)
-      if (n < G) a.fx[row0 + (int64_t)n * a.max_pages + j] = part[n];
-  }
-#pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    if (n < G) {
-      const uint64_t v = wave_sum_u64(part[n]);
-      if ((t & 63) == 0) wsum[t >> 6][n] = v;
-    }
-  }
-  __syncthreads();
-  if (t < G)
-    a.xpart[((int64_t)b * a.Hq + g * G + t) * a.nchunk + chunk] = wsum[0][t] + wsum[1][t] + wsum[2][t] + wsum[3][t];
-}
-
 // Bitonic sort of keys[0 .. np2) (np2 a power of two) in LDS, descending;
 // 256 threads, every thread calls it.
 __device__ void sort_desc(uint64_t* keys, int np2, int t) {
@@ -136,23 +96,93 @@ __device__ void sort_desc(uint64_t* keys, int np2, int t) {
   }
 }
 
-__global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a) {
+// Fixed-point risks, trigger test and (rarely) selection, one workgroup per
+// (sequence, KV head).
+//
+// Quiet pairs: with the merged meter R_h given, E_h = 2 R_h / (sqrt(1 + 2 R_h) + 1)
+// is the pair's head risk in float.  X_h / 2^40 is the same sum taken per block
+// (every block rounded up by less than 2^-40) from the same block risks, so
+// X_h <= 2^40 (E_h (1 + 2^-10) + (P + 1) 2^-39) with a wide margin for the
+// float roundings on both sides (about 1e-6 relative); when that bound is
+// below E_tau for every head the exact test could only answer "no trigger",
+// and the pair skips the block pass.
+__global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a, const int64_t* pool_used) {
   __shared__ uint64_t keys[kMaxSortPages];
   __shared__ uint64_t red[256];
   __shared__ float hlse[16];
   __shared__ uint8_t rep[kMaxSortPages];
+  __shared__ uint64_t hsum[4][16];
   __shared__ int kneed;
   const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  if (b == 0 && g == 0 && t == 0) *a.pool_old = *pool_used;
   const int hkv = c.num_kv_heads;
   const int S = a.ctx_len[b];
   const int P = (S + 15) >> 4;
   const int G = a.G;
   const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;   // head n's row: row0 + n * max_pages
-  // X_h from the chunk sums; the trigger test is uniform across the workgroup
+  if (a.meter && !a.fx) {
+    bool quiet = true;
+    for (int n = 0; n < G; ++n) {
+      const float R = a.meter[b * a.Hq + g * G + n];
+      const float E = 2.0f * R / (sqrtf(1.0f + 2.0f * R) + 1.0f);
+      quiet = quiet && R >= 0.0f && E * 1.0009765625f + (float)(P + 1) * 1.8189894035458565e-12f <= a.e_tau;
+    }
+    if (quiet || P == 0) {
+      if (t == 0) a.count[b * hkv + g] = 0;
+      return;
+    }
+  }
+  // X_h = sum_j rho_fx[h][j] over blocks j = t, t + 256, ...: each round
+  // issues its block-risk loads and its repaired-flag gathers together
+  uint64_t xs[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) xs[n] = 0;
+  float hl[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) hl[n] = n < G ? a.lse[b * a.Hq + g * G + n] : 0.0f;
+  const int jend = a.fx ? a.max_pages : P;           // the optional copy covers every block
+  for (int j0 = 0; j0 < jend; j0 += 4 * 256) {
+    float lr[4][16];
+    int ph[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * 256 + t, a.max_pages - 1);
+      ph[u] = a.page_table[(int64_t)b * a.max_pages + min(j, max(P - 1, 0))];
+#pragma unroll
+      for (int n = 0; n < 16; ++n) lr[u][n] = n < G ? a.logrisk[row0 + (int64_t)n * a.max_pages + j] : -INFINITY;
+    }
+    bool live[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * 256 + t;
+      // repaired blocks (exact keys in the pool) carry no risk
+      live[u] = j < P && c.exact_slot[((int64_t)a.layer * c.num_pages + ph[u]) * hkv + g] < 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * 256 + t;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        if (n < G) {
+          const uint64_t v = live[u] ? risk_fx(lr[u][n], hl[n]) : 0;
+          xs[n] += v;
+          if (a.fx && j < a.max_pages) a.fx[row0 + (int64_t)n * a.max_pages + j] = v;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    if (n < G) {
+      const uint64_t v = wave_sum_u64(xs[n]);
+      if ((t & 63) == 0) hsum[t >> 6][n] = v;
+    }
+  }
+  __syncthreads();
+  // the trigger test is uniform across the workgroup
   uint64_t xmax = 0;
   for (int n = 0; n < G; ++n) {
-    uint64_t X = 0;
-    for (int k = 0; k < a.nchunk; ++k) X += a.xpart[((int64_t)b * a.Hq + g * G + n) * a.nchunk + k];
+    const uint64_t X = hsum[0][n] + hsum[1][n] + hsum[2][n] + hsum[3][n];
     xmax = X > xmax ? X : xmax;
   }
   if (t == 0) a.count[b * hkv + g] = 0;
@@ -236,10 +266,11 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
 // the unrepaired blocks with max_h cmax[h][j] > c* (float32 comparison); sort
 // key = the float's bits (monotone for values >= 0) << 16 | (65535 - j).
 __global__ void __launch_bounds__(256) gate_tanh_select_kernel(wc_cache c, GateArgs a, const float* cmax,
-                                                               float cstar) {
+                                                               float cstar, const int64_t* pool_used) {
   __shared__ uint64_t keys[kMaxSortPages];
   __shared__ int ncand[256];
   const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  if (b == 0 && g == 0 && t == 0) *a.pool_old = *pool_used;
   const int hkv = c.num_kv_heads;
   const int P = (a.ctx_len[b] + 15) >> 4;
   const int G = a.G;
@@ -275,66 +306,62 @@ __global__ void __launch_bounds__(256) gate_tanh_select_kernel(wc_cache c, GateA
   if (t == 0) a.count[b * hkv + g] = k;
 }
 
-// One workgroup: slots in (b, g, rank) order from *pool_used, stop at capacity.
-__global__ void __launch_bounds__(256) gate_assign_kernel(GateArgs a, int n_bg, int64_t capacity, int64_t* pool_used,
-                                                          int64_t* bytes_paged, int32_t* selected) {
-  __shared__ int64_t sc[256];
-  __shared__ int64_t carry;
-  const int t = threadIdx.x;
-  if (t == 0) carry = *pool_used;
-  __syncthreads();
-  for (int c0 = 0; c0 < n_bg; c0 += 256) {
-    const int i = c0 + t;
-    const int64_t cnt = i < n_bg ? a.count[i] : 0;
-    sc[t] = cnt;
-    __syncthreads();
-    for (int s = 1; s < 256; s <<= 1) {
-      const int64_t add = t >= s ? sc[t - s] : 0;
-      __syncthreads();
-      sc[t] += add;
-      __syncthreads();
-    }
-    const int64_t start = carry + sc[t] - cnt;
-    if (i < n_bg) {
-      int64_t room = capacity - start;
-      room = room < 0 ? 0 : room;
-      const int64_t tk = cnt < room ? cnt : room;
-      a.base[i] = (int32_t)start;
-      a.take[i] = (int32_t)tk;
-    }
-    __syncthreads();
-    if (t == 255) carry += sc[255];
-    __syncthreads();
-  }
-  if (t == 0) {
-    const int64_t used0 = *pool_used;
-    const int64_t newu = carry < capacity ? carry : (used0 > capacity ? used0 : capacity);
-    *pool_used = newu;
-    *bytes_paged += (newu - used0) * 4096;
-  }
-  if (selected) {
-    for (int i = 0; i < n_bg; ++i) {
-      int32_t* out = selected + (int64_t)i * (a.max_pages + 1);
-      const int tk = a.take[i];
-      if (t == 0) out[0] = tk;
-      for (int j = t; j < tk; j += 256) out[1 + j] = a.sel[(int64_t)i * a.max_pages + j];
-    }
-  }
-}
-
-// Copy selected blocks: one workgroup per block, 256 threads x 8 bf16.
-__global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, const uint16_t* __restrict__ host_k) {
+// Pool slots and page-in, one workgroup per ((sequence, KV head) pair bg,
+// copy lane y).  Slots go in (b, g, rank) order from the counter's value
+// before the call: pair bg starts after the counts of pairs 0 .. bg-1, and
+// the selection stops where the pool is full.  One block per workgroup and
+// round, 256 threads x 8 bf16.
+__global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, const uint16_t* __restrict__ host_k,
+                                                        int n_bg, int64_t capacity, int64_t* pool_used,
+                                                        int64_t* bytes_paged, int32_t* selected) {
+  __shared__ int64_t red[2][4];
   const int bg = blockIdx.x;
   const int hkv = c.num_kv_heads;
   const int b = bg / hkv, g = bg % hkv;
-  const int tk = a.take[bg];
   const int t = threadIdx.x;
+  // exclusive prefix of the counts before bg, and their total
+  int64_t before = 0, total = 0;
+  for (int i = t; i < n_bg; i += 256) {
+    const int64_t n = a.count[i];
+    total += n;
+    before += i < bg ? n : 0;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    before += __shfl_xor(before, m, 64);
+    total += __shfl_xor(total, m, 64);
+  }
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = before;
+    red[1][t >> 6] = total;
+  }
+  __syncthreads();
+  before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  total = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const int64_t used0 = *a.pool_old;
+  const int64_t start = used0 + before;
+  const int64_t cnt = a.count[bg];
+  const int64_t room = capacity - start > 0 ? capacity - start : 0;
+  const int tk = (int)(cnt < room ? cnt : room);
+  if (blockIdx.y == 0) {
+    if (bg == n_bg - 1 && t == 0) {
+      const int64_t carry = used0 + total;
+      const int64_t newu = carry < capacity ? carry : (used0 > capacity ? used0 : capacity);
+      *pool_used = newu;
+      *bytes_paged += (newu - used0) * 4096;
+    }
+    if (selected) {
+      int32_t* out = selected + (int64_t)bg * (a.max_pages + 1);
+      if (t == 0) out[0] = tk;
+      for (int j = t; j < tk; j += 256) out[1 + j] = a.sel[(int64_t)bg * a.max_pages + j];
+    }
+  }
   const int tok = t >> 4, part = t & 15;
   for (int i = blockIdx.y; i < tk; i += gridDim.y) {
     const int j = a.sel[(int64_t)bg * a.max_pages + i];
     const int phys = a.page_table[(int64_t)b * a.max_pages + j];
     const int64_t pg = ((int64_t)a.layer * c.num_pages + phys) * hkv + g;
-    const int64_t slot = (int64_t)a.base[bg] + i;
+    const int64_t slot = start + i;
     const uint4 v = *reinterpret_cast<const uint4*>(host_k + (pg * 16 + tok) * 128 + 8 * part);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     float x[8];
@@ -372,10 +399,10 @@ using namespace wc;
 
 extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
   if (B < 0 || Hkv < 0 || max_pages < 0) return 0;
-  // chunk sums (up to 16 query heads per KV head), selected block indices,
-  // then count / base / take per (sequence, KV head)
-  const size_t nchunk = ((size_t)max_pages + 255) / 256;
-  return (size_t)B * Hkv * 16 * nchunk * 8 + (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 3 * 4;
+  // selected block indices and the count per (sequence, KV head), then the
+  // pool counter's value before the call (8-byte aligned)
+  const size_t head = (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 4;
+  return ((head + 7) & ~(size_t)7) + 8;
 }
 
 namespace {
@@ -408,20 +435,16 @@ int gate_prepare(const char* fn, const wc_cache* cache, int layer, int B, int Hq
   }
   const int hkv = c.num_kv_heads;
   char* ws = (char*)workspace;
-  const int nchunk = (max_pages + 255) / 256;
-  a.xpart = (uint64_t*)ws;
-  ws += (size_t)B * hkv * 16 * nchunk * 8;
   a.sel = (int32_t*)ws;
   ws += (size_t)B * hkv * max_pages * 4;
   a.count = (int32_t*)ws;
-  a.base = a.count + B * hkv;
-  a.take = a.base + B * hkv;
+  const size_t head = (size_t)B * hkv * max_pages * 4 + (size_t)B * hkv * 4;
+  a.pool_old = (int64_t*)((char*)workspace + ((head + 7) & ~(size_t)7));
   a.B = B;
   a.Hq = Hq;
   a.G = Hq / hkv;
   a.max_pages = max_pages;
   a.layer = layer;
-  a.nchunk = nchunk;
   return WC_OK;
 }
 }  // namespace
@@ -454,18 +477,15 @@ extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float
   const int hkv = c.num_kv_heads;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(gate_tanh_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a, block_cmax,
-                     cstar);
+                     cstar, (const int64_t*)pool_used);
   if (int e = check_launch("wc_gate_pagein_tanh select")) return e;
-  hipLaunchKernelGGL(gate_assign_kernel, dim3(1), dim3(256), 0, st, a, B * hkv, c.pool_capacity, pool_used,
-                     bytes_paged, selected);
-  if (int e = check_launch("wc_gate_pagein_tanh assign")) return e;
   hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,
-                     (const uint16_t*)dev_host);
+                     (const uint16_t*)dev_host, B * hkv, c.pool_capacity, pool_used, bytes_paged, selected);
   return check_launch("wc_gate_pagein_tanh copy");
 }
 
-extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse, int B,
-                              int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
+extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                              const float* meter, int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
                               int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
                               int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx, void* workspace,
                               size_t ws_bytes, void* stream) {
@@ -487,23 +507,21 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
   if (B == 0) return WC_OK;
   const wc_cache& c = *cache;
   const int hkv = c.num_kv_heads;
-  const int nchunk = a.nchunk;
   a.logrisk = block_logrisk;
   a.lse = lse;
+  a.meter = meter;
+  // E_tau rounded down to float: the quiet test errs toward the exact pass
+  a.e_tau = nextafterf((float)et, 0.0f);
   a.page_table = page_table;
   a.ctx_len = ctx_len;
   a.fx = rho_fx;
   a.T = (uint64_t)floor(et * 1099511627776.0);
   a.budget = budget_blocks;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(gate_risk_kernel, dim3((unsigned)nchunk, (unsigned)hkv, (unsigned)B), dim3(256), 0, st, c, a);
-  if (int e = check_launch("wc_gate_pagein risk")) return e;
-  hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a);
+  hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a,
+                     (const int64_t*)pool_used);
   if (int e = check_launch("wc_gate_pagein select")) return e;
-  hipLaunchKernelGGL(gate_assign_kernel, dim3(1), dim3(256), 0, st, a, B * hkv, c.pool_capacity, pool_used,
-                     bytes_paged, selected);
-  if (int e = check_launch("wc_gate_pagein assign")) return e;
   hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,
-                     (const uint16_t*)dev_host);
+                     (const uint16_t*)dev_host, B * hkv, c.pool_capacity, pool_used, bytes_paged, selected);
   return check_launch("wc_gate_pagein copy");
 }

@@ -320,6 +320,14 @@ int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, fl
  * are handed out in (b, g, rank) order from *pool_used; selection stops when
  * the pool is full.
  *
+ *  meter         nullable device fp32 [B][Hq]: the merged meter R of the same
+ *                tier as block_logrisk (R_B of a Tier B decode, else R_A), as
+ *                wc_lse_merge returns it with this lse.  A pair (b, g) whose
+ *                heads all have E = 2R / (sqrt(1 + 2R) + 1) with
+ *                E (1 + 2^-10) + (P_b + 1) 2^-39 <= E_tau cannot trigger (X_h
+ *                is that sum taken per block, each rounded up by < 2^-40), and
+ *                skips the pass over its block risks; the decisions are the
+ *                same as with meter = NULL.  Ignored when rho_fx is given.
  *  host_exact_k  pinned host bf16 [L][P][Hkv][16][128], device-readable.
  *  pool_used     device int64 [1], in/out.
  *  bytes_paged   device int64 [1], incremented by 4096 per repaired block.
@@ -330,7 +338,7 @@ int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, fl
  * Requires cache->exact_slot, exact_pool, exact_scale; 0 <= tau, E_tau < 64.
  */
 int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
-                   int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                   const float* meter, int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
                    double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
                    int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
                    void* workspace, size_t ws_bytes, void* stream);

@@ -104,7 +104,7 @@ def test_merge_and_gate_reject_bad_arguments():
     wsb = L.wc_gate_workspace_bytes(2, 4, 8)
 
     def call(cache=c, tau=0.2, mp=8, wsb=wsb, host=p):
-        return g(cache, 0, p, p, 2, 28, p, mp, p, tau, -1, host, p, p, None, None, p, wsb, None)
+        return g(cache, 0, p, p, None, 2, 28, p, mp, p, tau, -1, host, p, p, None, None, p, wsb, None)
 
     assert call(host=None) == L.WC_EINVAL
     assert call(tau=-1.0) == L.WC_EINVAL

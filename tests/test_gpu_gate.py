@@ -211,3 +211,49 @@ def test_tanh_gate_budget_and_no_trigger():
             want = gate.select_tanh(out["cmax"][b, g * 7:(g + 1) * 7, :P], np.zeros(P, bool), 0.0, budget=3)
             assert list(sel[b, g, 1:1 + sel[b, g, 0]]) == want
     assert used == int(sel[:, :, 0].sum())
+
+
+def _gate_meter(L, sc, host, out, tau, meter):
+    B, Hq, mp = sc.B, sc.Hq, sc.tab.shape[1]
+    ws = torch.empty(L.wc_gate_workspace_bytes(B, 4, mp), dtype=torch.uint8, device="cuda")
+    pool_used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    paged = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sel = torch.full((B, 4, mp + 1), -7, dtype=torch.int32, device="cuda")
+    L.wc_gate_pagein(sc.cache, sc.layer, torch.from_numpy(out["logrisk"]).cuda(),
+                     torch.from_numpy(out["lse"]).cuda(), sc.dev["tab"], sc.dev["ctx"], tau, host, pool_used, paged,
+                     ws, selected=sel, meter=None if meter is None else torch.from_numpy(meter).cuda())
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), int(pool_used.item()), int(paged.item())
+
+
+@pytest.mark.parametrize("scheme,mask,tier", [("fp8", 1, "R_A"), ("int8", 3, "R_B")])
+def test_meter_fast_path_same_decisions(scheme, mask, tier):
+    """With the merged meter given, quiet (sequence, KV head) pairs skip the
+    block pass; every decision, pool slot and page-in count must equal the
+    exact pass's, at thresholds where all, some and no pairs trigger."""
+    lens = [300, 1000, 64, 700, 17]
+    L, sc0, _ = _setup(lens, seed=31, scheme=scheme)
+    out0 = sc0.decode(n_split=4, mask=mask, risk=True)
+    R = out0[tier]
+    per_pair = R.reshape(len(lens), 4, 7).max(axis=2)
+    taus = [float(np.min(per_pair)) * 0.5, float(np.median(per_pair)), float(np.max(per_pair)) * 1.5]
+    mixed = None
+    for tau in taus:
+        print(f"gate fast path {scheme} tau={tau:.4g}", flush=True)
+        got = []
+        for meter in (None, R):
+            L, sc, host = _setup(lens, seed=31, scheme=scheme)
+            out = sc.decode(n_split=4, mask=mask, risk=True)
+            assert np.array_equal(out[tier], R)
+            got.append(_gate_meter(L, sc, host, out, tau, meter))
+        (s0, u0, p0), (s1, u1, p1) = got
+        assert u0 == u1 and p0 == p1, (tau, u0, u1)
+        for b in range(len(lens)):
+            for g in range(4):
+                n = s0[b, g, 0]
+                assert s1[b, g, 0] == n, (tau, b, g)
+                assert np.array_equal(s0[b, g, 1:1 + n], s1[b, g, 1:1 + n]), (tau, b, g)
+        if tau == taus[1]:
+            mixed = s0[:, :, 0]
+    # the middle threshold leaves some pairs quiet and triggers others
+    assert np.any(mixed > 0) and np.any(mixed == 0), mixed
