@@ -378,14 +378,9 @@ def prefill_write(iters, seed=4, NL=28, NT=4096):
             psd = torch.full((NT // 16,), 777, dtype=torch.int64, device="cuda")
             calls.append(("_pages", lambda: L.wc_write_kv_pages(cache, k, v, pg, p0, psd)))
         for suffix, call in calls:
-            call()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(iters):
-                call()
-            b.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) / iters * 1e3
+            # 100 untimed calls first: the clocks settle after a few hundred
+            # microseconds of back-to-back work
+            us = time_decode(call, iters, warm=100)
             tot = in_bytes + written
             out["schemes"][name + suffix] = {"us": round(us, 2), "bytes_written": written, "bytes_total": tot,
                                              "written_GBps": round(written / (us * 1e-6) / 1e9, 1),

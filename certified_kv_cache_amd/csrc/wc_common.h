@@ -66,32 +66,6 @@ __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, 
 // exact norm; scaling by 1 + 2^-17 keeps the stored value above it.
 constexpr float kWitnessGuard = 1.0f + 7.62939453125e-06f;
 
-// OCP fp8 e4m3fn, round to nearest even, saturating at +-448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fabsf(x);
-  uint32_t code;
-  if (!(a <= 448.0f)) {
-    code = 0x7Eu;                              // saturate (also NaN input)
-  } else if (a < 0.015625f) {                  // below 2^-6: subnormal grid 2^-9
-    code = (uint32_t)rintf(a * 512.0f);        // 8 -> smallest normal, coded 0x08
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // a in [2^e, 2^(e+1))
-    float m = ldexpf(a, 3 - e);                // in [8, 16)
-    uint32_t q = (uint32_t)rintf(m);
-    if (q == 16u) { q = 8u; e += 1; }
-    code = ((uint32_t)(e + 7) << 3) | (q - 8u);
-  }
-  return sign | code;
-}
-
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t e = (c >> 3) & 0xF, m = c & 7;
-  float v = e == 0 ? (float)m * 0.001953125f : ldexpf((float)(8 + m), (int)e - 10);
-  return (c & 0x80) ? -v : v;
-}
-
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

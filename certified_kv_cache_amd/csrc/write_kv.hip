@@ -76,6 +76,32 @@ template <int SCHEME>
 __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, const uint32_t (&words)[4],
                                        uint32_t exact, uint32_t (&packed)[2], float (&r)[8]) {
   packed[0] = packed[1] = 0;
+  if (SCHEME == WC_FP8_E4M3) {
+    // gfx950's conversions are OCP e4m3fn with round to nearest even; with the
+    // input clamped to +-448 first the encoding saturates there (a NaN input
+    // takes +-448 by its sign), and the decode is exact
+    float xc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xc[i] = fminf(fmaxf(x[i], -448.0f), 448.0f);
+      xc[i] = x[i] != x[i] ? copysignf(448.0f, x[i]) : xc[i];
+    }
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(xc[0], xc[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(xc[2], xc[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(xc[4], xc[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(xc[6], xc[7], w1, true);
+    packed[0] = (uint32_t)w0;
+    packed[1] = (uint32_t)w1;
+    r[0] = __builtin_amdgcn_cvt_f32_fp8(w0, 0) - x[0];
+    r[1] = __builtin_amdgcn_cvt_f32_fp8(w0, 1) - x[1];
+    r[2] = __builtin_amdgcn_cvt_f32_fp8(w0, 2) - x[2];
+    r[3] = __builtin_amdgcn_cvt_f32_fp8(w0, 3) - x[3];
+    r[4] = __builtin_amdgcn_cvt_f32_fp8(w1, 0) - x[4];
+    r[5] = __builtin_amdgcn_cvt_f32_fp8(w1, 1) - x[5];
+    r[6] = __builtin_amdgcn_cvt_f32_fp8(w1, 2) - x[6];
+    r[7] = __builtin_amdgcn_cvt_f32_fp8(w1, 3) - x[7];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t code;
@@ -101,8 +127,8 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
       code = (uint32_t)((int32_t)q + 128);
       xr = fmaf(s, q, -x[i]);                   // one rounding
     } else {
-      code = f32_to_e4m3(x[i]);
-      xr = e4m3_to_f32(code) - x[i];
+      code = 0u;                                // (fp8 returned above)
+      xr = 0.0f;
     }
     packed[i >> 2] |= code << (8 * (i & 3));
     r[i] = xr;
