@@ -409,10 +409,14 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
   const T* kb = kin + (int64_t)l * a.layer_stride;
   const T* vb = vin + (int64_t)l * a.layer_stride;
 
-  // keys: stage the 32 x 128 tile, per-channel min/max over the 32 tokens
-  for (int e = t; e < 32 * 128; e += 256) {
-    int tok = e >> 7, ch = e & 127;
-    xs[tok][ch] = ldf<T>(kb + ((i0 + tok) * a.hkv + g) * 128 + ch);
+  // keys: stage the 32 x 128 tile (8 channels per 16-byte load), per-channel
+  // min/max over the 32 tokens
+  for (int e = t; e < 32 * 16; e += 256) {
+    const int tok = e >> 4, c8 = (e & 15) * 8;
+    float x8[8];
+    load8<T>(kb + ((i0 + tok) * a.hkv + g) * 128 + c8, x8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xs[tok][c8 + j] = x8[j];
   }
   __syncthreads();
   const int ch = t & 127, h = t >> 7;
@@ -466,9 +470,11 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
     const int tok = t >> 3, part = t & 7;
     float x[16];
     const T* src = vb + ((i0 + tok) * a.hkv + g) * 128 + 16 * part;
-    float vmn = ldf<T>(src), vmx = vmn;
-    for (int k = 0; k < 16; ++k) {
-      x[k] = ldf<T>(src + k);
+    load8<T>(src, *reinterpret_cast<float(*)[8]>(&x[0]));
+    load8<T>(src + 8, *reinterpret_cast<float(*)[8]>(&x[8]));
+    float vmn = x[0], vmx = x[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
       vmn = fminf(vmn, x[k]);
       vmx = fmaxf(vmx, x[k]);
     }
