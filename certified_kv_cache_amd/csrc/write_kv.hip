@@ -68,6 +68,27 @@ struct RowArgs {
   const uint64_t* seed;
 };
 
+// All-reduce over the 16 lanes of a DPP row (a row holds one token's 128
+// channels, 8 per lane): rotations by 8 and 4 within the row, then the quad
+// swaps; VALU only, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kRowRor8>(v));
+  v = fmaxf(v, dpp_f<kRowRor4>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
+  return fmaxf(v, dpp_f<kQuadSwap1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kRowRor8>(v);
+  v += dpp_f<kRowRor4>(v);
+  v += dpp_f<kQuadSwap2>(v);
+  return v + dpp_f<kQuadSwap1>(v);
+}
+
 // Quantize the 8 channels of one lane; returns codes packed little-endian
 // in two words (INT8: offset binary code + 128) and the residual r = x^ - x.
 // words[w] holds the draws of channels 8 lane16 + 2w (low half) and + 1.
@@ -108,22 +129,20 @@ __device__ __forceinline__ void quant8(const float (&x)[8], float s, float inv, 
     float xr;
     if (SCHEME == WC_DITHER_INT8) {
       const uint32_t k16 = (i & 1) ? (words[i >> 1] >> 16) : (words[i >> 1] & 0xFFFFu);
-      const float xi = (float)k16 * 1.52587890625e-05f - 0.5f;   // exact
-      float q;
-      if (s == 0.0f) {
-        q = 0.0f;
-      } else {
-        const float y = add_rn(mul_rn(x[i], inv), xi);
-        q = fminf(fmaxf(rintf(y), -128.0f), 127.0f);
-      }
-      xr = s == 0.0f ? -x[i] : fmaf(s, q - xi, -x[i]);   // q - xi exact; one rounding
+      const float xi = fmaf((float)k16, 1.52587890625e-05f, -0.5f);   // exact
+      // an all-zero row has s = inv = 0: y = xi in [-1/2, 1/2) rounds to 0
+      // and the residual below is -x = 0, so no case of its own is needed
+      const float y = add_rn(mul_rn(x[i], inv), xi);
+      float q = __builtin_amdgcn_fmed3f(rintf(y), -128.0f, 127.0f);
+      xr = fmaf(s, q - xi, -x[i]);              // q - xi exact; one rounding
       if ((exact >> i) & 1u) {
         q = 0.0f;
         xr = 0.0f;
       }
       code = (uint32_t)((int32_t)q + 128);
     } else if (SCHEME == WC_RTN_INT8) {
-      const float q = s == 0.0f ? 0.0f : fminf(fmaxf(rintf(mul_rn(x[i], inv)), -128.0f), 127.0f);
+      // (s = inv = 0 on an all-zero row gives code 0 and residual 0 as well)
+      const float q = __builtin_amdgcn_fmed3f(rintf(mul_rn(x[i], inv)), -128.0f, 127.0f);
       code = (uint32_t)((int32_t)q + 128);
       xr = fmaf(s, q, -x[i]);                   // one rounding
     } else {
@@ -159,8 +178,7 @@ __device__ __forceinline__ RowQ quant_row(const T* kin, const T* vin, int64_t in
     float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) am = fmaxf(am, ((ex >> k) & 1u) ? 0.0f : fabsf(x[k]));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, shfl_xor(am, m));
+    am = row16_max(am);
     float s = 0.0f, inv = 0.0f;
     if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && am > 0.0f) {
       s = div_rn(am, 127.0f);
@@ -173,15 +191,14 @@ __device__ __forceinline__ RowQ quant_row(const T* kin, const T* vin, int64_t in
 #pragma unroll
     for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
     if (!isv) {
-      const float tot = ss + shfl_xor(ss, 8);
+      const float tot = ss + dpp_f<kRowRor8>(ss);   // lanes l, l + 8: the two halves of band l % 8
       o.w = sqrtf(tot) * kWitnessGuard;
       o.kp[0] = packed[0];
       o.kp[1] = packed[1];
       o.ks = s;
     } else {
       // value witness ||v^ - v|| over the row's 128 channels (16-lane sum)
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) ss += shfl_xor(ss, m);
+      ss = row16_sum(ss);
       o.wv = sqrtf(ss) * kWitnessGuard;
       o.vp[0] = packed[0];
       o.vp[1] = packed[1];
@@ -229,7 +246,7 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
   if (SCHEME == WC_DITHER_INT8) {
     const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
+    for (int w = 0; w < 4; ++w) words[w] = pcg_out_sdwa((key + (uint32_t)(64 * p + 4 * lane16 + w)) * kPcgMul + kPcgInc);
   }
   const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
   if (!live) return;
@@ -287,7 +304,7 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
   if (SCHEME == WC_DITHER_INT8) {
     const uint32_t key = stream_key(a.seed[pi], (uint32_t)layer, (uint32_t)g);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) words[w] = pcg(key + (uint32_t)(64 * p + 4 * lane16 + w));
+    for (int w = 0; w < 4; ++w) words[w] = pcg_out_sdwa((key + (uint32_t)(64 * p + 4 * lane16 + w)) * kPcgMul + kPcgInc);
   }
   const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
   constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
@@ -360,8 +377,7 @@ __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __res
     ss = fmaf(r, r, ss);
   }
   if (VAL) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) ss += shfl_xor(ss, m);
+    ss = row16_sum(ss);
     if (live && lane16 == 0) {
       const int64_t slot = a.slot[i];
       const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
@@ -369,7 +385,7 @@ __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __res
     }
     return;
   }
-  const float tot = ss + shfl_xor(ss, 8);
+  const float tot = ss + dpp_f<kRowRor8>(ss);
   if (live && lane16 < 8) {
     const int64_t slot = a.slot[i];
     const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
