@@ -1175,6 +1175,53 @@ __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ par
   }
 }
 
+// The merge for at most 16 splits in one round of loads: lane s < n_split
+// reads split s's scalars, every lane reads its two output channels of
+// every split, all before the first wait; the maxima and sums over the
+// splits are DPP reductions within the first 16 lanes.
+__global__ void __launch_bounds__(64) merge16_kernel(const float* __restrict__ part, int n_split, float* o,
+                                                     float* lse, float* meter_a, float* meter_b, float* tanh_a,
+                                                     float* tanh_b, float* meter_v) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const float* pp = part + (int64_t)bh * n_split * kPartial;
+  float2 v[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    v[s] = s < n_split ? *reinterpret_cast<const float2*>(pp + s * kPartial + 4 + 2 * lane) : make_float2(0.f, 0.f);
+  const bool mine = lane < n_split;
+  const float4 q = mine ? *reinterpret_cast<const float4*>(pp + lane * kPartial) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+  const float4 cm = mine ? *reinterpret_cast<const float4*>(pp + lane * kPartial + 132) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // lanes 16 .. 63 hold -inf and zeros: the row-0 reductions are the totals
+  const float M = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_max(q.x))));
+  const float w = (q.x == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(q.x - M);
+  const float L = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_sum(w * q.y))));
+  const float NA = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_sum(w * q.z))));
+  const float NB = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_sum(w * q.w))));
+  const float NV = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_sum(w * cm.z))));
+  const float CA = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_max(cm.x))));
+  const float CB = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_max(cm.y))));
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    if (s < n_split) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+      o0 = fmaf(ws, v[s].x, o0);
+      o1 = fmaf(ws, v[s].y, o1);
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *reinterpret_cast<float2*>(o + (int64_t)bh * 128 + 2 * lane) = make_float2(o0 * inv, o1 * inv);
+  if (lane == 0) {
+    lse[bh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    const float ea = NA * inv, eb = NB * inv;
+    if (meter_a) meter_a[bh] = ea * (1.0f + 0.5f * ea);
+    if (meter_b) meter_b[bh] = eb * (1.0f + 0.5f * eb);
+    if (tanh_a) tanh_a[bh] = tanhf(0.5f * CA);
+    if (tanh_b) tanh_b[bh] = tanhf(0.5f * CB);
+    if (meter_v) meter_v[bh] = NV * inv;
+  }
+}
+
 }  // namespace wc
 
 using namespace wc;
@@ -1333,7 +1380,11 @@ extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, f
     return WC_EINVAL;
   }
   if (B == 0) return WC_OK;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split, o,
-                     lse, meter_a, meter_b, tanh_a, tanh_b, meter_v);
+  if (n_split <= 16)
+    hipLaunchKernelGGL(merge16_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split,
+                       o, lse, meter_a, meter_b, tanh_a, tanh_b, meter_v);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(B * Hq)), dim3(64), 0, (hipStream_t)stream, partials, n_split, o,
+                       lse, meter_a, meter_b, tanh_a, tanh_b, meter_v);
   return check_launch("wc_lse_merge");
 }

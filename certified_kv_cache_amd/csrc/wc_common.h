@@ -69,4 +69,24 @@ constexpr float kWitnessGuard = 1.0f + 7.62939453125e-06f;
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// All-reduce over the 16 lanes of a DPP row: rotations by 8 and 4 within
+// the row, then the quad swaps; VALU only, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kRowRor8>(v));
+  v = fmaxf(v, dpp_f<kRowRor4>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
+  return fmaxf(v, dpp_f<kQuadSwap1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kRowRor8>(v);
+  v += dpp_f<kRowRor4>(v);
+  v += dpp_f<kQuadSwap2>(v);
+  return v + dpp_f<kQuadSwap1>(v);
+}
+
 }  // namespace wc

@@ -68,27 +68,6 @@ struct RowArgs {
   const uint64_t* seed;
 };
 
-// All-reduce over the 16 lanes of a DPP row (a row holds one token's 128
-// channels, 8 per lane): rotations by 8 and 4 within the row, then the quad
-// swaps; VALU only, no LDS round trip.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<kRowRor8>(v));
-  v = fmaxf(v, dpp_f<kRowRor4>(v));
-  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
-  return fmaxf(v, dpp_f<kQuadSwap1>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<kRowRor8>(v);
-  v += dpp_f<kRowRor4>(v);
-  v += dpp_f<kQuadSwap2>(v);
-  return v + dpp_f<kQuadSwap1>(v);
-}
-
 // Quantize the 8 channels of one lane; returns codes packed little-endian
 // in two words (INT8: offset binary code + 128) and the residual r = x^ - x.
 // words[w] holds the draws of channels 8 lane16 + 2w (low half) and + 1.
