@@ -18,10 +18,11 @@
 //   QK   S^T[token][head] = Khat[token][:] . Q'[head][:]   (MFMA 16x16x32 f16)
 //        A = key codes of token n, channels 32k..32k+31 (one 32 B load);
 //        B = the scaled query of head n, same channels.  The dequantized key
-//        is s_t (code - xi) with xi = h 2^-8 + l 2^-16 (h in [-128,127],
-//        l in [0,255] the two bytes of the 16-bit draw): three MFMAs on exact
-//        fp16 integers (code, h, l) against one fp16 query, so the products
-//        are exact and only the fp32 accumulation rounds.
+//        is s_t (code - xi) with xi = hb 2^-8 + lb 2^-16 - 1/2 (hb, lb the
+//        two bytes of the 16-bit draw): three MFMAs into one accumulator on
+//        exact fp16 operands (the code, -(4 + hb 2^-8), -(2^-6 + lb 2^-16))
+//        against one fp16 query, so the products are exact and only the fp32
+//        accumulation rounds.
 //   D    lane (n, k) holds tokens 4k..4k+3 of head n: softmax, both meter
 //        tiers and the block risk stay lane-local up to 4-lane reductions.
 //   PV   O^T[channel][head] += Vhat^T[channel][token] . P^T[token][head]
@@ -70,8 +71,10 @@ __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, 
 __device__ __forceinline__ h2 make_h2(_Float16 a, _Float16 b) { return h2{a, b}; }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// fp16 bit pattern 0x64XX is 1024 + XX exactly.
+// fp16 bit pattern 0x64XX is 1024 + XX exactly; 0xC4XX is -(4 + XX 2^-8) and
+// 0xA4XX is -(2^-6 + XX 2^-16): a byte spliced under a fixed exponent.
 constexpr uint32_t kMagic = 0x64646464u;
+constexpr uint32_t kMagicHiNeg = 0xC4C4C4C4u, kMagicLoNeg = 0xA4A4A4A4u;
 
 // Four INT8 codes stored as offset binary (code + 128, one word) -> two fp16
 // pairs of the exact integers: splice under the 1024 exponent, subtract 1152.
@@ -553,8 +556,9 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   // Tier A operands of the two fp32 MFMAs: K slot k <-> bands 2k and 2k+1
   const float bA0 = hv ? beta[2 * kq] : 0.0f, bA1 = hv ? beta[2 * kq + 1] : 0.0f;
   const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // log2-unit logit per raw unit
-  // the high and low dither bytes enter the key MFMAs as 1152 + h and
-  // 1024 + l; scaled by -2^-8 and -2^-16 their bias is -qsum (4.5 + 2^-6)
+  // the dither bytes enter the key MFMAs as -(4 + hb 2^-8) and
+  // -(2^-6 + lb 2^-16); with xi = hb 2^-8 + lb 2^-16 - 1/2 the chain's start
+  // value qsum (4.5 + 2^-6) leaves sum q' (code - xi)
   const float qbias = qsum * 4.515625f;
   const f4 kb4 = SCHEME == WC_DITHER_INT8 ? f4{qbias, qbias, qbias, qbias} : f4{0.f, 0.f, 0.f, 0.f};
   const float logterm = logf(2.0f * (float)S) + a.neg_log_dloc;
@@ -573,7 +577,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const float qs2c = CMP ? dpp_shr8_hi(qs2, qs2) : qs2;
   const float kappac = CMP ? dpp_shr8_hi(kappa, kappa) : kappa;
   // Per-wave LDS tile of the page's dither high bytes as fp16 operands
-  // (1024 + byte): the key side (lane = token) hashes each draw once and
+  // -(4 + byte 2^-8): the key side (lane = token) hashes each draw once and
   // stores [token][8-channel group]; the value side (lane = channel group)
   // reads four tokens back.  Rows are padded to 17 slots so that neither
   // side's 16 lanes of one instruction share a bank.  The space is the
@@ -663,20 +667,21 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     }
 
     // ---------------- QK^T: three MFMA chains over 128 channels
-    f4 Dc = zero4, Dh = zero4, Dl = zero4;
+    f4 Dc = zero4;
     float st[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     // LCG state of the lane's first counter, key + 64 token + 16 k; the
     // other 15 counters are consecutive (their states differ by constants)
     const uint32_t st0 = (key + (uint32_t)(64 * (tok0 + n) + 16 * kq)) * kPcgMul + kPcgInc;
-    // draws of token n, channels 32k + 8j .. +7, as fp16 pairs 1024 + high byte
-    // (= 1152 + h) and 1024 + low byte; published to LDS for the values
+    // draws of token n, channels 32k + 8j .. +7, as fp16 pairs -(4 + hb 2^-8)
+    // and -(2^-6 + lb 2^-16) of the high and low byte; the high ones are
+    // published to LDS for the values
     auto draws = [&](int j, uint32_t (&hh)[4], uint32_t (&ll)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t wd = pcg_out_sdwa(st0 + (uint32_t)(4 * j + e) * kPcgMul);
-        hh[e] = perm(kMagic, wd, 0x04030401u);
-        ll[e] = perm(kMagic, wd, 0x04020400u);
+        hh[e] = perm(kMagicHiNeg, wd, 0x04030401u);
+        ll[e] = perm(kMagicLoNeg, wd, 0x04020400u);
       }
       sH[n][4 * kq + j] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
     };
@@ -705,17 +710,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
           fp8_to_h(kw[2 * j + 1], c2, c3);
         }
         const h8 Ac = make_h8(c0, c1, c2, c3);
-        // the code chain starts from the byte-bias correction (INT8)
+        // the chain starts from the cancellation of the byte offsets (INT8)
         Dc = mfma32(Ac, Qhi[j], j == 0 ? kb4 : Dc);
         if (QF32) Dc = mfma32(Ac, Qlo[j], Dc);
         if (SCHEME == WC_DITHER_INT8) {
           const h8 Ah = make_h8(hh[0], hh[1], hh[2], hh[3]);
           const h8 Al = make_h8(ll[0], ll[1], ll[2], ll[3]);
-          Dh = mfma32(Ah, Qhi[j], j == 0 ? zero4 : Dh);
-          Dl = mfma32(Al, Qhi[j], j == 0 ? zero4 : Dl);
+          Dc = mfma32(Ah, Qhi[j], Dc);
+          Dc = mfma32(Al, Qhi[j], Dc);
           if (QF32) {
-            Dh = mfma32(Ah, Qlo[j], Dh);
-            Dl = mfma32(Al, Qlo[j], Dl);
+            Dc = mfma32(Ah, Qlo[j], Dc);
+            Dc = mfma32(Al, Qlo[j], Dc);
           }
         }
       }
@@ -767,14 +772,8 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       H2 = sH[4 * kq + 2][n];
       H3 = sH[4 * kq + 3][n];
     }
-    // raw = sum q' (code - h 2^-8 - l 2^-16); the chain's start value cancels the byte biases
-    float raw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // (a repaired block left Dh, Dl and the start value at zero: raw = Dc exactly)
-      raw[r] = Dc[r];
-      if (SCHEME == WC_DITHER_INT8) raw[r] = fmaf(Dh[r], -0.00390625f, fmaf(Dl[r], -1.52587890625e-05f, raw[r]));
-    }
+    // raw = sum q' (code - xi) (a repaired block: sum q' k of the exact keys)
+    float raw[4] = {Dc[0], Dc[1], Dc[2], Dc[3]};
     float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
     float lo2[4] = {Do[0], Do[1], Do[2], Do[3]};
     if (CMP) {                                 // lanes n + 8 take tokens 2, 3 of head n
@@ -929,10 +928,12 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     }
     const uint32_t vw[8] = {vl.v0.x, vl.v0.y, vl.v0.z, vl.v0.w, vl.v1.x, vl.v1.y, vl.v1.z, vl.v1.w};
     if (SCHEME == WC_DITHER_INT8) {
-      // Vhat = s (code - (h - 128) 2^-8 - l 2^-16): one 16x16x32 MFMA per channel
-      // tile takes the four codes and the four exact (128 - h) / 256 of the
-      // lane's tokens against P^T twice over; the low byte l enters through its
-      // mean 255/2 (its spread moves an output by < 2^-9 of one code step).
+      // Vhat = s (code - hb 2^-8 - lb 2^-16 + 1/2): one 16x16x32 MFMA per
+      // channel tile takes the four codes and the four exact -(4 + hb 2^-8) of
+      // the lane's tokens (the key side's LDS tile as it stands) against P^T
+      // twice over; the 4 + 1/2 and the low byte, through its mean 255/2 (its
+      // spread moves an output by < 2^-9 of one code step), are added once
+      // after the loop from the sum of the weights.
       const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
       vsum = __builtin_amdgcn_fdot2(make_h2(Bc[0], Bc[1]), ones, vsum, false);
       vsum = __builtin_amdgcn_fdot2(make_h2(Bc[2], Bc[3]), ones, vsum, false);
@@ -940,19 +941,14 @@ decode_kernel(wc_cache c, DecodeArgs a) {
                             as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])));
       const uint32_t h0w[4] = {H0.x, H0.y, H0.z, H0.w}, h1w[4] = {H1.x, H1.y, H1.z, H1.w};
       const uint32_t h2w[4] = {H2.x, H2.y, H2.z, H2.w}, h3w[4] = {H3.x, H3.y, H3.z, H3.w};
-      const h2 km = {(_Float16)-0.00390625f, (_Float16)-0.00390625f};
-      const h2 kb = {(_Float16)4.5f, (_Float16)4.5f};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        // channel 8n + t: half (t % 2) of word t / 2 of each token's group;
-        // (1024 + h) (-2^-8) + 4.5 = (128 - h) / 256 exactly
+        // channel 8n + t: half (t % 2) of word t / 2 of each token's group
         const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
         const int w = t >> 1;
         uint32_t c0, c1;
         codes_to_h(vw[t], c0, c1);
-        const uint32_t ha = as_u32(__builtin_elementwise_fma(as_h2(perm(h1w[w], h0w[w], sel)), km, kb));
-        const uint32_t hb = as_u32(__builtin_elementwise_fma(as_h2(perm(h3w[w], h2w[w], sel)), km, kb));
-        O[t] = mfma32(make_h8(c0, c1, ha, hb), B2, O[t]);
+        O[t] = mfma32(make_h8(c0, c1, perm(h1w[w], h0w[w], sel), perm(h3w[w], h2w[w], sel)), B2, O[t]);
       }
     } else if (SCHEME == WC_BF16_STORE) {
       // [V|V] . [P_hi|P_lo]: tokens 4k..4k+3 of channel 8n + t twice, against
@@ -1025,10 +1021,10 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     }
   }
   const float m_run = m_ref;
-  if (SCHEME == WC_DITHER_INT8) {                // the low bytes' mean 255/2 times 2^-16
-    const float vb = sum4k(vsum) * 0.0019454956054688f;
+  if (SCHEME == WC_DITHER_INT8) {                // 4 + 1/2 - (255/2) 2^-16 per unit of weight
+    const float vb = sum4k(vsum) * 4.49805450439453125f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) O[t] -= vb;
+    for (int t = 0; t < 8; ++t) O[t] += vb;
   }
 
   // ---------------------------------------------------------------- combine waves
