@@ -817,7 +817,8 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       lmax = vmax(lmax, vmax(l2[2], l2[3]));
       svmax = vmax(svmax, vmax(sv[2], sv[3]));
     }
-    const bool need = lmax > m_ref + kRescaleSlack || (svmax > 128.0f && lmax > m_ref);
+    // (bitwise, so that the test compiles to compares and mask logic, not branches)
+    const bool need = (lmax > m_ref + kRescaleSlack) | ((svmax > 128.0f) & (lmax > m_ref));
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       float tmax = lmax, anyn = need ? 1.0f : 0.0f;
       if (CMP) {
@@ -861,18 +862,28 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       for (int r = 0; r < NV; ++r)
         cmin = min(cmin, min(__float_as_uint(cA[r]) - 1u, __float_as_uint(cB[r]) - 1u));
       const bool tiny = cmin < 0x3C7FFFFFu;
+      // (the sums start from the first token's term: a 0.0f start value
+      // would cost an add, since 0 + (-0) is not -0)
+      float ta[NV], tb[NV];
       if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
         for (int r = 0; r < NV; ++r) {
-          ea += __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
-          if (meterB) eb += __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r];
+          ta[r] = __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
+          tb[r] = meterB ? __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r] : 0.0f;
         }
       } else {
 #pragma unroll
         for (int r = 0; r < NV; ++r) {
-          ea += fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
-          if (meterB) eb += fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f);
+          ta[r] = fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
+          tb[r] = meterB ? fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f) : 0.0f;
         }
+      }
+      ea = ta[0];
+      eb = tb[0];
+#pragma unroll
+      for (int r = 1; r < NV; ++r) {
+        ea += ta[r];
+        eb += tb[r];
       }
       na += ea;
       nb += eb;
