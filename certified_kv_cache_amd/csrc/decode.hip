@@ -1279,7 +1279,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
                                     const uint64_t* seed, float sm_scale, unsigned meter_mask, double delta_req,
                                     int L, int H, int T, int n_split, float* partials, size_t ws_bytes,
                                     float* block_logrisk, void* stream) {
-  if (!cache || !q || !page_table || !ctx_len || !partials) {
+  if (!cache || (B != 0 && (!q || !page_table || !ctx_len || !partials))) {
     set_error("wc_decode_attn_meter: null pointer");
     return WC_EINVAL;
   }
@@ -1326,7 +1326,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: WC_BLOCK_CMAX needs the block output");
     return WC_EINVAL;
   }
-  if (c.scheme == WC_DITHER_INT8 && (!seed || !c.k_scale || !c.v_scale)) {
+  if (c.scheme == WC_DITHER_INT8 && ((!seed && B != 0) || !c.k_scale || !c.v_scale)) {
     set_error("wc_decode_attn_meter: INT8 cache needs seeds and scales");
     return WC_EINVAL;
   }
@@ -1382,7 +1382,7 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
 extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,
                             float* meter_a, float* meter_b, float* tanh_a, float* tanh_b, float* meter_v,
                             void* stream) {
-  if (!partials || !o || !lse || B < 0 || Hq < 1 || n_split < 1 || n_split > 1024) {
+  if ((B != 0 && (!partials || !o || !lse)) || B < 0 || Hq < 1 || n_split < 1 || n_split > 1024) {
     set_error("wc_lse_merge: bad arguments");
     return WC_EINVAL;
   }

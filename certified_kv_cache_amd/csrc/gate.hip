@@ -423,6 +423,7 @@ int gate_prepare(const char* fn, const wc_cache* cache, int layer, int B, int Hq
     set_error("%s: bad B/Hq/max_pages (<= %d)/layer", fn, kMaxSortPages);
     return WC_EINVAL;
   }
+  if (B == 0) return WC_OK;                    // nothing to do (the caller returns too)
   if (ws_bytes < wc_gate_workspace_bytes(B, c.num_kv_heads, max_pages)) {
     set_error("%s: workspace too small", fn);
     return WC_EWORKSPACE;
@@ -454,8 +455,8 @@ extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float
                                    int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
                                    int64_t* bytes_paged, int32_t* selected, void* workspace, size_t ws_bytes,
                                    void* stream) {
-  if (!cache || !block_cmax || !page_table || !ctx_len || !host_exact_k || !pool_used || !bytes_paged ||
-      !workspace) {
+  if (!cache || (B != 0 && (!block_cmax || !page_table || !ctx_len || !host_exact_k || !pool_used || !bytes_paged ||
+                             !workspace))) {
     set_error("wc_gate_pagein_tanh: null pointer");
     return WC_EINVAL;
   }
@@ -489,8 +490,8 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
                               int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
                               int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx, void* workspace,
                               size_t ws_bytes, void* stream) {
-  if (!cache || !block_logrisk || !lse || !page_table || !ctx_len || !host_exact_k || !pool_used || !bytes_paged ||
-      !workspace) {
+  if (!cache || (B != 0 && (!block_logrisk || !lse || !page_table || !ctx_len || !host_exact_k || !pool_used ||
+                             !bytes_paged || !workspace))) {
     set_error("wc_gate_pagein: null pointer");
     return WC_EINVAL;
   }

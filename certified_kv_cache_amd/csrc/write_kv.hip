@@ -561,7 +561,7 @@ using namespace wc;
 extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
                            int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot,
                            const int32_t* pos, const uint64_t* seed, void* stream) {
-  if (!cache || !k || !v || !slot || !pos || !seed) {
+  if (!cache || (n_tok != 0 && (!k || !v || !slot || !pos || !seed))) {
     set_error("wc_write_kv: null pointer");
     return WC_EINVAL;
   }
@@ -679,7 +679,7 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
 extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers, const void* k, const void* v,
                                  int in_dtype, int64_t n_pages, int64_t layer_stride, const int32_t* pages,
                                  const int32_t* pos0, const uint64_t* seed, void* stream) {
-  if (!cache || !k || !v || !pages || !pos0 || !seed) {
+  if (!cache || (n_pages != 0 && (!k || !v || !pages || !pos0 || !seed))) {
     set_error("wc_write_kv_pages: null pointer");
     return WC_EINVAL;
   }
@@ -748,7 +748,7 @@ extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers
 extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat,
                           int in_dtype, int64_t n_tok, int64_t layer_stride, const int64_t* slot, int values,
                           void* stream) {
-  if (!cache || !x || !xhat || !slot) {
+  if (!cache || (n_tok != 0 && (!x || !xhat || !slot))) {
     set_error("wc_witness: null pointer");
     return WC_EINVAL;
   }
@@ -828,7 +828,7 @@ extern "C" int wc_outlier_select(const void* x, int in_dtype, int n_layers, int6
 
 extern "C" int wc_dither_fill(uint64_t seed, int layer, int kv_head, int64_t pos0, int64_t n_pos, uint16_t* out,
                               void* stream) {
-  if (!out || n_pos < 0 || pos0 < 0 || pos0 + n_pos > (int64_t(1) << 26)) {
+  if ((!out && n_pos != 0) || n_pos < 0 || pos0 < 0 || pos0 + n_pos > (int64_t(1) << 26)) {
     set_error("wc_dither_fill: bad arguments");
     return WC_EINVAL;
   }

@@ -24,6 +24,9 @@
  *      WC_EUNSUPPORTED -2 (scheme/dtype/shape not built),
  *      WC_EWORKSPACE -3 (workspace too small), WC_EHIP -4 (launch error).
  *    wc_last_error() returns a text for the last failure on this thread.
+ *  - A call with nothing to do (n_tok = 0, n_pages = 0 or B = 0) checks its
+ *    other arguments and returns WC_OK without a launch; its data pointers
+ *    may then be NULL (the cache descriptor may not).
  *  - Device-resident index arrays (slots, positions, page tables, lengths)
  *    cannot be checked on the host: out-of-range values are undefined
  *    behaviour, as for any kernel argument.
