@@ -1,6 +1,6 @@
 """Benchmark of the WitCert hot path on one MI355X.
 
-Workload (the headline configuration): decode batch 32, 32768 cached tokens
+Default workload: decode batch 32, 32768 cached tokens
 per sequence, Qwen2.5-7B attention shape (28 query / 4 KV heads, d = 128),
 dithered INT8 cache paged at 16 tokens with a random page permutation,
 16 KV splits, Tier A + Tier B meter (delta_req 1e-2 over L = 28, H = 28,
@@ -149,7 +149,7 @@ def scheme_variant(w, B, S, iters, scheme):
 
 
 def vcert_variant(w, B, S, iters):
-    """The headline decode with the value certificate added (value witness
+    """The 32 x 32768 INT8 decode with the value certificate added (value witness
     stored at write time, E_V in the same pass)."""
     import torch
     L = w["L"]
@@ -508,7 +508,7 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
 
 
 def decode_bounds(B, S, iters=20):
-    """What bounds the decode: the headline launch (dithered INT8 with block
+    """What bounds the decode: the 32 x 32768 launch (dithered INT8 with block
     risks, and meter off; fp8 raw cast the same) with its random page table,
     and again with every page-table entry folded into 64 physical pages, so
     that the cache the launch reads stays in L2 and the time is the kernel's
@@ -658,7 +658,7 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill-write", "gate-flow", "gate-compare", "latency", "decode-bounds"],
-                    help="decode: the headline line (default); prefill-write: the 28-layer write path per scheme; "
+                    help="decode: the 32 x 32768 decode step line (default); prefill-write: the 28-layer write path per scheme; "
                          "gate-flow: a ragged 64-sequence fp8 decode with the gate over several steps; "
                          "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate; "
                          "latency: decode + merge latency at the two parity sizes; "
@@ -666,8 +666,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU; the path shards without communication "
-              "(see the design notes), so --gpus must be 1", file=sys.stderr)
+        print("bench.py: runs on one GPU (sequences and KV heads shard without communication), "
+              "so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -4,7 +4,7 @@ WitCert (m.montaan.com summary, Tier B paragraph) quantizes with subtractive
 dither x^ = s(round(x/s + xi) - xi), xi ~ U[-1/2, 1/2), and regenerates xi
 deterministically when the cache is read instead of storing it; the draw is
 a counter hash of (seed, layer, head, token, channel).  The pages do not fix
-the generator.  Reading used here (stated in the design doc):
+the generator.  Reading used here:
 
 * The generator is the ``pcg`` hash published by Jarzynski and Olano,
   "Hash Functions for GPU Rendering", JCGT 9(3), 2020 (an RXS-M-XS output

@@ -7,7 +7,7 @@ repairs at block granularity, zeroes the repaired witnesses, and the repair
 persists; it is risk-ranked where the witness is saturated (tau >= 1) and
 certified where it is informative (tau < 1).
 
-Reading (DESIGN.md): R = E (1 + E/2) <= tau  <=>  E <= E_tau = sqrt(1 + 2 tau) - 1,
+Reading: R = E (1 + E/2) <= tau  <=>  E <= E_tau = sqrt(1 + 2 tau) - 1,
 so the gate works on E.  Per (sequence, KV head) with its G query heads:
 
 1. rho_fx[h, j] = ceil(rho[h, j] * 2**40), capped at 2**47, where rho[h, j]

@@ -27,7 +27,7 @@ Sources (WitCert pages):
   two ends of the range), so TV <= tanh(max_t c_t / 2).  It is evaluated per
   tier: with Tier A's c it is deterministic (delta = 0).
 
-Readings (the design doc lists them):
+Readings taken where the pages leave a step open:
 
 * Logits are l_t = sm_scale * q . k_t; the pages' 1/sqrt(d) is sm_scale, and
   both tiers scale with sm_scale (they reduce to the pages at sm_scale =

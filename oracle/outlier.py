@@ -9,7 +9,7 @@ Sources (WitCert pages):
 * Summary, Tier B paragraph: the variance proxy sums q_c^2 s_{c,t}^2 over
   channels, so a channel whose stored key is exact (s_{c,t} = 0) drops out.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
 
 * The bypass set O of one (layer, KV head) is the m channels of largest
   energy E_c = sum_t k_{t,c}^2 over a calibration batch of its keys (the

@@ -15,7 +15,7 @@ Sources (WitCert pages):
   same witness of its residual (summary implementation paragraph; the
   abstract's scheme registration).
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 
 * Scale per (token, KV head) row: s = absmax/127 and the reciprocal
   inv_s = 127/absmax, both correctly rounded float32 divisions; x/s is

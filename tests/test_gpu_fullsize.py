@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the headline workloads.
+"""GPU parity at the full sizes of the benchmark workloads.
 
 * decode: batch 32 x 32768 tokens, 28 query / 4 KV heads, 16 KV splits, block
   risks on -- the launch configuration bench.py times -- for the dithered INT8
