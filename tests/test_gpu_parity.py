@@ -1,8 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
 Bars: codes, dither draws and gate decisions bit-exact; witness and meters
-within 1e-4 relative; attention output within 2e-3 relative L2; and the
-GPU meter never below the oracle's true TV.
+within 1e-4 relative (Tier A's R plus the share of the witness rounding
+guard, which e^c amplifies once the meter saturates); attention output
+within 2e-3 relative L2; and the GPU meter never below the oracle's true TV.
 """
 import math
 
@@ -84,6 +85,11 @@ def test_write_codes_bit_exact_and_witness(scheme, dtype):
                 ks = H.gather_rows(sc.cache.k_scale.cpu().numpy(), sc.layer, sc.tab[b], S, g)
                 vs = H.gather_rows(sc.cache.v_scale.cpu().numpy(), sc.layer, sc.tab[b], S, g)
                 assert np.array_equal(ks, oc["sk"]) and np.array_equal(vs, oc["sv"])
+    # the same cache decoded with the query in the input dtype (fp32 queries
+    # take the kernels' hi/lo split operand)
+    for n_split in (1, 3):
+        out = sc.decode(n_split=n_split, mask=3 if scheme == "int8" else 1)
+        _check_decode(sc, out)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -145,7 +151,15 @@ def _check_decode(sc, out, n_check=None):
             assert np.all(err <= OUT_TOL), (b, g, err.max())
             assert np.all(np.abs(out["lse"][b, hs] - r["lse"]) <= 1e-4 * np.maximum(1, np.abs(r["lse"]))), (b, g)
             ra = out["R_A"][b, hs]
-            assert np.all(np.abs(ra - r["R_A"]) <= MET_TOL * r["R_A"]), (b, g, ra, r["R_A"])
+            # The stored witness is the band norm rounded up by 1 + 2^-17 (the
+            # soundness guard of the write path) plus fp32 rounding (< 2^-20):
+            # every Tier A bound c_t rises by at most that fraction, which e^c
+            # turns into 2 (e^{c_max (2^-17 + 2^-20)} - 1) relative in
+            # R = E (1 + E/2).  Informative meters (small c) keep the 1e-4 bar;
+            # saturated ones (R >> 1, TV bound 1) get the guard's share on top.
+            guard = 2.0 * np.expm1((2.0**-17 + 2.0**-20) * r["a"].max(axis=1))
+            assert np.all(np.abs(ra - r["R_A"]) <= (MET_TOL + guard) * r["R_A"]), (b, g, ra, r["R_A"])
+            assert np.all(ra >= r["R_A"] * (1 - MET_TOL)), (b, g)
             assert np.all(ra >= r["tv_true"]), (b, g)
             # the tanh bound of Tier A: deterministic, sound
             ta = out["T_A"][b, hs]
