@@ -151,6 +151,20 @@ def test_gate_at_the_sort_capacity():
         assert np.all(dev <= 2e-4 * ref + 1), (g, (dev - 1).max())
     assert used == total and paged == 4096 * total
     print(f"selected {total} blocks", flush=True)
+    # the tanh gate ranks the same 4096 pages (a fresh cache of the same input)
+    L, sc, host = _setup(lens, seed=41, capacity=16384)
+    out = sc.decode(n_split=4, mask=1, cmax=True)
+    cm = out["cmax"]
+    tau = float(np.median(out["T_A"]))
+    rep0 = sc.cache.exact_slot.cpu().numpy()[sc.layer].copy()
+    sel, used, paged = _tanh_gate(L, sc, host, cm, tau)
+    total = 0
+    for g in range(4):
+        want = gate.select_tanh(cm[0, g * 7:(g + 1) * 7, :4096], rep0[sc.tab[0], g] >= 0, tau)
+        assert list(sel[0, g, 1:1 + sel[0, g, 0]]) == want, g
+        total += len(want)
+    assert used == total and paged == 4096 * total
+    print(f"tanh gate selected {total} blocks", flush=True)
 
 
 def test_gate_budget_and_pool_capacity():
