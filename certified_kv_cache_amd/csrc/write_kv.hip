@@ -34,20 +34,25 @@ int check_launch(const char* what) {
   return WC_OK;
 }
 
+// Inputs are read once and code blocks written once: their accesses carry
+// the non-temporal cache policy (native vector types, which the builtins take).
+typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&x)[8]);
 
 template <>
 __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-  float4 a = *reinterpret_cast<const float4*>(p);
-  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const nt_f4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p));
+  const nt_f4 b = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p + 4));
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
 template <>
 __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
-  uint4 a = *reinterpret_cast<const uint4*>(p);
+  const nt_u4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
   uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -303,7 +308,8 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
   __syncthreads();
   const int t = threadIdx.x & 127;
   uint8_t* dst = reinterpret_cast<uint8_t*>(threadIdx.x < 128 ? c.k_codes : c.v_codes) + pg * 2048 + 16 * t;
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((threadIdx.x < 128 ? sK : sV) + 16 * t);
+  __builtin_nontemporal_store(*reinterpret_cast<const nt_u4*>((threadIdx.x < 128 ? sK : sV) + 16 * t),
+                              reinterpret_cast<nt_u4*>(dst));
 }
 
 // 16-bit store: the scheme's outputs (bf16) copied into the decode layouts,
