@@ -226,10 +226,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + off), (short)0,
                                            bytes, kRsrcFlags);
 }
-// Every page of the cache is read once per decode: its loads carry the
-// non-temporal cache policy (2), so they stream through L2 instead of
-// displacing lines that are reused (3-7% faster than the default policy on
-// the 32 x 32768 decode).
+// Every page of the cache is read once per decode: the 16-byte code loads
+// carry the non-temporal cache policy (2), so they stream through L2 instead
+// of displacing lines that are reused.  The 8-byte loads (scales and
+// witnesses with the compacted softmax) keep the default policy: one line
+// holds several page-heads' entries, read by different workgroups, and a
+// streamed line is fetched again for each (8% faster than the default policy
+// everywhere on the 32 x 32768 decode, 5% faster than streaming everything).
 constexpr int kStream = 2;
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream));
@@ -313,7 +316,7 @@ __device__ __forceinline__ uint4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kStream));
 }
 __device__ __forceinline__ float2 bload8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
-  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kStream));
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
 __device__ __forceinline__ uint32_t bload4s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kStream);
