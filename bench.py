@@ -425,19 +425,20 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
                                              for b, S_ in enumerate(lens0)])).to(dev)
     pos0 = torch.from_numpy(np.concatenate([np.arange(S_) for S_ in lens0]).astype(np.int32)).to(dev)
     tseed0 = seeds_d.repeat_interleave(torch.from_numpy(lens0).to(dev))
-    host = torch.empty((n_layers, npages, HKV, 16, D), dtype=torch.bfloat16, pin_memory=True)
+    # the exact host store holds the keys of the tokens written so far: the
+    # prefix now, each appended token when it is written (a repair copies the
+    # rows of its block that exist; the write path keeps the pool rows of
+    # tokens appended later)
+    host = torch.zeros((n_layers, npages, HKV, 16, D), dtype=torch.bfloat16, pin_memory=True)
     layer_kv = []
-    for layer in range(n_layers):                      # per-layer K/V, its exact keys to the host store
+    for layer in range(n_layers):                      # per-layer K/V, the prefix's exact keys to the host store
         k, v = inputs.ragged_kv_torch(seed * 100 + layer, cap, Hkv=HKV)
-        store = torch.zeros((npages, HKV, 16, D), dtype=torch.bfloat16, device=dev)
         starts = np.concatenate([[0], np.cumsum(cap)[:-1]])
-        idx = torch.from_numpy(np.concatenate([starts[b] + np.arange(S_) for b, S_ in enumerate(cap)])).to(dev)
-        slot_all = torch.from_numpy(np.concatenate([tab[b, np.arange(S_) // 16].astype(np.int64) * 16 +
-                                                    np.arange(S_) % 16 for b, S_ in enumerate(cap)])).to(dev)
-        store[slot_all // 16, :, slot_all % 16, :] = k[idx]
+        first = torch.from_numpy(np.concatenate([starts[b] + np.arange(S_) for b, S_ in enumerate(lens0)])).to(dev)
+        store = torch.zeros((npages, HKV, 16, D), dtype=torch.bfloat16, device=dev)
+        store[slot0 // 16, :, slot0 % 16, :] = k[first]
         host[layer].copy_(store)
         del store
-        first = torch.from_numpy(np.concatenate([starts[b] + np.arange(S_) for b, S_ in enumerate(lens0)])).to(dev)
         later = [torch.from_numpy(starts + lens0 + s).to(dev) for s in range(n_steps)]
         layer_kv.append((k[first].contiguous(), v[first].contiguous(),
                          [(k[i].contiguous(), v[i].contiguous()) for i in later]))
@@ -461,6 +462,10 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
         for layer in range(n_layers):
             kf, vf, _ = layer_kv[layer]
             L.wc_write_kv(cache, kf, vf, slot0, pos0, tseed0, layer0=layer)
+        for s in range(n_steps):                       # the appended tokens are not in the host store yet
+            t_ = lens0 + s
+            sl = torch.from_numpy(tab[np.arange(NB), t_ // 16].astype(np.int64) * 16 + t_ % 16)
+            host[:, sl // 16, :, sl % 16, :] = 0
         pool_used = torch.zeros(1, dtype=torch.int64, device=dev)
         paged = torch.zeros(1, dtype=torch.int64, device=dev)
         per_step, dec_us = [], []
@@ -472,9 +477,11 @@ def gate_flow(n_layers, n_steps, seed=5, NB=64, taus=(1.0, 0.2, 0.05), scheme="f
             before = int(paged.item())
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t_dec = 0.0
+            slot_h = slot.cpu()
             for layer in range(n_layers):
                 kn, vn = layer_kv[layer][2][s]
                 L.wc_write_kv(cache, kn, vn, slot, pos, seeds_d, layer0=layer)
+                host[layer][slot_h // 16, :, slot_h % 16, :] = kn.cpu()
                 a.record()
                 L.wc_decode_attn_meter(cache, layer, q, tab_d, ctx, seeds_d, part, sm,
                                        mask | (L.WC_BLOCK_CMAX if kind == "tanh" else 0), DELTA[0], *DELTA[1:],

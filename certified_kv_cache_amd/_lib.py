@@ -10,8 +10,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# WITCERT_LIB may name another build of the same library (A/B timing runs)
-LIB_PATH = os.environ.get("WITCERT_LIB") or os.path.join(_HERE, "libwitcert.so")
+LIB_PATH = os.path.join(_HERE, "libwitcert.so")
 
 WC_OK, WC_EINVAL, WC_EUNSUPPORTED, WC_EWORKSPACE, WC_EHIP = 0, -1, -2, -3, -4
 WC_DITHER_INT8, WC_FP8_E4M3, WC_KIVI2, WC_RTN_INT8, WC_BF16_STORE = 0, 1, 2, 3, 4
@@ -29,7 +28,7 @@ class WcCache(ctypes.Structure):
                 ("k_codes", _c_void_p), ("v_codes", _c_void_p), ("k_scale", _c_void_p),
                 ("v_scale", _c_void_p), ("k_aux", _c_void_p), ("v_aux", _c_void_p),
                 ("witness", _c_void_p), ("exact_slot", _c_void_p), ("exact_pool", _c_void_p),
-                ("exact_scale", _c_void_p), ("pool_capacity", _i64), ("num_outliers", _i32),
+                ("pool_capacity", _i64), ("num_outliers", _i32),
                 ("reserved", _i32), ("outlier_ch", _c_void_p), ("k_outlier", _c_void_p), ("v_witness", _c_void_p)]
 
 
@@ -146,11 +145,11 @@ class KVCache:
         self.v_witness = torch.zeros(shp + (ps,), **f32) if v_witness else None
         self.pool_capacity = pool_capacity
         if pool_capacity > 0:
+            # repaired blocks' exact keys: bf16 [slot][token][128]
             self.exact_slot = torch.full(shp, -1, dtype=torch.int32, device=device)
-            self.exact_pool = torch.zeros((pool_capacity, 16, 128), dtype=torch.float16, device=device)
-            self.exact_scale = torch.zeros((pool_capacity, 16), **f32)
+            self.exact_pool = torch.zeros((pool_capacity, 16, 128), dtype=torch.bfloat16, device=device)
         else:
-            self.exact_slot = self.exact_pool = self.exact_scale = None
+            self.exact_slot = self.exact_pool = None
         # outlier bypass: channels [L][Hkv][m] (filled by wc_outlier_select or
         # the caller) and the exact bf16 keys on them [L][P][Hkv][16][m]
         self.num_outliers = num_outliers
@@ -163,7 +162,7 @@ class KVCache:
         self.desc = WcCache(scheme, 128, num_kv_heads, 8, ps, num_layers, num_pages,
                             *[t.data_ptr() if t is not None else None for t in
                               (self.k_codes, self.v_codes, self.k_scale, self.v_scale, self.k_aux,
-                               self.v_aux, self.witness, self.exact_slot, self.exact_pool, self.exact_scale)],
+                               self.v_aux, self.witness, self.exact_slot, self.exact_pool)],
                             pool_capacity, num_outliers, 0,
                             *[t.data_ptr() if t is not None else None for t in
                               (self.outlier_ch, self.k_outlier, self.v_witness)])

@@ -453,6 +453,36 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
   }
+  // The query of head n as bf16 pieces for repaired blocks (exact bf16 keys
+  // on bf16 MFMAs): one piece for a bf16 query, three that sum exactly to an
+  // fp32 one.  Staged in LDS once per workgroup (rows padded to 17 slots, so
+  // the 16 lanes of one read hit distinct banks); the repaired branch reads
+  // them per MFMA.
+  constexpr int NQP = QF32 ? 3 : 1;
+  __shared__ __align__(16) uint4 sQ[NQP][16][17];
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t pc[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a0 = __float_as_uint(qf[8 * j + 2 * e]), a1 = __float_as_uint(qf[8 * j + 2 * e + 1]);
+        const uint32_t h0 = a0 & 0xFFFF0000u, h1 = a1 & 0xFFFF0000u;
+        pc[0][e] = (h0 >> 16) | h1;
+        if (QF32) {
+          const float r0 = __uint_as_float(a0) - __uint_as_float(h0), r1 = __uint_as_float(a1) - __uint_as_float(h1);
+          const uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u, m1 = __float_as_uint(r1) & 0xFFFF0000u;
+          const uint32_t l0 = __float_as_uint(r0 - __uint_as_float(m0));
+          const uint32_t l1 = __float_as_uint(r1 - __uint_as_float(m1));
+          pc[1][e] = (m0 >> 16) | m1;
+          pc[2][e] = (l0 >> 16) | (l1 & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int pq = 0; pq < NQP; ++pq) sQ[pq][n][4 * kq + j] = make_uint4(pc[pq][0], pc[pq][1], pc[pq][2], pc[pq][3]);
+    }
+  }
+  __syncthreads();
   float qmax = 0.0f, bsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 32; ++i) bsum[i >> 3] = fmaf(qf[i], qf[i], bsum[i >> 3]);   // Tier A: the full query
@@ -733,21 +763,18 @@ decode_kernel(wc_cache c, DecodeArgs a) {
         }
       }
     } else {
-      // repaired block: exact keys from the pool; the values still need the
-      // draws.  All loads are issued before the hashing so that their latency
-      // overlaps it.
-      const uint4* xp = reinterpret_cast<const uint4*>(c.exact_pool + ((int64_t)cur.slot * 16 + n) * 128 + 32 * kq);
+      // repaired block: the exact bf16 keys of token n (channels 32k..32k+31)
+      // from the pool against head n's unscaled query pieces on bf16 MFMAs,
+      // so every product is exact.  The full query meets the full exact key
+      // (the outlier bypass's side-store logits are not added here).  The
+      // values still need the draws.  The pool loads are issued before the
+      // hashing so that their latency overlaps it.
+      // (a wave-uniform base, the slot's 4 KB, plus the lane offset 256 n + 64 k)
+      const uint8_t* pb = reinterpret_cast<const uint8_t*>(c.exact_pool) + (int64_t)cur.slot * 4096;
+      const uint32_t po = (uint32_t)(256 * n + 64 * kq);
       uint4 xv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = xp[j];
-      float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (CMP) {
-        const float2 s2 = *reinterpret_cast<const float2*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq + r0);
-        s4.x = s2.x;
-        s4.y = s2.y;
-      } else {
-        s4 = *reinterpret_cast<const float4*>(c.exact_scale + (int64_t)cur.slot * 16 + 4 * kq);
-      }
+      for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(pb + po + 16 * j);
       if (SCHEME == WC_DITHER_INT8) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -757,18 +784,14 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // (settled here so that the wait for these loads stays in this branch)
-        const h8 Ax = make_h8(settle((int)xv[j].x), settle((int)xv[j].y), settle((int)xv[j].z), settle((int)xv[j].w));
-        Dc = mfma32(Ax, Qhi[j], j == 0 ? zero4 : Dc);
-        if (QF32) Dc = mfma32(Ax, Qlo[j], Dc);
+#pragma unroll
+        for (int pq = 0; pq < NQP; ++pq) Dc = mfma_bf(xv[j], sQ[pq][n][4 * kq + j], (j == 0 && pq == 0) ? zero4 : Dc);
       }
-      st[0] = settle(s4.x);
-      st[1] = settle(s4.y);
-      if (!CMP) {
-        st[2] = settle(s4.z);
-        st[3] = settle(s4.w);
-      }
+      // the unscaled query: the token factor 2^qe cancels the logit scale's 2^-qe
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[r] = store_st;
       Da = zero4;
+      Do = zero4;
     }
     // the value side's draws (tokens 4k..4k+3, channels 8n..8n+7), read back
     // now so that the LDS latency hides behind the softmax
@@ -1346,8 +1369,8 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     set_error("wc_decode_attn_meter: cache codes not set");
     return WC_EINVAL;
   }
-  if (c.exact_slot && (!c.exact_pool || !c.exact_scale)) {
-    set_error("wc_decode_attn_meter: exact_slot set without exact_pool/exact_scale");
+  if (c.exact_slot && !c.exact_pool) {
+    set_error("wc_decode_attn_meter: exact_slot set without exact_pool");
     return WC_EINVAL;
   }
   if (c.num_outliers != 0) {

@@ -13,19 +13,24 @@
 //
 // Kernels: (1) per (sequence, KV head): fixed-point risks of all the group's
 // query heads summed in the workgroup, the trigger test on the sums, then
-// (rarely) bitonic sort of the candidates by risk in LDS and per-head scans
-// for the shortest sufficient prefix; (2) per (sequence, KV head) and copy
-// lane: the pool slots of the pair from the exclusive prefix of the counts in
-// (sequence, head) order (deterministic, no atomics), the pool counters
-// updated by one workgroup, then each selected block copied from pinned host
-// memory (zero-copy reads), stored as fp16 with a per-token power of two, its
-// witness zeroed and the block marked.  Kernel (1) keeps the pool counter's
-// value from before the call in the workspace, which is all kernel (2) reads
-// of it, so the one write of the counter races with no read.
+// (rarely) the candidates sorted by risk and per-head scans for the shortest
+// sufficient prefix; (2) per (sequence, KV head) and copy lane: the pool
+// slots of the pair from the exclusive prefix of the counts in (sequence,
+// head) order (deterministic, no atomics), the pool counters updated by one
+// workgroup, then each selected block copied from pinned host memory
+// (zero-copy reads) into the bf16 pool, its witness zeroed and the block
+// marked.  Kernel (1) keeps the pool counter's value from before the call in
+// the workspace, which is all kernel (2) reads of it, so the one write of the
+// counter races with no read.
+//
+// Sorting any number of blocks: the candidates are cut into tiles of 4096
+// that are sorted in LDS (bitonic) and written to the workspace, then merged
+// pairwise in the workspace (merge path: every thread finds its share of the
+// output by a binary search on the two runs) until one run is left.
 //
 // The tanh gate (the page-in comparison of the summary): the bound
 // tanh(max_t c_t / 2) is <= tau for every head exactly when no unrepaired
-// token has c_t > c* = 2 artanh(tau), so kernel (2) is replaced by one that
+// token has c_t > c* = 2 artanh(tau), so kernel (1) is replaced by one that
 // takes every unrepaired block whose largest bound over the group's heads
 // exceeds c*, ranked by that bound; (2) is shared.
 #include <math.h>
@@ -36,7 +41,9 @@ namespace wc {
 
 constexpr int kFxBits = 40;
 constexpr uint64_t kFxCap = uint64_t(1) << 47;
-constexpr int kMaxSortPages = 4096;
+constexpr int kTile = 4096;          // blocks sorted per LDS tile
+constexpr int kMaxPages = 65536;     // block index in the low 16 bits of a sort key
+constexpr int kGateThreads = 256;
 
 struct GateArgs {
   const float* logrisk;
@@ -48,6 +55,8 @@ struct GateArgs {
   int32_t* sel;           // [B][Hkv][max_pages]
   int32_t* count;         // [B][Hkv]
   int64_t* pool_old;      // the pool counter before this call
+  uint64_t* keys;         // [B][Hkv][max_pages] sort keys
+  uint64_t* keys2;        // [B][Hkv][max_pages] merge buffer
   int B, Hq, G, max_pages, layer;
   uint64_t T;
   float e_tau;            // E_tau rounded down to float (the quiet test)
@@ -76,11 +85,11 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 }
 
 // Bitonic sort of keys[0 .. np2) (np2 a power of two) in LDS, descending;
-// 256 threads, every thread calls it.
+// every thread of the workgroup calls it.
 __device__ void sort_desc(uint64_t* keys, int np2, int t) {
   for (int kk = 2; kk <= np2; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < np2; i += 256) {
+      for (int i = t; i < np2; i += kGateThreads) {
         const int ixj = i ^ jj;
         if (ixj > i) {
           const bool desc = (i & kk) == 0;
@@ -96,6 +105,61 @@ __device__ void sort_desc(uint64_t* keys, int np2, int t) {
   }
 }
 
+// Elements of the descending run A among the first d outputs of the merge of
+// A (length a) and B (length b), ties to A.
+__device__ __forceinline__ int merge_split(const uint64_t* A, int a, const uint64_t* B, int b, int d) {
+  int lo = d > b ? d - b : 0, hi = d < a ? d : a;
+  while (lo < hi) {
+    const int m = (lo + hi) >> 1;
+    if (A[m] >= B[d - 1 - m]) lo = m + 1; else hi = m;
+  }
+  return lo;
+}
+
+// Sort the n keys that `key_of(j)` gives for j < n, descending, through the
+// LDS tile `tile` and the two global buffers; returns the buffer holding the
+// sorted keys.  Every thread of the workgroup calls it.
+template <typename KeyOf>
+__device__ uint64_t* sort_keys(int n, uint64_t* tile, uint64_t* buf0, uint64_t* buf1, int t, KeyOf key_of) {
+  for (int base = 0; base < n; base += kTile) {
+    const int len = min(kTile, n - base);
+    int np2 = 1;
+    while (np2 < len) np2 <<= 1;
+    for (int i = t; i < np2; i += kGateThreads) tile[i] = i < len ? key_of(base + i) : 0;
+    __syncthreads();
+    sort_desc(tile, np2, t);
+    for (int i = t; i < len; i += kGateThreads) buf0[base + i] = tile[i];
+    __syncthreads();
+  }
+  uint64_t* src = buf0;
+  uint64_t* dst = buf1;
+  for (int w = kTile; w < n; w <<= 1) {
+    __threadfence_block();
+    __syncthreads();
+    for (int lo = 0; lo < n; lo += 2 * w) {
+      const int mid = min(lo + w, n), hi = min(lo + 2 * w, n);
+      const int a = mid - lo, b = hi - mid, tot = a + b;
+      const int per = (tot + kGateThreads - 1) / kGateThreads;
+      const int d0 = min(tot, t * per), d1 = min(tot, d0 + per);
+      if (d0 < d1) {
+        const uint64_t* A = src + lo;
+        const uint64_t* B = src + mid;
+        int i = merge_split(A, a, B, b, d0), j = d0 - i;
+        for (int d = d0; d < d1; ++d) {
+          const bool takeA = i < a && (j >= b || A[i] >= B[j]);
+          dst[lo + d] = takeA ? A[i++] : B[j++];
+        }
+      }
+    }
+    uint64_t* s = src;
+    src = dst;
+    dst = s;
+  }
+  __threadfence_block();
+  __syncthreads();
+  return src;
+}
+
 // Fixed-point risks, trigger test and (rarely) selection, one workgroup per
 // (sequence, KV head).
 //
@@ -106,12 +170,11 @@ __device__ void sort_desc(uint64_t* keys, int np2, int t) {
 // float roundings on both sides (about 1e-6 relative); when that bound is
 // below E_tau for every head the exact test could only answer "no trigger",
 // and the pair skips the block pass.
-__global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a, const int64_t* pool_used) {
-  __shared__ uint64_t keys[kMaxSortPages];
-  __shared__ uint64_t red[256];
+__global__ void __launch_bounds__(kGateThreads) gate_select_kernel(wc_cache c, GateArgs a, const int64_t* pool_used) {
+  __shared__ uint64_t tile[kTile];
+  __shared__ uint64_t red[kGateThreads];
   __shared__ float hlse[16];
-  __shared__ uint8_t rep[kMaxSortPages];
-  __shared__ uint64_t hsum[4][16];
+  __shared__ uint64_t hsum[kGateThreads / 64][16];
   __shared__ int kneed;
   const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
   if (b == 0 && g == 0 && t == 0) *a.pool_old = *pool_used;
@@ -120,6 +183,8 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   const int P = (S + 15) >> 4;
   const int G = a.G;
   const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;   // head n's row: row0 + n * max_pages
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int32_t* eslot = c.exact_slot + (int64_t)a.layer * c.num_pages * hkv + g;   // [phys * hkv]
   if (a.meter && !a.fx) {
     bool quiet = true;
     for (int n = 0; n < G; ++n) {
@@ -141,26 +206,26 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
 #pragma unroll
   for (int n = 0; n < 16; ++n) hl[n] = n < G ? a.lse[b * a.Hq + g * G + n] : 0.0f;
   const int jend = a.fx ? a.max_pages : P;           // the optional copy covers every block
-  for (int j0 = 0; j0 < jend; j0 += 4 * 256) {
+  for (int j0 = 0; j0 < jend; j0 += 4 * kGateThreads) {
     float lr[4][16];
     int ph[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j = min(j0 + u * 256 + t, a.max_pages - 1);
-      ph[u] = a.page_table[(int64_t)b * a.max_pages + min(j, max(P - 1, 0))];
+      const int j = min(j0 + u * kGateThreads + t, a.max_pages - 1);
+      ph[u] = ptab[min(j, max(P - 1, 0))];
 #pragma unroll
       for (int n = 0; n < 16; ++n) lr[u][n] = n < G ? a.logrisk[row0 + (int64_t)n * a.max_pages + j] : -INFINITY;
     }
     bool live[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * 256 + t;
+      const int j = j0 + u * kGateThreads + t;
       // repaired blocks (exact keys in the pool) carry no risk
-      live[u] = j < P && c.exact_slot[((int64_t)a.layer * c.num_pages + ph[u]) * hkv + g] < 0;
+      live[u] = j < P && eslot[(int64_t)ph[u] * hkv] < 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * 256 + t;
+      const int j = j0 + u * kGateThreads + t;
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         if (n < G) {
@@ -182,61 +247,56 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   // the trigger test is uniform across the workgroup
   uint64_t xmax = 0;
   for (int n = 0; n < G; ++n) {
-    const uint64_t X = hsum[0][n] + hsum[1][n] + hsum[2][n] + hsum[3][n];
+    uint64_t X = 0;
+    for (int w = 0; w < kGateThreads / 64; ++w) X += hsum[w][n];
     xmax = X > xmax ? X : xmax;
   }
   if (t == 0) a.count[b * hkv + g] = 0;
   if (xmax <= a.T || P == 0) return;
 
   if (t < 16) hlse[t] = t < G ? a.lse[b * a.Hq + g * G + t] : 0.0f;
-  for (int j = t; j < P; j += 256) {
-    const int phys = a.page_table[(int64_t)b * a.max_pages + j];
-    rep[j] = c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] >= 0;
-  }
   __syncthreads();
-  auto fx_of = [&](int n, int j) -> uint64_t {
-    return rep[j] ? 0 : risk_fx(a.logrisk[row0 + (int64_t)n * a.max_pages + j], hlse[n]);
-  };
-
-  // sort key: max_h rho_fx (47 bits) << 16 | (65535 - j): descending = risk
-  // descending, ties to the lower block index; non-candidates are 0.
-  int np2 = 1;
-  while (np2 < P) np2 <<= 1;
-  for (int j = t; j < np2; j += 256) {
-    uint64_t k = 0;
-    if (j < P) {
-      uint64_t m = 0;
-      for (int n = 0; n < G; ++n) {
-        const uint64_t v = fx_of(n, j);
-        m = v > m ? v : m;
-      }
-      k = m ? (m << 16) | (uint64_t)(65535 - j) : 0;
+  // sort key: max_h rho_fx (at most 2^47) << 16 | (65535 - j): descending =
+  // risk descending, ties to the lower block index; non-candidates (repaired
+  // or riskless blocks) are 0 and sort last.
+  auto key_of = [&](int j) -> uint64_t {
+    if (eslot[(int64_t)ptab[j] * hkv] >= 0) return 0;
+    uint64_t m = 0;
+    for (int n = 0; n < G; ++n) {
+      const uint64_t v = risk_fx(a.logrisk[row0 + (int64_t)n * a.max_pages + j], hlse[n]);
+      m = v > m ? v : m;
     }
-    keys[j] = k;
-  }
-  __syncthreads();
-  sort_desc(keys, np2, t);
+    return m ? (m << 16) | (uint64_t)(65535 - j) : 0;
+  };
+  const int64_t pair = ((int64_t)b * hkv + g) * a.max_pages;
+  const uint64_t* keys = sort_keys(P, tile, a.keys + pair, a.keys2 + pair, t, key_of);
+  // a candidate's block and its fixed-point risk for head n (candidates are
+  // never repaired)
+  auto fx_at = [&](int n, uint64_t k) -> uint64_t {
+    const int j = 65535 - (int)(k & 0xFFFF);
+    return risk_fx(a.logrisk[row0 + (int64_t)n * a.max_pages + j], hlse[n]);
+  };
   // shortest prefix: per head, k_h = #{i : exclusive prefix sum < X_h - T}
   if (t == 0) kneed = 0;
   __syncthreads();
-  const int per = (P + 255) / 256;
-  const int i0 = t * per, i1 = min(P, i0 + per);
+  const int per = (P + kGateThreads - 1) / kGateThreads;
+  const int i0 = min(P, t * per), i1 = min(P, i0 + per);
   for (int n = 0; n < G; ++n) {
     uint64_t mine = 0;
     for (int i = i0; i < i1; ++i) {
       const uint64_t k = keys[i];
-      if (k) mine += fx_of(n, 65535 - (int)(k & 0xFFFF));
+      if (k) mine += fx_at(n, k);
     }
     // exclusive scan of the per-thread sums (Hillis-Steele in LDS)
     red[t] = mine;
     __syncthreads();
-    for (int s = 1; s < 256; s <<= 1) {
+    for (int s = 1; s < kGateThreads; s <<= 1) {
       const uint64_t add = t >= s ? red[t - s] : 0;
       __syncthreads();
       red[t] += add;
       __syncthreads();
     }
-    const uint64_t total = red[255];
+    const uint64_t total = red[kGateThreads - 1];
     uint64_t pre = red[t] - mine;
     __syncthreads();
     const uint64_t need = total > a.T ? total - a.T : 0;
@@ -245,11 +305,11 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
       const uint64_t k = keys[i];
       if (!k) break;
       if (pre < need) ++cnt;
-      pre += fx_of(n, 65535 - (int)(k & 0xFFFF));
+      pre += fx_at(n, k);
     }
     red[t] = (uint64_t)cnt;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
+    for (int s = kGateThreads / 2; s > 0; s >>= 1) {
       if (t < s) red[t] += red[t + s];
       __syncthreads();
     }
@@ -258,51 +318,46 @@ __global__ void __launch_bounds__(256) gate_select_kernel(wc_cache c, GateArgs a
   }
   int k = kneed;
   if (a.budget >= 0 && k > a.budget) k = (int)a.budget;
-  for (int i = t; i < k; i += 256) a.sel[((int64_t)b * hkv + g) * a.max_pages + i] = 65535 - (int)(keys[i] & 0xFFFF);
+  for (int i = t; i < k; i += kGateThreads) a.sel[pair + i] = 65535 - (int)(keys[i] & 0xFFFF);
   if (t == 0) a.count[b * hkv + g] = k;
 }
 
 // Tanh gate selection, one workgroup per (sequence, KV head): candidates are
 // the unrepaired blocks with max_h cmax[h][j] > c* (float32 comparison); sort
 // key = the float's bits (monotone for values >= 0) << 16 | (65535 - j).
-__global__ void __launch_bounds__(256) gate_tanh_select_kernel(wc_cache c, GateArgs a, const float* cmax,
-                                                               float cstar, const int64_t* pool_used) {
-  __shared__ uint64_t keys[kMaxSortPages];
-  __shared__ int ncand[256];
+__global__ void __launch_bounds__(kGateThreads) gate_tanh_select_kernel(wc_cache c, GateArgs a, const float* cmax,
+                                                                        float cstar, const int64_t* pool_used) {
+  __shared__ uint64_t tile[kTile];
+  __shared__ int ncand[kGateThreads];
   const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
   if (b == 0 && g == 0 && t == 0) *a.pool_old = *pool_used;
   const int hkv = c.num_kv_heads;
   const int P = (a.ctx_len[b] + 15) >> 4;
   const int G = a.G;
   const int64_t row0 = ((int64_t)b * a.Hq + g * G) * a.max_pages;
-  int np2 = 1;
-  while (np2 < P) np2 <<= 1;
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int32_t* eslot = c.exact_slot + (int64_t)a.layer * c.num_pages * hkv + g;
+  auto key_of = [&](int j) -> uint64_t {
+    if (eslot[(int64_t)ptab[j] * hkv] >= 0) return 0;
+    float m = 0.0f;
+    for (int n = 0; n < G; ++n) m = fmaxf(m, cmax[row0 + (int64_t)n * a.max_pages + j]);
+    return m > cstar ? ((uint64_t)__float_as_uint(m) << 16) | (uint64_t)(65535 - j) : 0;
+  };
   int mine = 0;
-  for (int j = t; j < np2; j += 256) {
-    uint64_t k = 0;
-    if (j < P) {
-      const int phys = a.page_table[(int64_t)b * a.max_pages + j];
-      if (c.exact_slot[((int64_t)a.layer * c.num_pages + phys) * hkv + g] < 0) {
-        float m = 0.0f;
-        for (int n = 0; n < G; ++n) m = fmaxf(m, cmax[row0 + (int64_t)n * a.max_pages + j]);
-        if (m > cstar) {
-          k = ((uint64_t)__float_as_uint(m) << 16) | (uint64_t)(65535 - j);
-          ++mine;
-        }
-      }
-    }
-    keys[j] = k;
-  }
+  for (int j = t; j < P; j += kGateThreads) mine += key_of(j) != 0;
   ncand[t] = mine;
   __syncthreads();
-  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+  for (int s2 = kGateThreads / 2; s2 > 0; s2 >>= 1) {
     if (t < s2) ncand[t] += ncand[t + s2];
     __syncthreads();
   }
   int k = ncand[0];
-  if (k > 0) sort_desc(keys, np2, t);
+  if (t == 0) a.count[b * hkv + g] = 0;
+  if (k == 0) return;
+  const int64_t pair = ((int64_t)b * hkv + g) * a.max_pages;
+  const uint64_t* keys = sort_keys(P, tile, a.keys + pair, a.keys2 + pair, t, key_of);
   if (a.budget >= 0 && k > a.budget) k = (int)a.budget;
-  for (int i = t; i < k; i += 256) a.sel[((int64_t)b * hkv + g) * a.max_pages + i] = 65535 - (int)(keys[i] & 0xFFFF);
+  for (int i = t; i < k; i += kGateThreads) a.sel[pair + i] = 65535 - (int)(keys[i] & 0xFFFF);
   if (t == 0) a.count[b * hkv + g] = k;
 }
 
@@ -362,31 +417,9 @@ __global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, 
     const int phys = a.page_table[(int64_t)b * a.max_pages + j];
     const int64_t pg = ((int64_t)a.layer * c.num_pages + phys) * hkv + g;
     const int64_t slot = start + i;
+    // the exact bf16 keys go to the pool as they are: [slot][token][128]
     const uint4 v = *reinterpret_cast<const uint4*>(host_k + (pg * 16 + tok) * 128 + 8 * part);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float x[8];
-    float am = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = __uint_as_float(w[e] << 16);
-      x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      am = fmaxf(am, fmaxf(fabsf(x[2 * e]), fabsf(x[2 * e + 1])));
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
-    int ex = 0, sh = 0;
-    if (am > 0.0f && am < INFINITY) {
-      frexpf(am, &ex);
-      sh = 15 - ex;                            // row max in [2^14, 2^15)
-    }
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      _Float16 h0 = (_Float16)ldexpf(x[2 * e], sh), h1 = (_Float16)ldexpf(x[2 * e + 1], sh);
-      o[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    }
-    *reinterpret_cast<uint4*>(c.exact_pool + (slot * 16 + tok) * 128 + 8 * part) = make_uint4(o[0], o[1], o[2], o[3]);
-    if (part == 0) c.exact_scale[slot * 16 + tok] = ldexpf(1.0f, -sh);
+    *reinterpret_cast<uint4*>(c.exact_pool + (slot * 16 + tok) * 128 + 8 * part) = v;
     if (part < 8) c.witness[(pg * 16 + tok) * 8 + part] = 0.0f;
     __syncthreads();
     if (t == 0) c.exact_slot[pg] = (int32_t)slot;
@@ -397,12 +430,19 @@ __global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, 
 
 using namespace wc;
 
-extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
-  if (B < 0 || Hkv < 0 || max_pages < 0) return 0;
+namespace {
+size_t gate_ws_head(int B, int Hkv, int max_pages) {
   // selected block indices and the count per (sequence, KV head), then the
   // pool counter's value before the call (8-byte aligned)
   const size_t head = (size_t)B * Hkv * max_pages * 4 + (size_t)B * Hkv * 4;
   return ((head + 7) & ~(size_t)7) + 8;
+}
+}  // namespace
+
+extern "C" size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages) {
+  if (B < 0 || Hkv < 0 || max_pages < 0) return 0;
+  // ... and the two sort buffers of 64-bit keys
+  return gate_ws_head(B, Hkv, max_pages) + 2 * (size_t)B * Hkv * max_pages * 8;
 }
 
 namespace {
@@ -414,13 +454,13 @@ int gate_prepare(const char* fn, const wc_cache* cache, int layer, int B, int Hq
     set_error("%s: need head_dim 128, 8 bands, 16-token pages", fn);
     return WC_EUNSUPPORTED;
   }
-  if (!c.exact_slot || !c.exact_pool || !c.exact_scale || !c.witness || c.pool_capacity < 0) {
-    set_error("%s: cache needs exact_slot, exact_pool, exact_scale and witness", fn);
+  if (!c.exact_slot || !c.exact_pool || !c.witness || c.pool_capacity < 0) {
+    set_error("%s: cache needs exact_slot, exact_pool and witness", fn);
     return WC_EINVAL;
   }
   if (B < 0 || Hq < 1 || Hq % c.num_kv_heads != 0 || Hq / c.num_kv_heads > 16 || max_pages < 1 ||
-      max_pages > kMaxSortPages || layer < 0 || layer >= c.num_layers) {
-    set_error("%s: bad B/Hq/max_pages (<= %d)/layer", fn, kMaxSortPages);
+      max_pages > kMaxPages || layer < 0 || layer >= c.num_layers) {
+    set_error("%s: bad B/Hq/max_pages (<= %d)/layer", fn, kMaxPages);
     return WC_EINVAL;
   }
   if (B == 0) return WC_OK;                    // nothing to do (the caller returns too)
@@ -428,19 +468,23 @@ int gate_prepare(const char* fn, const wc_cache* cache, int layer, int B, int Hq
     set_error("%s: workspace too small", fn);
     return WC_EWORKSPACE;
   }
-  // host store: translate to the device view of the pinned allocation
+  // host store: the device view of the pinned allocation; a pointer the
+  // device cannot map (pageable memory) is refused before any launch
   *dev_host = nullptr;
   if (hipHostGetDevicePointer(dev_host, const_cast<void*>(host_exact_k), 0) != hipSuccess || !*dev_host) {
     (void)hipGetLastError();
-    *dev_host = const_cast<void*>(host_exact_k);   // unified addressing: same pointer
+    set_error("%s: host_exact_k is not pinned, device-readable host memory", fn);
+    return WC_EINVAL;
   }
   const int hkv = c.num_kv_heads;
   char* ws = (char*)workspace;
   a.sel = (int32_t*)ws;
   ws += (size_t)B * hkv * max_pages * 4;
   a.count = (int32_t*)ws;
-  const size_t head = (size_t)B * hkv * max_pages * 4 + (size_t)B * hkv * 4;
-  a.pool_old = (int64_t*)((char*)workspace + ((head + 7) & ~(size_t)7));
+  const size_t head = gate_ws_head(B, hkv, max_pages);
+  a.pool_old = (int64_t*)((char*)workspace + head - 8);
+  a.keys = (uint64_t*)((char*)workspace + head);
+  a.keys2 = a.keys + (size_t)B * hkv * max_pages;
   a.B = B;
   a.Hq = Hq;
   a.G = Hq / hkv;
@@ -477,8 +521,8 @@ extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float
   const float cstar = tau >= 1.0 ? INFINITY : (float)(2.0 * atanh(tau));
   const int hkv = c.num_kv_heads;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(gate_tanh_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a, block_cmax,
-                     cstar, (const int64_t*)pool_used);
+  hipLaunchKernelGGL(gate_tanh_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(kGateThreads), 0, st, c, a,
+                     block_cmax, cstar, (const int64_t*)pool_used);
   if (int e = check_launch("wc_gate_pagein_tanh select")) return e;
   hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,
                      (const uint16_t*)dev_host, B * hkv, c.pool_capacity, pool_used, bytes_paged, selected);
@@ -486,10 +530,10 @@ extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float
 }
 
 extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
-                              const float* meter, int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,
-                              int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
-                              int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx, void* workspace,
-                              size_t ws_bytes, void* stream) {
+                              const float* meter, int B, int Hq, const int32_t* page_table, int max_pages,
+                              const int32_t* ctx_len, double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
+                              int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
+                              void* workspace, size_t ws_bytes, void* stream) {
   if (!cache || (B != 0 && (!block_logrisk || !lse || !page_table || !ctx_len || !host_exact_k || !pool_used ||
                              !bytes_paged || !workspace))) {
     set_error("wc_gate_pagein: null pointer");
@@ -519,7 +563,7 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
   a.T = (uint64_t)floor(et * 1099511627776.0);
   a.budget = budget_blocks;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(256), 0, st, c, a,
+  hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(kGateThreads), 0, st, c, a,
                      (const int64_t*)pool_used);
   if (int e = check_launch("wc_gate_pagein select")) return e;
   hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,

@@ -62,9 +62,12 @@ __device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, 
 __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
 __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
 
-// Witness rounding guard: the float32 band norm is within ~2^-20 of the
-// exact norm; scaling by 1 + 2^-17 keeps the stored value above it.
-constexpr float kWitnessGuard = 1.0f + 7.62939453125e-06f;
+// Witness rounding guard.  With u = 2^-24: each residual is one rounding of
+// the exact r (relative u), its square enters a sum of nonnegative terms whose
+// longest chain has at most 12 roundings, and the square root adds at most 2u,
+// so the float32 norm is >= (1 - 9u) of the exact one; the guard 1 + 16u (one
+// more rounding on the product) keeps the stored value above it.
+constexpr float kWitnessGuard = 1.0f + 9.5367431640625e-07f;   // 1 + 2^-20
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }

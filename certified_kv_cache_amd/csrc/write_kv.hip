@@ -206,6 +206,23 @@ __device__ __forceinline__ void bypass_lanes(const wc_cache& c, int layer, int h
   ochan = lane16 < m ? (oc[lane16] & 127) : -1;   // (in range even for a corrupt list)
 }
 
+// Persistent repair: a token written into a repaired block (exact_slot >= 0)
+// also stores its exact key (bf16, 8 channels per lane) in the block's pool
+// row, and its witness is 0 (the decode takes c = 0 there).  The host refuses
+// float32 keys for a cache with exact_slot set, so only the bf16 instance
+// copies.  Returns whether the row's block is repaired.
+template <typename T>
+__device__ __forceinline__ bool repaired_row(const wc_cache& c, int64_t pg, int64_t off, const T* krow, int lane16) {
+  if (!c.exact_slot) return false;
+  const int32_t s = c.exact_slot[pg];
+  if (s < 0) return false;
+  if constexpr (sizeof(T) == 2) {
+    const uint4 x = *reinterpret_cast<const uint4*>(krow);
+    *reinterpret_cast<uint4*>(c.exact_pool + ((int64_t)s * 16 + off) * 128 + 8 * lane16) = x;
+  }
+  return true;
+}
+
 // Grid (ceil(n_tok / 16), Hkv, n_layers): 16 consecutive tokens of one KV
 // head per workgroup (no index division).
 template <typename T, int SCHEME, bool OUTL>
@@ -240,7 +257,8 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
   uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 2048 + ((lane16 & 3) >> 1) * 1024 +
                 (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
   *reinterpret_cast<uint2*>(kc) = make_uint2(o.kp[0], o.kp[1]);
-  if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = o.w;
+  const bool rep = repaired_row<T>(c, pg, off, kin + in_off, lane16);
+  if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = rep ? 0.0f : o.w;
   if (SC && lane16 == 0) c.k_scale[pg * 16 + off] = o.ks;
   if (OUTL && ochan >= 0)
     c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] = reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
@@ -297,7 +315,8 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     sV[(k >> 2) * 1024 + (j >> 2) * 256 + lane16 * 16 + (k & 3) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
-  if (lane16 < 8) c.witness[(pg * 16 + j) * 8 + lane16] = o.w;
+  const bool rep = repaired_row<T>(c, pg, j, kin + in_off, lane16);
+  if (lane16 < 8) c.witness[(pg * 16 + j) * 8 + lane16] = rep ? 0.0f : o.w;
   if (SC && lane16 == 0) {
     c.k_scale[pg * 16 + j] = o.ks;
     c.v_scale[pg * 16 + j] = o.vs;
@@ -371,11 +390,12 @@ __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __res
     return;
   }
   const float tot = ss + dpp_f<kRowRor8>(ss);
-  if (live && lane16 < 8) {
-    const int64_t slot = a.slot[i];
-    const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
-    c.witness[(pg * 16 + slot % 16) * 8 + lane16] = sqrtf(tot) * kWitnessGuard;
-  }
+  if (!live) return;
+  const int64_t slot = a.slot[i];
+  const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
+  // a repaired block: the exact key x to the pool row, witness 0
+  const bool rep = repaired_row<T>(c, pg, slot % 16, x + in_off, lane16);
+  if (lane16 < 8) c.witness[(pg * 16 + slot % 16) * 8 + lane16] = rep ? 0.0f : sqrtf(tot) * kWitnessGuard;
 }
 
 // ---------------------------------------------------------------- 2-bit (KIVI-style)
@@ -597,6 +617,14 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
     set_error("wc_write_kv: at most 2^26 tokens per call");
     return WC_EINVAL;
   }
+  if (c.exact_slot && in_dtype == WC_F32) {
+    set_error("wc_write_kv: a cache with an exact pool (exact_slot set) takes bf16 keys: the exact store is bf16");
+    return WC_EUNSUPPORTED;
+  }
+  if (c.exact_slot && !c.exact_pool) {
+    set_error("wc_write_kv: exact_slot set without exact_pool");
+    return WC_EINVAL;
+  }
   RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, pos, seed};
   hipStream_t st = (hipStream_t)stream;
   if (n_tok == 0) return WC_OK;
@@ -717,6 +745,14 @@ extern "C" int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers
     set_error("wc_write_kv_pages: cache codes, scales and witness must be set");
     return WC_EINVAL;
   }
+  if (c.exact_slot && in_dtype == WC_F32) {
+    set_error("wc_write_kv_pages: a cache with an exact pool (exact_slot set) takes bf16 keys: the exact store is bf16");
+    return WC_EUNSUPPORTED;
+  }
+  if (c.exact_slot && !c.exact_pool) {
+    set_error("wc_write_kv_pages: exact_slot set without exact_pool");
+    return WC_EINVAL;
+  }
   if (c.num_outliers != 0) {
     if (c.scheme != WC_DITHER_INT8 || (c.num_outliers != 8 && c.num_outliers != 16)) {
       set_error("wc_write_kv_pages: the outlier bypass needs the dithered INT8 scheme and m = 8 or 16");
@@ -780,6 +816,14 @@ extern "C" int wc_witness(const wc_cache* cache, int layer0, int n_layers, const
   if (in_dtype != WC_F32 && in_dtype != WC_BF16) {
     set_error("wc_witness: in_dtype must be WC_F32 or WC_BF16");
     return WC_EUNSUPPORTED;
+  }
+  if (!values && c.exact_slot && in_dtype == WC_F32) {
+    set_error("wc_witness: a cache with an exact pool (exact_slot set) takes bf16 keys: the exact store is bf16");
+    return WC_EUNSUPPORTED;
+  }
+  if (!values && c.exact_slot && !c.exact_pool) {
+    set_error("wc_witness: exact_slot set without exact_pool");
+    return WC_EINVAL;
   }
   if (n_tok == 0) return WC_OK;
   RowArgs a{n_tok, layer_stride, c.num_pages, c.num_kv_heads, layer0, n_layers, slot, nullptr, nullptr};

@@ -56,16 +56,28 @@
  *  v_aux     2-bit: fp32 [L][P][Hkv][32][4][2] (scale, min) per token group.
  *  witness   fp32 [L][P][Hkv][page][8]: w_{t,b} = ||r_{t,b}||, keys only.
  *  exact_slot int32 [L][P][Hkv]: -1 = quantized, else the slot of the
- *            repaired block in the exact pool.
- *  exact_pool fp16 [capacity][16][128] and exact_scale fp32 [capacity][16]:
- *            a repaired block's exact keys as fp16(k * 2^e_t) with the
- *            per-token power of two 2^-e_t in exact_scale.
+ *            repaired block in the exact pool.  A caller that hands a
+ *            physical page to another sequence resets its entries to -1.
+ *  exact_pool bf16 [capacity][16][128]: a repaired block's exact keys, token
+ *            t of the block at row t (row t of slot s at (16 s + t) * 128).
  *  outlier_ch int32 [L][Hkv][m] (m = num_outliers): the outlier-bypass
  *            channels O of each layer and KV head, ascending and distinct.
  *  k_outlier bf16 [L][P][Hkv][16][m]: entry i of a token is its exact key on
  *            channel O[i].
  *  v_witness fp32 [L][P][Hkv][page]: the value witness w^V_t = ||v^_t - v_t||
  *            over all 128 channels (written when the pointer is set).
+ *
+ * Exact keys and repair (the gate).  The exact store is bf16: the pinned host
+ * store, the exact pool and the keys the write path copies into it.  A
+ * repaired block's tokens are decoded with their exact keys and c_t = 0, so
+ * a cache with exact_slot set takes bf16 keys only (wc_write_kv,
+ * wc_write_kv_pages and the key witness of wc_witness refuse float32 keys
+ * with WC_EUNSUPPORTED).  Repair persists (paperswithlean Figure 5 caption:
+ * incremental persistent repair): a token written into a repaired block also
+ * gets its exact key in the block's pool row and a zero witness, so appends
+ * into a partially filled repaired page stay exact.  The host store must hold
+ * the exact keys of every token written before a gate call that may repair
+ * its block.
  *
  * Value certificate (WC_METER_V).  The summary reports joint K+V coverage but
  * defines witnesses for keys only.  Reading implemented here: the value
@@ -135,8 +147,7 @@ typedef struct {
   float* v_aux;
   float* witness;
   int32_t* exact_slot;  /* may be NULL when no block is ever repaired        */
-  uint16_t* exact_pool;
-  float* exact_scale;
+  uint16_t* exact_pool; /* bf16 [pool_capacity][16][128]                     */
   int64_t pool_capacity;
   int32_t num_outliers; /* m: 0 (no bypass), 8 or 16 (dithered INT8 only)     */
   int32_t reserved;     /* 0                                                 */
@@ -165,7 +176,9 @@ typedef struct {
  *             sequence (dither counter).
  *  seed       device uint64 [n_tok]: dither seed of the token's sequence.
  * Writes k_codes, v_codes, scales (or aux), the key witness and, when
- * cache->v_witness is set, the value witness; with the
+ * cache->v_witness is set, the value witness; in a repaired block (exact_slot
+ * >= 0) the key witness is 0 and the exact key goes to the block's pool row
+ * (bf16 input only when exact_slot is set); with the
  * outlier bypass (num_outliers > 0, bf16 input only) also k_outlier, reading
  * the channels of each layer from outlier_ch.  RTN INT8: code =
  * clamp(rint(x * (127/absmax)), -128, 127), x^ = s code.  16-bit store
@@ -211,8 +224,11 @@ int wc_write_kv_pages(const wc_cache* cache, int layer0, int n_layers, const voi
  *  slot       device int64 [n_tok]: page * 16 + offset (16-token pages).
  *  values     0: x are keys, the banded key witness goes to cache->witness;
  *             1: x are values, ||x^ - x|| goes to cache->v_witness.
- * The stored value is rounded up (by a factor 1 + 2^-17) so that it never
- * falls below the exact norm.
+ * The stored value is rounded up (by a factor 1 + 2^-20) so that it never
+ * falls below the exact norm.  Keys in a repaired block (exact_slot >= 0)
+ * store a zero witness and their exact key x in the block's pool row (for the
+ * 16-bit store this call completes a token's write there); with exact_slot
+ * set, keys must be bf16.
  */
 int wc_witness(const wc_cache* cache, int layer0, int n_layers, const void* x, const void* xhat, int in_dtype,
                int64_t n_tok, int64_t layer_stride, const int64_t* slot, int values, void* stream);
@@ -253,6 +269,9 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *  page_table device int32 [B][max_pages] physical page of each logical block.
  *  ctx_len    device int32 [B]: tokens cached per sequence (<= max_pages*16).
  *  seed       device uint64 [B]: dither seed of each sequence.
+ *  Repaired blocks (exact_slot >= 0) take their keys from the bf16 pool,
+ *             multiplied with the query on bf16 MFMAs (exact products; an fp32
+ *             query enters as three bf16 pieces that sum to it exactly).
  *  meter_mask 0, WC_METER_A or WC_METER_A|WC_METER_B (B needs dithered INT8),
  *             plus WC_METER_V for the value certificate (any scheme; needs
  *             cache->v_witness) and WC_BLOCK_CMAX for the block output mode.
@@ -331,14 +350,23 @@ int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, fl
  *                is that sum taken per block, each rounded up by < 2^-40), and
  *                skips the pass over its block risks; the decisions are the
  *                same as with meter = NULL.  Ignored when rho_fx is given.
- *  host_exact_k  pinned host bf16 [L][P][Hkv][16][128], device-readable.
+ *  host_exact_k  pinned host bf16 [L][P][Hkv][16][128], device-readable
+ *                (hipHostMalloc / torch pin_memory); a pointer the device
+ *                cannot map returns WC_EINVAL before any launch.  It holds
+ *                the exact keys of every token written so far; the pool rows
+ *                of tokens appended after a repair are written by the write
+ *                path.
  *  pool_used     device int64 [1], in/out.
  *  bytes_paged   device int64 [1], incremented by 4096 per repaired block.
  *  selected      nullable device int32 [B][Hkv][max_pages + 1]: count, then
  *                the chosen blocks in rank order (those that got a slot).
  *  rho_fx        nullable device uint64 [B][Hq][max_pages] test export.
  *  workspace     device scratch, ws_bytes >= wc_gate_workspace_bytes().
- * Requires cache->exact_slot, exact_pool, exact_scale; 0 <= tau, E_tau < 64.
+ * Requires cache->exact_slot and exact_pool; 0 <= tau, E_tau < 64;
+ * max_pages <= 65536 (sequences of up to 1,048,576 tokens).  A triggered
+ * (sequence, KV head) sorts its candidate blocks in LDS tiles of 4096 and
+ * merges the tiles in the workspace, so any length up to that bound is ranked
+ * exactly.
  */
 int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
                    const float* meter, int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
@@ -346,7 +374,9 @@ int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk,
                    int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
                    void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of the gate workspace for B sequences, Hkv heads and max_pages blocks. */
+/* Bytes of the gate workspace for B sequences, Hkv heads and max_pages blocks:
+ * the selection (4 B per block), the counts, the pool counter and two sort
+ * buffers (8 B per block each). */
 size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages);
 
 /*
@@ -363,7 +393,8 @@ size_t wc_gate_workspace_bytes(int B, int Hkv, int max_pages);
  *  block_cmax  device fp32 [B][Hq][max_pages]: the decode's block output
  *              with WC_BLOCK_CMAX.
  *  workspace   as for wc_gate_pagein (wc_gate_workspace_bytes()).
- * Requires cache->exact_slot, exact_pool, exact_scale; tau >= 0.
+ * Requires cache->exact_slot and exact_pool; tau >= 0; max_pages <= 65536;
+ * host_exact_k as for wc_gate_pagein.
  */
 int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float* block_cmax, int B, int Hq,
                         const int32_t* page_table, int max_pages, const int32_t* ctx_len, double tau,

@@ -44,10 +44,17 @@ def test_version_and_workspace_sizes():
 
 
 def _cache(L, **kw):
-    c = L.WcCache(L.WC_DITHER_INT8, 128, 4, 8, 16, 2, 10, *([1] * 10), 0)
+    """A descriptor with fake non-NULL array pointers (never dereferenced on
+    the host) and no exact pool unless asked for."""
+    c = L.WcCache(L.WC_DITHER_INT8, 128, 4, 8, 16, 2, 10, *([1] * 9), 0)
+    c.exact_slot = None
+    c.exact_pool = None
     for k, v in kw.items():
         setattr(c, k, v)
     return c
+
+
+POOL = dict(exact_slot=16, exact_pool=16, pool_capacity=4)
 
 
 def test_write_rejects_bad_arguments():
@@ -100,7 +107,7 @@ def test_merge_and_gate_reject_bad_arguments():
     assert L.lib.wc_lse_merge(None, 1, 1, 1, p, p, None, None, None, None, None, None) == L.WC_EINVAL
     assert L.lib.wc_lse_merge(p, 1, 1, 0, p, p, None, None, None, None, None, None) == L.WC_EINVAL
     g = L.lib.wc_gate_pagein
-    c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
+    c = ctypes.byref(_cache(L, scheme=1, **POOL))
     wsb = L.wc_gate_workspace_bytes(2, 4, 8)
 
     def call(cache=c, tau=0.2, mp=8, wsb=wsb, host=p):
@@ -109,9 +116,9 @@ def test_merge_and_gate_reject_bad_arguments():
     assert call(host=None) == L.WC_EINVAL
     assert call(tau=-1.0) == L.WC_EINVAL
     assert call(tau=1e6) == L.WC_EINVAL
-    assert call(mp=5000) == L.WC_EINVAL
+    assert call(mp=65537) == L.WC_EINVAL              # block index beyond 16 bits
     assert call(wsb=1) == L.WC_EWORKSPACE
-    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
+    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_pool=16, pool_capacity=4))) == L.WC_EINVAL
     assert L.lib.wc_dither_fill(1, 0, 0, -1, 4, p, None) == L.WC_EINVAL
     assert L.lib.wc_dither_fill(1, 0, 0, 0, 4, None, None) == L.WC_EINVAL
 
@@ -146,7 +153,7 @@ def test_tanh_gate_and_cmax_reject_bad_arguments():
     L = _lib()
     p = ctypes.c_void_p(16)
     g = L.lib.wc_gate_pagein_tanh
-    c = ctypes.byref(_cache(L, scheme=1, pool_capacity=4))
+    c = ctypes.byref(_cache(L, scheme=1, **POOL))
     wsb = L.wc_gate_workspace_bytes(2, 4, 8)
 
     def call(cache=c, tau=0.2, mp=8, wsb=wsb, cm=p):
@@ -154,9 +161,9 @@ def test_tanh_gate_and_cmax_reject_bad_arguments():
 
     assert call(cm=None) == L.WC_EINVAL
     assert call(tau=-0.5) == L.WC_EINVAL
-    assert call(mp=5000) == L.WC_EINVAL
+    assert call(mp=65537) == L.WC_EINVAL
     assert call(wsb=1) == L.WC_EWORKSPACE
-    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_slot=None))) == L.WC_EINVAL
+    assert call(cache=ctypes.byref(_cache(L, scheme=1, exact_pool=16, pool_capacity=4))) == L.WC_EINVAL
     d = L.lib.wc_decode_attn_meter
     ws = L.wc_decode_workspace_bytes(2, 28, 4)
     cc = ctypes.byref(_cache(L))
@@ -209,3 +216,49 @@ def test_write_pages_rejects_bad_arguments():
     assert f(ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
     assert f(ctypes.byref(_cache(L, k_scale=None)), 0, 1, p, p, 1, 4, 0, p, p, p, None) == L.WC_EINVAL
     assert f(ok, 0, 1, p, p, 1, 0, 0, p, p, p, None) == L.WC_OK                  # nothing to do
+
+
+def test_gate_refuses_a_host_store_the_device_cannot_map():
+    """A pageable host buffer (here a numpy array) is refused with WC_EINVAL
+    before any launch: every other argument is valid, so the refusal comes from
+    the device-pointer lookup of host_exact_k (which fails for memory that was
+    not allocated pinned, and on a machine without a GPU)."""
+    import numpy as np
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    pageable = np.zeros((2, 10, 4, 16, 128), dtype=np.uint16)
+    host = ctypes.c_void_p(pageable.ctypes.data)
+    c = ctypes.byref(_cache(L, scheme=1, **POOL))
+    wsb = L.wc_gate_workspace_bytes(2, 4, 8)
+    rc = L.lib.wc_gate_pagein(c, 0, p, p, None, 2, 28, p, 8, p, 0.2, -1, host, p, p, None, None, p, wsb, None)
+    assert rc == L.WC_EINVAL
+    assert b"not pinned" in L.lib.wc_last_error()
+    rc = L.lib.wc_gate_pagein_tanh(c, 0, p, 2, 28, p, 8, p, 0.2, -1, host, p, p, None, p, wsb, None)
+    assert rc == L.WC_EINVAL
+    assert b"not pinned" in L.lib.wc_last_error()
+
+
+def test_gate_workspace_covers_the_sort_buffers():
+    L = _lib()
+    B, hkv, mp = 3, 4, 8192
+    head = B * hkv * mp * 4 + B * hkv * 4
+    assert L.wc_gate_workspace_bytes(B, hkv, mp) == ((head + 7) // 8) * 8 + 8 + 2 * B * hkv * mp * 8
+
+
+def test_caches_with_an_exact_pool_take_bf16_keys():
+    """The exact store is bf16: with exact_slot set, float32 keys are refused
+    by every call that writes keys (they could not be stored exactly)."""
+    L = _lib()
+    p = ctypes.c_void_p(16)
+    pooled = ctypes.byref(_cache(L, **POOL))
+    assert L.lib.wc_write_kv(pooled, 0, 1, p, p, L.WC_F32, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    assert b"bf16" in L.lib.wc_last_error()
+    assert L.lib.wc_write_kv(pooled, 0, 1, p, p, L.WC_BF16, 0, 0, p, p, p, None) == L.WC_OK
+    assert L.lib.wc_write_kv_pages(pooled, 0, 1, p, p, L.WC_F32, 4, 0, p, p, p, None) == L.WC_EUNSUPPORTED
+    store = ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE, **POOL))
+    assert L.lib.wc_witness(store, 0, 1, p, p, L.WC_F32, 4, 0, p, 0, None) == L.WC_EUNSUPPORTED
+    # values carry no exact keys
+    assert L.lib.wc_witness(ctypes.byref(_cache(L, scheme=L.WC_BF16_STORE, v_witness=16, **POOL)), 0, 1, p, p,
+                            L.WC_F32, 0, 0, p, 1, None) == L.WC_OK
+    no_pool = ctypes.byref(_cache(L, exact_slot=16))
+    assert L.lib.wc_write_kv(no_pool, 0, 1, p, p, L.WC_BF16, 4, 0, p, p, p, None) == L.WC_EINVAL

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _snapshot(cache):
-    names = ["k_codes", "v_codes", "k_scale", "v_scale", "witness", "exact_slot", "exact_pool", "exact_scale"]
+    names = ["k_codes", "v_codes", "k_scale", "v_scale", "witness", "exact_slot", "exact_pool"]
     return {n: getattr(cache, n).clone() for n in names if getattr(cache, n) is not None}
 
 

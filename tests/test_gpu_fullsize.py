@@ -180,7 +180,7 @@ def test_decode_bench_size_sampled_against_oracle(scheme):
             assert np.all(np.abs(out["E_V"][b, hs] - r["E_V"]) <= MET_TOL * r["E_V"]), (b, g)
             assert np.all(out["E_V"][b, hs] >= r["dv_true"])
         rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
-        assert np.all(np.abs(rho - r["block_risk"]) <= 2e-4 * r["block_risk"] + 1e-30), (b, g)
+        assert np.all(np.abs(rho - r["block_risk"]) <= 1e-4 * r["block_risk"] + 1e-30), (b, g)
     del cache, k, v
     _free()
 
@@ -322,7 +322,7 @@ def test_gate_flow_64_ragged_fp8():
             P = -(-int(lens[b]) // 16)
             fx_ref = gate.rho_to_fx(r["block_risk"])
             got = rho_np[b, g * G:(g + 1) * G, :P].astype(np.float64)
-            assert np.all(np.abs(got - fx_ref) <= 2e-4 * np.maximum(fx_ref.astype(np.float64), 1)), (tau, b, g)
+            assert np.all(np.abs(got - fx_ref) <= 1e-4 * fx_ref.astype(np.float64) + 1), (tau, b, g)
         # the repaired cache: exact keys in the pool, witnesses zeroed, and the
         # sampled heads' outputs and meters against the oracle on the repaired
         # cache (repairs move the softmax too, so the new meter is re-measured,
@@ -347,11 +347,10 @@ def test_gate_flow_64_ragged_fp8():
             for j in sel_np[b, g, 1:1 + sel_np[b, g, 0]][:4]:
                 p = tab[b, j]
                 s = slots[p, g]
-                exact = k[starts[b] + 16 * j:starts[b] + 16 * j + 16, g].float().cpu().numpy().astype(np.float64)
-                pool = cache.exact_pool[s].cpu().numpy().astype(np.float64)
-                scale = cache.exact_scale[s].cpu().numpy().astype(np.float64)
+                exact = k[starts[b] + 16 * j:starts[b] + 16 * j + 16, g].view(torch.int16).cpu().numpy()
+                pool = cache.exact_pool[s].view(torch.int16).cpu().numpy()
                 rows = min(16, S_ - 16 * j)
-                assert np.array_equal((pool * scale[:, None])[:rows], exact[:rows])
+                assert np.array_equal(pool[:rows], exact[:rows])         # bf16 bit for bit
                 assert np.all(cache.witness[0, p, g].cpu().numpy() == 0)
         del cache
         _free()

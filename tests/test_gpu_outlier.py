@@ -124,7 +124,7 @@ def test_bypass_decode_parity(m, qdtype):
             _, r = sc.oracle(b, g)
             hs = slice(g * 7, (g + 1) * 7)
             rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
-            assert np.all(np.abs(rho - r["block_risk"]) <= 2e-4 * r["block_risk"] + 1e-30), (b, g)
+            assert np.all(np.abs(rho - r["block_risk"]) <= 1e-4 * r["block_risk"] + 1e-30), (b, g)
     # the bypass pays off on the x20-outlier keys: Tier B well below the plain cache's
     plain = Scenario(L.WC_DITHER_INT8, k, v, q, lens, "bf16", Hkv=4)
     pout = plain.decode(n_split=6, mask=3)

@@ -1,9 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
-Bars: codes, dither draws and gate decisions bit-exact; witness and meters
-within 1e-4 relative (Tier A's R plus the share of the witness rounding
-guard, which e^c amplifies once the meter saturates); attention output
-within 2e-3 relative L2; and the GPU meter never below the oracle's true TV.
+Bars: codes, dither draws and gate decisions bit-exact; witness, meters and
+block risks within 1e-4 relative; attention output within 2e-3 relative L2;
+and the GPU meter never below the oracle's true TV.
 """
 import math
 
@@ -151,14 +150,14 @@ def _check_decode(sc, out, n_check=None):
             assert np.all(err <= OUT_TOL), (b, g, err.max())
             assert np.all(np.abs(out["lse"][b, hs] - r["lse"]) <= 1e-4 * np.maximum(1, np.abs(r["lse"]))), (b, g)
             ra = out["R_A"][b, hs]
-            # The stored witness is the band norm rounded up by 1 + 2^-17 (the
-            # soundness guard of the write path) plus fp32 rounding (< 2^-20):
-            # every Tier A bound c_t rises by at most that fraction, which e^c
-            # turns into 2 (e^{c_max (2^-17 + 2^-20)} - 1) relative in
-            # R = E (1 + E/2).  Informative meters (small c) keep the 1e-4 bar;
-            # saturated ones (R >> 1, TV bound 1) get the guard's share on top.
-            guard = 2.0 * np.expm1((2.0**-17 + 2.0**-20) * r["a"].max(axis=1))
-            assert np.all(np.abs(ra - r["R_A"]) <= (MET_TOL + guard) * r["R_A"]), (b, g, ra, r["R_A"])
+            # The stored witness is the band norm rounded up by 1 + 2^-20 (the
+            # write path's soundness guard): every Tier A bound c_t rises by at
+            # most that fraction, which e^c turns into at most
+            # 2 (e^{c_max 2^-20} - 1) relative in R = E (1 + E/2) -- 2.2e-5 at
+            # the largest c_max of these cases (11.3, fp32 keys scaled up to 30
+            # under fp8, R ~ 1e8), so the plain 1e-4 bar holds for saturated
+            # meters too.
+            assert np.all(np.abs(ra - r["R_A"]) <= MET_TOL * r["R_A"]), (b, g, ra, r["R_A"])
             assert np.all(ra >= r["R_A"] * (1 - MET_TOL)), (b, g)
             assert np.all(ra >= r["tv_true"]), (b, g)
             # the tanh bound of Tier A: deterministic, sound
@@ -248,7 +247,7 @@ def test_block_risk_matches_oracle(scheme):
             hs = slice(g * sc.G, (g + 1) * sc.G)
             rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
             ref = r["block_risk"]
-            assert np.all(np.abs(rho - ref) <= 2e-4 * ref + 1e-30), (b, g)
+            assert np.all(np.abs(rho - ref) <= 1e-4 * ref + 1e-30), (b, g)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(32, 2), (9, 1), (8, 1)])
