@@ -57,6 +57,8 @@ def _load():
         "wc_write_kv_pages": [P, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, _i64, _i64, P, P, P, P],
         "wc_gate_pagein_tanh": [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_double,
                                 _i64, P, P, P, P, P, ctypes.c_size_t, P],
+        "wc_gate_pagein_noalloc": [P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
+                                   ctypes.c_double, _i64, P, P, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -74,8 +76,11 @@ def _load():
 lib = _load()
 
 EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
-           "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_workspace_bytes", "wc_dither_fill", "wc_outlier_select",
-           "wc_witness", "wc_write_kv_pages", "wc_last_error", "wc_version"]
+           "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_pagein_noalloc", "wc_gate_workspace_bytes",
+           "wc_dither_fill", "wc_outlier_select", "wc_witness", "wc_write_kv_pages", "wc_last_error", "wc_version"]
+
+# scratch of wc_gate_pagein_noalloc (the header's WC_GATE_NOALLOC_MAX_BYTES)
+GATE_NOALLOC_MAX_BYTES = 16 << 20
 
 
 def _check(fn, code):
@@ -241,6 +246,15 @@ def wc_gate_pagein(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, h
         _ptr(ctx_len),
         float(tau), int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged), _ptr(selected),
         _ptr(rho_fx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def wc_gate_pagein_noalloc(cache, layer, block_logrisk, lse, page_table, ctx_len, tau, host_exact_k, pool_used,
+                           bytes_paged, budget_blocks=-1, selected=None, rho_fx=None, meter=None, stream=None):
+    B, Hq, max_pages = block_logrisk.shape
+    _check("wc_gate_pagein_noalloc", lib.wc_gate_pagein_noalloc(
+        cache.ref(), layer, _ptr(block_logrisk), _ptr(lse), _ptr(meter), B, Hq, _ptr(page_table), max_pages,
+        _ptr(ctx_len), float(tau), int(budget_blocks), _ptr(host_exact_k), _ptr(pool_used), _ptr(bytes_paged),
+        _ptr(selected), _ptr(rho_fx), _stream(stream)))
 
 
 def wc_outlier_select(x, m, channels, stream=None):

@@ -35,6 +35,8 @@
 // exceeds c*, ranked by that bound; (2) is shared.
 #include <math.h>
 
+#include <mutex>
+
 #include "wc_common.h"
 
 namespace wc {
@@ -426,6 +428,11 @@ __global__ void __launch_bounds__(256) gate_copy_kernel(wc_cache c, GateArgs a, 
   }
 }
 
+// Scratch of wc_gate_pagein_noalloc: the workspace of wc_gate_pagein in a
+// file-scope device array (one copy per GPU, held until the process ends).
+constexpr size_t kScratchBytes = WC_GATE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 }  // namespace wc
 
 using namespace wc;
@@ -529,25 +536,25 @@ extern "C" int wc_gate_pagein_tanh(const wc_cache* cache, int layer, const float
   return check_launch("wc_gate_pagein_tanh copy");
 }
 
-extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
-                              const float* meter, int B, int Hq, const int32_t* page_table, int max_pages,
-                              const int32_t* ctx_len, double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
-                              int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
-                              void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int gate_pagein(const char* fn, const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                const float* meter, int B, int Hq, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                double tau, int64_t budget_blocks, const uint16_t* host_exact_k, int64_t* pool_used,
+                int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx, void* workspace, size_t ws_bytes,
+                void* stream) {
   if (!cache || (B != 0 && (!block_logrisk || !lse || !page_table || !ctx_len || !host_exact_k || !pool_used ||
                              !bytes_paged || !workspace))) {
-    set_error("wc_gate_pagein: null pointer");
+    set_error("%s: null pointer", fn);
     return WC_EINVAL;
   }
   const double et = sqrt(1.0 + 2.0 * tau) - 1.0;
   if (!(tau >= 0.0) || !(et < 64.0)) {
-    set_error("wc_gate_pagein: need 0 <= tau and sqrt(1 + 2 tau) - 1 < 64");
+    set_error("%s: need 0 <= tau and sqrt(1 + 2 tau) - 1 < 64", fn);
     return WC_EINVAL;
   }
   GateArgs a{};
   void* dev_host = nullptr;
-  if (int e = gate_prepare("wc_gate_pagein", cache, layer, B, Hq, max_pages, host_exact_k, workspace, ws_bytes,
-                           &dev_host, a))
+  if (int e = gate_prepare(fn, cache, layer, B, Hq, max_pages, host_exact_k, workspace, ws_bytes, &dev_host, a))
     return e;
   if (B == 0) return WC_OK;
   const wc_cache& c = *cache;
@@ -565,8 +572,76 @@ extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* blo
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(gate_select_kernel, dim3((unsigned)B, (unsigned)hkv), dim3(kGateThreads), 0, st, c, a,
                      (const int64_t*)pool_used);
-  if (int e = check_launch("wc_gate_pagein select")) return e;
+  if (int e = check_launch(fn)) return e;
   hipLaunchKernelGGL(gate_copy_kernel, dim3((unsigned)(B * hkv), 8u), dim3(256), 0, st, c, a,
                      (const uint16_t*)dev_host, B * hkv, c.pool_capacity, pool_used, bytes_paged, selected);
-  return check_launch("wc_gate_pagein copy");
+  return check_launch(fn);
+}
+
+// The device address of `scratch` on each device, looked up once per device
+// (with that device current) on its first use.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_ptr(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    set_error("%s: no current HIP device", fn);
+    return WC_EHIP;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      set_error("%s: hipGetSymbolAddress of the scratch array failed: %s", fn, hipGetErrorString(e));
+      return WC_EHIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return WC_OK;
+}
+}  // namespace
+
+extern "C" int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                              const float* meter, int B, int Hq, const int32_t* page_table, int max_pages,
+                              const int32_t* ctx_len, double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
+                              int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return gate_pagein("wc_gate_pagein", cache, layer, block_logrisk, lse, meter, B, Hq, page_table, max_pages, ctx_len,
+                     tau, budget_blocks, host_exact_k, pool_used, bytes_paged, selected, rho_fx, workspace, ws_bytes,
+                     stream);
+}
+
+extern "C" int wc_gate_pagein_noalloc(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                                      const float* meter, int B, int Hq, const int32_t* page_table, int max_pages,
+                                      const int32_t* ctx_len, double tau, int64_t budget_blocks,
+                                      const uint16_t* host_exact_k, int64_t* pool_used, int64_t* bytes_paged,
+                                      int32_t* selected, uint64_t* rho_fx, void* stream) {
+  const char* fn = "wc_gate_pagein_noalloc";
+  if (!cache) {
+    set_error("%s: null pointer", fn);
+    return WC_EINVAL;
+  }
+  if (B < 0 || max_pages < 0 || cache->num_kv_heads < 1) {
+    set_error("%s: bad B/max_pages/num_kv_heads", fn);
+    return WC_EINVAL;
+  }
+  const size_t need = wc_gate_workspace_bytes(B, cache->num_kv_heads, max_pages);
+  if (need > kScratchBytes) {
+    set_error("%s: needs %zu bytes of scratch for B=%d, Hkv=%d, max_pages=%d; the static scratch holds %zu", fn,
+              need, B, cache->num_kv_heads, max_pages, kScratchBytes);
+    return WC_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  if (B != 0) {
+    if (int e = scratch_ptr(fn, &ws)) return e;
+  }
+  return gate_pagein(fn, cache, layer, block_logrisk, lse, meter, B, Hq, page_table, max_pages, ctx_len, tau,
+                     budget_blocks, host_exact_k, pool_used, bytes_paged, selected, rho_fx, ws, kScratchBytes,
+                     stream);
 }

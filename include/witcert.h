@@ -374,6 +374,27 @@ int wc_gate_pagein(const wc_cache* cache, int layer, const float* block_logrisk,
                    int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * wc_gate_pagein_noalloc -- wc_gate_pagein for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks, kernels and outputs, without the
+ * workspace.  Its scratch (the workspace wc_gate_pagein takes) is a static
+ * device array of WC_GATE_NOALLOC_MAX_BYTES in the library, one copy per GPU,
+ * held until the process ends; its device address is looked up once per
+ * device, on the first call with that device current.  A call whose
+ * wc_gate_workspace_bytes(B, Hkv, max_pages) exceeds the array returns
+ * WC_EWORKSPACE before any launch.  The call allocates nothing (no hipMalloc,
+ * no hipFree).  Every call on one GPU shares its array: calls that overlap on
+ * one GPU (different streams or threads without ordering) race; calls ordered
+ * on one stream do not (each call writes everything it later reads).
+ */
+#define WC_GATE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int wc_gate_pagein_noalloc(const wc_cache* cache, int layer, const float* block_logrisk, const float* lse,
+                           const float* meter, int B, int Hq, const int32_t* page_table, int max_pages,
+                           const int32_t* ctx_len, double tau, int64_t budget_blocks, const uint16_t* host_exact_k,
+                           int64_t* pool_used, int64_t* bytes_paged, int32_t* selected, uint64_t* rho_fx,
+                           void* stream);
+
 /* Bytes of the gate workspace for B sequences, Hkv heads and max_pages blocks:
  * the selection (4 B per block), the counts, the pool counter and two sort
  * buffers (8 B per block each). */

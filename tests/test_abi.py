@@ -262,3 +262,20 @@ def test_caches_with_an_exact_pool_take_bf16_keys():
                             L.WC_F32, 0, 0, p, 1, None) == L.WC_OK
     no_pool = ctypes.byref(_cache(L, exact_slot=16))
     assert L.lib.wc_write_kv(no_pool, 0, 1, p, p, L.WC_BF16, 4, 0, p, p, p, None) == L.WC_EINVAL
+
+
+def test_noalloc_gate_limit_and_refusal():
+    """The header's WC_GATE_NOALLOC_MAX_BYTES is the binding's constant, and a
+    request beyond it is refused on the host (WC_EWORKSPACE) before any
+    device call."""
+    L = _lib()
+    txt = open(os.path.join(ROOT, "include", "witcert.h")).read()
+    m = re.search(r"#define WC_GATE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.GATE_NOALLOC_MAX_BYTES
+    p = ctypes.c_void_p(16)
+    c = ctypes.byref(_cache(L, scheme=1, **POOL))
+    assert L.wc_gate_workspace_bytes(64, 4, 65536) > L.GATE_NOALLOC_MAX_BYTES
+    rc = L.lib.wc_gate_pagein_noalloc(c, 0, p, p, None, 64, 28, p, 65536, p, 0.2, -1, p, p, p, None, None, None)
+    assert rc == L.WC_EWORKSPACE and b"scratch" in L.lib.wc_last_error()
+    assert L.lib.wc_gate_pagein_noalloc(None, 0, p, p, None, 2, 28, p, 8, p, 0.2, -1, p, p, p, None, None,
+                                        None) == L.WC_EINVAL
