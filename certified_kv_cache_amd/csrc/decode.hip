@@ -123,6 +123,8 @@ __device__ __forceinline__ float max4k(float v) {
   auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return vmax(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
+// Maximum over the whole wave: within each 16-lane row, then across rows.
+__device__ __forceinline__ float wave_max64(float v) { return max4k(row16_max(v)); }
 __device__ __forceinline__ float sum4k(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -408,7 +410,10 @@ constexpr int decode_waves_per_simd() {
 // compacted on two tokens per lane (lanes n + 8 take tokens 2, 3 of head n).
 // NO4: outlier bypass with m = 4 NO4 exact key channels (0 = none).
 // MV: the value certificate (reads the value witnesses).
-template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4, bool MV>
+// MODE: the meter configuration fixed at compile time (kModeRuntime: read
+// from the arguments), so the common launches carry no flag tests.
+constexpr int kModeRuntime = 0, kModeOff = 1, kModeOn = 2;
+template <int SCHEME, bool QF32, bool CMP, bool SOFF, int NO4, bool MV, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<SCHEME, QF32, NO4>())))
 decode_kernel(wc_cache c, DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -420,10 +425,15 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const int S = a.ctx_len[b];
   const int P = (S + 15) >> 4;
   const int p0 = (int)((int64_t)split * P / a.n_split), p1 = (int)((int64_t)(split + 1) * P / a.n_split);
-  const bool meterA = (a.mask & WC_METER_A) != 0;
-  const bool meterB = SCHEME == WC_DITHER_INT8 && (a.mask & WC_METER_B) != 0;
+  // fixed modes: off; Tier A (+ B for dithered INT8)
+  const bool meterA = MODE == kModeRuntime ? (a.mask & WC_METER_A) != 0 : MODE != kModeOff;
+  const bool meterB = SCHEME == WC_DITHER_INT8 &&
+                      (MODE == kModeRuntime ? (a.mask & WC_METER_B) != 0 : MODE != kModeOff);
+  // (the block output stays a run-time test: with it fixed, the compiler's
+  // schedule of the risk path needs more registers than three waves per SIMD
+  // allow, and spills)
   const bool risk = a.block_logrisk != nullptr;
-  const bool riskmax = (a.mask & WC_BLOCK_CMAX) != 0;   // block output: max c instead of log risk
+  const bool riskmax = MODE == kModeRuntime && (a.mask & WC_BLOCK_CMAX) != 0;   // block output: max c, not log risk
 
   // ---------------------------------------------------------------- query prep
   // lane (n, k) holds channels 32k..32k+31 of head n.
@@ -603,6 +613,9 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const float kappa = a.sm_scale * sqrtf(NO4 > 0 ? qz2 : qn2) * sqrtf(fmaxf(logterm, 0.0f) / 6.0f);
 
   const uint32_t key = SCHEME == WC_DITHER_INT8 ? stream_key(a.seed[b], (uint32_t)a.layer, (uint32_t)g) : 0u;
+  // LCG state of the lane's first counter on logical page 0, key + 64 n + 16 k
+  // (page jj adds 1024 jj counters: a wave-uniform constant times kPcgMul)
+  const uint32_t st_lane = (key + (uint32_t)(64 * n + 16 * kq)) * kPcgMul + kPcgInc;
   // compacted softmax: lane (n, k) evaluates head n & 7, tokens 4k + r0, +1
   constexpr int NV = CMP ? 2 : 4;
   const int r0 = CMP ? 2 * (n >> 3) : 0;
@@ -626,7 +639,12 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   float (*sR)[16] = sRisk[wave];
 
   // ---------------------------------------------------------------- state
+  // m_ref: the running max of the logits (log2 units) minus sig, the
+  // value-range offset (INT8 caches; 0 otherwise); sv_ref: the largest value
+  // scale seen so far (wave-uniform)
   float m_ref = -INFINITY, l_run = 0.0f, na = 0.0f, nb = 0.0f;
+  float sig = 0.0f, sv_ref = 0.0f;
+  float m_lim = -INFINITY;                     // the running max plus the rescale slack
   float ca_max = 0.0f, cb_max = 0.0f;          // largest per-token bound of each tier (tanh bound)
   float nvv = 0.0f;                            // value certificate: sum 2^(l2 - m) ||v^ - v||
   f4 O[8];
@@ -710,7 +728,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     // LCG state of the lane's first counter, key + 64 token + 16 k; the
     // other 15 counters are consecutive (their states differ by constants)
-    const uint32_t st0 = (key + (uint32_t)(64 * (tok0 + n) + 16 * kq)) * kPcgMul + kPcgInc;
+    const uint32_t st0 = st_lane + (uint32_t)jj * (1024u * kPcgMul);
     // draws of token n, channels 32k + 8j .. +7, as fp16 pairs -(4 + hb 2^-8)
     // and -(2^-6 + lb 2^-16) of the high and low byte; the high ones are
     // published to LDS for the values
@@ -849,16 +867,34 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       svmax = vmax(svmax, vmax(sv[2], sv[3]));
     }
     // (bitwise, so that the test compiles to compares and mask logic, not branches)
-    const bool need = (lmax > m_ref + kRescaleSlack) | ((svmax > 128.0f) & (lmax > m_ref));
+    // (a value scale above the largest seen so far also rescales: the
+    // weights p s_v fed to the fp16 PV operand are kept in range by taking
+    // m_ref = the running max minus sig, with the wave-uniform sig chosen so
+    // that s_max 2^sig lies in (64, 128]: then p s_v <= 2^8 2^7 and the
+    // weights of the largest scales stay far above fp16's subnormals.  Every
+    // sum is taken relative to m_ref, so sig cancels in o, LSE and the meters.)
+    const bool need_m = lmax > m_lim;
+    const bool need = int8_codes<SCHEME>() ? need_m | (svmax > sv_ref) : need_m;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      float tmax = lmax, anyn = need ? 1.0f : 0.0f;
+      float tmax = lmax, anyn = need_m ? 1.0f : 0.0f;
       if (CMP) {
         tmax = vmax_ror8(tmax);
         anyn = vmax_ror8(anyn);
       }
       tmax = max4k(tmax);
       anyn = max4k(anyn);
-      const float m_new = anyn > 0.0f ? tmax : m_ref;
+      float m_new = anyn > 0.0f ? tmax - sig : m_ref;
+      if (int8_codes<SCHEME>()) {
+        const float smax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max64(svmax))));
+        if (smax > sv_ref) {
+          int e;
+          frexpf(smax, &e);                    // smax in [2^(e-1), 2^e): 2^(7-e) smax in [64, 128)
+          const float sig_new = (float)(7 - e);
+          m_new += sig - sig_new;              // the same running max, the new offset
+          sig = sig_new;
+          sv_ref = smax;
+        }
+      }
       const float alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
       l_run *= alpha;
       na *= alpha;
@@ -868,14 +904,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) O[t] *= alpha;
       m_ref = m_new;
+      m_lim = m_new + sig + kRescaleSlack;
     }
-    float p[4], dl[4], psum = 0.0f;
+    float p[4], dl[4];
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       dl[r] = l2[r] - m_ref;
       p[r] = __builtin_amdgcn_exp2f(dl[r]);
-      psum += p[r];
     }
+    float psum = p[0];
+#pragma unroll
+    for (int r = 1; r < NV; ++r) psum += p[r];
     l_run += psum;
     if (MV) {                                  // repaired blocks too: their values stay quantized
 #pragma unroll
@@ -935,10 +974,13 @@ decode_kernel(wc_cache c, DecodeArgs a) {
         cm = max4k(cm);
         if (kq == 0 && n < G) sR[n][i & 15] = cm;
       } else {
+        // (every lane writes: the four k lanes of head n hold the same sum,
+        // and rows n >= G of the tile are never read; the terms are >= 0, so
+        // a riskless block gets log 0 = -inf)
         float er = meterB ? eb : ea;
         if (CMP) er += dpp_ror8(er);
         er = sum4k(er);
-        if (kq == 0 && n < G) sR[n][i & 15] = er > 0.0f ? (__builtin_amdgcn_logf(er) + m_ref) * kLn2 : -INFINITY;
+        sR[n][i & 15] = (__builtin_amdgcn_logf(er) + m_ref) * kLn2;
       }
     }
 
@@ -1269,39 +1311,53 @@ extern "C" size_t wc_decode_workspace_bytes(int B, int Hq, int n_split) {
   return (size_t)B * Hq * n_split * kPartial * sizeof(float);
 }
 
-// Host dispatch from the run-time shape to the template instance.
+// Host dispatch from the run-time shape to the template instance.  The meter
+// configurations of the common shape (bf16 query, group <= 8, 32-bit layer
+// offsets, no bypass, no value certificate) have instances of their own.
 template <int SCH, bool QF, bool CM, bool SO, int NO>
-static void launch_mv(bool mv, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
+static void launch_mv(bool mv, int mode, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
+  if constexpr (!QF && CM && SO && NO == 0) {
+    if (!mv && mode == kModeOff) {
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false, kModeOff>), grid, dim3(kThreads), 0, st, c, a);
+      return;
+    }
+    if (!mv && mode == kModeOn) {
+      hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false, kModeOn>), grid, dim3(kThreads), 0, st, c, a);
+      return;
+    }
+  }
   if (mv)
-    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, true>), grid, dim3(kThreads), 0, st, c, a);
+    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, true, kModeRuntime>), grid, dim3(kThreads), 0, st, c, a);
   else
-    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false>), grid, dim3(kThreads), 0, st, c, a);
+    hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false, kModeRuntime>), grid, dim3(kThreads), 0, st, c, a);
 }
 template <int SCH, bool QF, bool CM, bool SO>
-static void launch_no(int no4, bool mv, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
+static void launch_no(int no4, bool mv, int mode, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
   if constexpr (SCH == WC_DITHER_INT8) {
-    if (no4 == 2) return launch_mv<SCH, QF, CM, SO, 2>(mv, grid, st, c, a);
-    if (no4 == 4) return launch_mv<SCH, QF, CM, SO, 4>(mv, grid, st, c, a);
+    if (no4 == 2) return launch_mv<SCH, QF, CM, SO, 2>(mv, mode, grid, st, c, a);
+    if (no4 == 4) return launch_mv<SCH, QF, CM, SO, 4>(mv, mode, grid, st, c, a);
   }
-  launch_mv<SCH, QF, CM, SO, 0>(mv, grid, st, c, a);
+  launch_mv<SCH, QF, CM, SO, 0>(mv, mode, grid, st, c, a);
 }
 template <int SCH, bool QF>
-static void launch_shape(bool cm, bool so, int no4, bool mv, dim3 grid, hipStream_t st, const wc_cache& c,
+static void launch_shape(bool cm, bool so, int no4, bool mv, int mode, dim3 grid, hipStream_t st, const wc_cache& c,
                          const DecodeArgs& a) {
   if (cm) {
-    if (so) launch_no<SCH, QF, true, true>(no4, mv, grid, st, c, a); else launch_no<SCH, QF, true, false>(no4, mv, grid, st, c, a);
+    if (so) launch_no<SCH, QF, true, true>(no4, mv, mode, grid, st, c, a);
+    else launch_no<SCH, QF, true, false>(no4, mv, mode, grid, st, c, a);
   } else {
-    if (so) launch_no<SCH, QF, false, true>(no4, mv, grid, st, c, a); else launch_no<SCH, QF, false, false>(no4, mv, grid, st, c, a);
+    if (so) launch_no<SCH, QF, false, true>(no4, mv, mode, grid, st, c, a);
+    else launch_no<SCH, QF, false, false>(no4, mv, mode, grid, st, c, a);
   }
 }
 template <bool QF>
-static void launch_scheme(int scheme, bool cm, bool so, int no4, bool mv, dim3 grid, hipStream_t st,
+static void launch_scheme(int scheme, bool cm, bool so, int no4, bool mv, int mode, dim3 grid, hipStream_t st,
                           const wc_cache& c, const DecodeArgs& a) {
   switch (scheme) {
-    case WC_DITHER_INT8: launch_shape<WC_DITHER_INT8, QF>(cm, so, no4, mv, grid, st, c, a); break;
-    case WC_FP8_E4M3: launch_shape<WC_FP8_E4M3, QF>(cm, so, no4, mv, grid, st, c, a); break;
-    case WC_RTN_INT8: launch_shape<WC_RTN_INT8, QF>(cm, so, no4, mv, grid, st, c, a); break;
-    default: launch_shape<WC_BF16_STORE, QF>(cm, so, no4, mv, grid, st, c, a); break;
+    case WC_DITHER_INT8: launch_shape<WC_DITHER_INT8, QF>(cm, so, no4, mv, mode, grid, st, c, a); break;
+    case WC_FP8_E4M3: launch_shape<WC_FP8_E4M3, QF>(cm, so, no4, mv, mode, grid, st, c, a); break;
+    case WC_RTN_INT8: launch_shape<WC_RTN_INT8, QF>(cm, so, no4, mv, mode, grid, st, c, a); break;
+    default: launch_shape<WC_BF16_STORE, QF>(cm, so, no4, mv, mode, grid, st, c, a); break;
   }
 }
 
@@ -1403,10 +1459,15 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   const bool soff = (uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * page_b <= 0xFFFFFFFFull;
   const int no4 = c.scheme == WC_DITHER_INT8 ? c.num_outliers / 4 : 0;
   const bool mv = (meter_mask & WC_METER_V) != 0;
+  // the fixed meter configurations: off; on (Tier A, and B for dithered INT8)
+  const unsigned full = c.scheme == WC_DITHER_INT8 ? (WC_METER_A | WC_METER_B) : WC_METER_A;
+  int mode = kModeRuntime;
+  if (meter_mask == 0) mode = kModeOff;
+  else if (meter_mask == full) mode = kModeOn;
   if (q_dtype == WC_BF16)
-    launch_scheme<false>(c.scheme, cmp, soff, no4, mv, grid, st, c, a);
+    launch_scheme<false>(c.scheme, cmp, soff, no4, mv, mode, grid, st, c, a);
   else
-    launch_scheme<true>(c.scheme, cmp, soff, no4, mv, grid, st, c, a);
+    launch_scheme<true>(c.scheme, cmp, soff, no4, mv, mode, grid, st, c, a);
   return check_launch("wc_decode_attn_meter");
 }
 

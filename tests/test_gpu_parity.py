@@ -262,3 +262,36 @@ def test_decode_group_sizes(Hq, Hkv):
     sc = Scenario(L.WC_DITHER_INT8, d["k"], d["v"], q, lens, "bf16", Hkv=Hkv)
     out = sc.decode(n_split=3, mask=3)
     _check_decode(sc, out)
+
+
+@pytest.mark.parametrize("scheme", ["int8", "rtn"])
+@pytest.mark.parametrize("scales", ["small", "large", "mixed"])
+def test_decode_small_and_large_value_scales(scheme, scales):
+    """Value rows whose absmax spans [1e-3, 1e-2] (small), about 1e4 (large),
+    or [1e-3, 1e4] within one sequence (mixed): the attention weights times the
+    value scales, fed to the fp16 PV operand, must stay in fp16's range (the
+    kernel offsets its running max by a power of two chosen from the largest
+    value scale), so the output keeps the 2e-3 bar."""
+    L = H.need_gpu()
+    _flush(f"value scales {scales} {scheme}")
+    lens = [700, 129, 33]
+    n = sum(lens)
+    k, v, _ = _ragged_layer(21, lens)
+    q = inputs.layer(seed=22, S=1, batch=len(lens))["q"]
+    rng = np.random.default_rng(23)
+    lo, hi = {"small": (1e-3, 1e-2), "large": (5e3, 2e4), "mixed": (1e-3, 1e4)}[scales]
+    target = np.exp(rng.uniform(np.log(lo), np.log(hi), (n, 4, 1)))
+    v32 = inputs.bf16_bits_to_f32(v).astype(np.float64)
+    v32 = v32 / np.max(np.abs(v32), axis=-1, keepdims=True) * target
+    vb = inputs.f32_to_bf16_bits(v32.astype(np.float32))
+    sch = L.WC_DITHER_INT8 if scheme == "int8" else L.WC_RTN_INT8
+    sc = Scenario(sch, k, vb, q, lens, "bf16", Hkv=4)
+    for n_split in (1, 3):
+        out = sc.decode(n_split=n_split, mask=3 if scheme == "int8" else 1)
+        for b in range(len(lens)):
+            for g in range(4):
+                _, r = sc.oracle(b, g)
+                hs = slice(g * sc.G, (g + 1) * sc.G)
+                err = H.rel_l2(out["o"][b, hs], r["o_tilde"])
+                assert np.all(err <= OUT_TOL), (scales, n_split, b, g, err.max())
+                assert np.all(np.abs(out["R_A"][b, hs] - r["R_A"]) <= MET_TOL * r["R_A"]), (b, g)
