@@ -106,13 +106,21 @@ def fp8_variant(w, B, S, iters):
         L.wc_decode_attn_meter(cache, 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    t = time_modes(decode, iters, {"risk": dict(mask=1, with_risk=True), "on": dict(mask=1, with_risk=False),
-                                   "off": dict(mask=0, with_risk=False)}, warm=60)
+    floor = make_floor(w, B, cache)
+
+    def run(mask=1, with_risk=True, fl=False):
+        if fl:
+            floor(mask=mask)
+        else:
+            decode(mask, with_risk)
+
+    t = time_modes(run, iters, {"risk": dict(mask=1, with_risk=True), "on": dict(mask=1, with_risk=False),
+                                "off": dict(mask=0, with_risk=False), "floor": dict(mask=1, fl=True)}, warm=60)
     t_risk, t_on, t_off = t["risk"], t["on"], t["off"]
     nb = decode_bytes(B, S, True, scales=False)
     del cache
     return {"decode_us": round(t_risk, 2), "decode_meter_on_us": round(t_on, 2), "decode_meter_off_us": round(t_off, 2),
-            "meter_overhead": round(t_on / t_off - 1, 4), "decode_bytes": nb,
+            "meter_overhead": round(t_on / t_off - 1, 4), "decode_bytes": nb, "load_floor_us": round(t["floor"], 2),
             "achieved_GBps": round(nb / (t_risk * 1e-6) / 1e9, 1), "frac": round(nb / (t_risk * 1e-6) / 1e9 / PEAK_GBS, 4)}
 
 
@@ -263,6 +271,19 @@ def make_step(w, B, S):
                          meter=rb)
 
     return step, decode, dict(o=o, lse=lse, ra=ra, rb=rb, paged=paged)
+
+
+def make_floor(w, B, cache):
+    """Launcher of the decode's load floor on `cache` (same page table and
+    splits as the decode)."""
+    import torch
+    L = w["L"]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def floor(mask=3, match=True):
+        L.wc_decode_load_floor(cache, 0, HQ, w["tab"], w["ctx"], NSPLIT, mask, sink, match_residency=match)
+
+    return floor
 
 
 def time_modes(decode, iters, modes, rounds=3, warm=20):
@@ -652,6 +673,63 @@ def decode_bytes_ragged(lens, scales=True):
     return int(sum(int(S_) * HKV * per_tok + (-(-int(S_) // 16)) * 4 for S_ in lens)) + len(lens) * (HQ * D * 2 + 12)
 
 
+HEADLINE_KERNEL = "decode_kernel<0, false, true, true, 0, false, 2>"
+FLOOR_KERNEL = "decode_floor_kernel<0, true>"
+
+
+def _counter_rows(d):
+    """(kernel name, grid size, dispatch id, counter, value) of every row of
+    the rocprofv3 counter_collection CSVs under directory d."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                k = {c.lower(): c for c in r}
+                rows.append((r[k["kernel_name"]], int(r[k["grid_size"]]), int(r[k["dispatch_id"]]),
+                             r[k["counter_name"]], float(r[k["counter_value"]])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def reduce_counters(fetch_dir, write_dir, launches, B, S):
+    """HBM bytes per launch of the headline decode from two rocprofv3 --pmc
+    runs of bench.py (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by what the same counter reads for the 1 GiB device copies that
+    --copy-ref adds (1 GiB read and 1 GiB written per copy).  The decode's
+    figure is the mean over its first `launches` dispatches (the warm-up and
+    timed steps); the load floor's over all its dispatches."""
+    import numpy as np
+    out = {"source_sha": decode_source_sha(), "batch": B, "ctx": S, "launches": launches}
+    total = 0.0
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[3] == name]
+        copies = [r for r in rows if "copyBuffer" in r[0]]
+        if not copies:
+            raise SystemExit(f"{name}: no device copy dispatches (run bench.py with --copy-ref)")
+        gmax = max(r[1] for r in copies)
+        ref_kib = float(np.median([r[4] for r in copies if r[1] == gmax]))
+        factor = (1 << 20) / ref_kib                    # KiB that 1 GiB moves
+        dec = sorted((r for r in rows if HEADLINE_KERNEL in r[0]), key=lambda r: r[2])[:launches]
+        flo = [r for r in rows if FLOOR_KERNEL in r[0]]
+        if len(dec) < launches:
+            raise SystemExit(f"{name}: {len(dec)} headline decode dispatches, expected {launches}")
+        kib = float(np.mean([r[4] for r in dec]))
+        key = name.split("_")[0].lower()
+        out[f"{key}_factor"] = factor
+        out[f"{key}_copy_ref_KiB"] = ref_kib
+        out[f"{key}_KiB_per_launch"] = kib
+        out[f"{key}_bytes_per_launch"] = int(round(kib * 1024 * factor))
+        if flo:
+            out[f"floor_{key}_bytes_per_launch"] = int(round(float(np.mean([r[4] for r in flo])) * 1024 * factor))
+        total += kib * 1024 * factor
+    out["hbm_bytes_per_launch"] = int(round(total))
+    out["algorithmic_bytes_per_launch"] = decode_bytes(B, S, True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -671,7 +749,17 @@ def main():
                          "latency: decode + merge latency at the two parity sizes; "
                          "decode-bounds: the decode with its cache in HBM and L2-resident (compute alone)")
     ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
+    ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of "
+                         "`bench.py --steps K --warmup W --no-cpu --copy-ref` (same K, W, --batch, --ctx given here) "
+                         "into the headline decode's HBM bytes per launch, written to " + COUNTERS)
     args = ap.parse_args()
+    if args.reduce_counters:
+        res = reduce_counters(*args.reduce_counters, args.warmup + args.steps, args.batch, args.ctx)
+        with open(COUNTERS, "w") as fh:
+            json.dump(res, fh, indent=1)
+        print(json.dumps(res), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: runs on one GPU (sequences and KV heads shard without communication), "
               "so --gpus must be 1", file=sys.stderr)
@@ -712,15 +800,19 @@ def main():
     # GPU's clocks over the run falls on all three alike; median and p10-p90
     # of the loop means
     iters = max(args.steps, 10)
-    loops, on_loops, off_loops = [], [], []
+    floor = make_floor(w, B, w["cache"])
+    loops, on_loops, off_loops, floor_loops = [], [], [], []
     for _ in range(10):
         loops.append(time_decode(decode, iters, mask=3, with_risk=True))
         on_loops.append(time_decode(decode, iters, mask=3, with_risk=False))
         off_loops.append(time_decode(decode, iters, mask=0, with_risk=False))
+        floor_loops.append(time_decode(floor, iters, mask=3, match=True))
     loops.sort()
     t_risk = float(np.median(loops))
     t_on = float(np.median(on_loops))
     t_off = float(np.median(off_loops))
+    t_floor = float(np.median(floor_loops))
+    fl = time_modes(floor, iters, {"free": dict(mask=3, match=False), "off": dict(mask=0, match=True)}, warm=20)
     dec_step_us = t_risk
     bytes_on = decode_bytes(B, S, True)
     ach = bytes_on / (dec_step_us * 1e-6) / 1e9
@@ -730,19 +822,6 @@ def main():
         if cnt.get("source_sha") == decode_source_sha() and cnt.get("batch") == B and cnt.get("ctx") == S:
             traffic = cnt.get("hbm_bytes_per_launch")
     value = step_bytes(B, S) / (ms_step * 1e-3) / 1e9
-    # measured device copy peak (1 GiB read + 1 GiB written per copy)
-    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ca.record()
-    for _ in range(10):
-        dst.copy_(src)
-    cb.record()
-    torch.cuda.synchronize()
-    copy_peak = 2 * src.numel() * 4 / (ca.elapsed_time(cb) / 10 * 1e-3) / 1e9
-    del src, dst
     props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -762,7 +841,12 @@ def main():
         "pct_peak": round(100 * ach / PEAK_GBS, 2),
         "kv_tokens_per_s": round(B * S / (dec_step_us * 1e-6), 1),
         "decode_steps_per_s_per_layer": round(1e6 / dec_step_us, 1),
-        "copy_peak_GBps": round(copy_peak, 1), "pct_copy_peak": round(100 * ach / copy_peak, 2),
+        "load_floor": {"us": round(t_floor, 2), "GBps": round(bytes_on / (t_floor * 1e-6) / 1e9, 1),
+                       "decode_pct_of_floor": round(100 * t_floor / dec_step_us, 2),
+                       "us_without_lds_reservation": round(fl["free"], 2), "meter_off_us": round(fl["off"], 2),
+                       "what": "wc_decode_load_floor: the decode's page loads (codes, scales, witness, page "
+                               "table) on the same grid, no arithmetic; 10 loops taken in turn with the "
+                               "decode's, median"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count},
         "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),

@@ -49,6 +49,8 @@ def _load():
                                  P, P, ctypes.c_float, ctypes.c_uint, ctypes.c_double, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P, P],
         "wc_lse_merge": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P],
+        "wc_decode_load_floor": [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int,
+                                 ctypes.c_uint, ctypes.c_int, P, P],
         "wc_gate_pagein": [P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
                            ctypes.c_double, _i64, P, P, P, P, P, P, ctypes.c_size_t, P],
         "wc_dither_fill": [_u64, ctypes.c_int, ctypes.c_int, _i64, _i64, P, P],
@@ -75,7 +77,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge",
+EXPORTS = ["wc_write_kv", "wc_decode_attn_meter", "wc_decode_workspace_bytes", "wc_lse_merge", "wc_decode_load_floor",
            "wc_gate_pagein", "wc_gate_pagein_tanh", "wc_gate_pagein_noalloc", "wc_gate_workspace_bytes",
            "wc_dither_fill", "wc_outlier_select", "wc_witness", "wc_write_kv_pages", "wc_last_error", "wc_version"]
 
@@ -225,6 +227,14 @@ def wc_decode_attn_meter(cache, layer, q, page_table, ctx_len, seed, partials, s
         cache.ref(), layer, _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[1],
         _ptr(ctx_len), _ptr(seed), float(sm_scale), int(meter_mask), float(delta_req), L, H, T, n_split,
         _ptr(partials), partials.numel() * partials.element_size(), _ptr(block_logrisk), _stream(stream)))
+
+
+def wc_decode_load_floor(cache, layer, Hq, page_table, ctx_len, n_split, meter_mask, sink, match_residency=True,
+                         stream=None):
+    assert page_table.is_contiguous()
+    _check("wc_decode_load_floor", lib.wc_decode_load_floor(
+        cache.ref(), layer, page_table.shape[0], Hq, _ptr(page_table), page_table.shape[1], _ptr(ctx_len), n_split,
+        int(meter_mask), int(bool(match_residency)), _ptr(sink), _stream(stream)))
 
 
 def wc_lse_merge(partials, B, Hq, n_split, o, lse, meter_a=None, meter_b=None, tanh_a=None, tanh_b=None,

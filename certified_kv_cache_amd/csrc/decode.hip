@@ -377,6 +377,15 @@ __device__ __forceinline__ float expm1_fast(float c) {
   return c < 0.03125f ? p : e;
 }
 
+// p (e^c - 1) for a bound c in [0, 1/4): p c (1 + c/2 + c^2/6 + c^3/24 +
+// c^4/120 + c^5/720), whose truncation error is below c^6/5040 < 5e-8
+// relative, under the fp32 rounding; no exp and no cancellation.
+__device__ __forceinline__ float p_expm1_small(float p, float c) {
+  const float t = fmaf(c, fmaf(c, fmaf(c, fmaf(c, fmaf(c, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f), 1.0f / 6.0f),
+                                0.5f), 1.0f);
+  return (p * c) * t;
+}
+
 __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -437,25 +446,89 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 
   // ---------------------------------------------------------------- query prep
   // lane (n, k) holds channels 32k..32k+31 of head n.
+  // (the query's words are requested first and converted after the first
+  // page-table batch and page are requested, so that the latencies overlap)
+  uint4 qw[8];
+  if (hv) {
+    const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) +
+                                                     (((int64_t)b * a.Hq + h) * 128 + 32 * kq) * (QF32 ? 4 : 2));
+#pragma unroll
+    for (int i = 0; i < (QF32 ? 8 : 4); ++i) qw[i] = qp[i];
+  }
+  const int r0 = CMP ? 2 * (n >> 3) : 0;
+  LaneOff lo;
+  lo.k = (uint32_t)(16 * lane);
+  lo.s = (uint32_t)(4 * (4 * kq + r0));
+  lo.w = meterA ? (uint32_t)(4 * (8 * n + 2 * kq)) : lo.k;
+  lo.v = (uint32_t)(16 * lane);
+  lo.o = (uint32_t)(2 * NO4 * (4 * n + kq));
+  // Each wave takes a contiguous quarter of the split's pages: page i of
+  // this wave is page w0 + i.  Its physical page and exact-pool slot come
+  // from lane i % 64 of a batch read once per 64 pages, so the loop never
+  // waits on a page-table read.  The first batch and page are requested
+  // before the query is prepared, so that their latency overlaps it.
+  const int per = (p1 - p0 + kNW - 1) / kNW;
+  const int w0 = p0 + wave * per;
+  const int npw = max(0, min(p1, w0 + per) - w0);
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int64_t pg_base = (int64_t)a.layer * c.num_pages;
+  LayerBufs lb;
+  if (SOFF) {
+    const int64_t lph = c.num_pages * c.num_kv_heads;     // page-head blocks per layer
+    const int64_t l0 = (int64_t)a.layer * lph;
+    constexpr int64_t PB = page_bytes<SCHEME>();
+    lb.k = layer_rsrc(c.k_codes, l0 * PB, (uint64_t)lph * PB);
+    lb.v = layer_rsrc(c.v_codes, l0 * PB, (uint64_t)lph * PB);
+    lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
+    lb.o = lb.ks = lb.vs = lb.wv = lb.k;       // (unused unless set below)
+    if (MV) lb.wv = layer_rsrc(c.v_witness, l0 * 64, (uint64_t)lph * 64);
+    if (NO4 > 0) lb.o = layer_rsrc(c.k_outlier, l0 * (128 * NO4), (uint64_t)lph * (128 * NO4));
+    if (int8_codes<SCHEME>()) {
+      lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
+      lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
+    }
+  }
+  int bphys = 0, bslot = -1;
+  auto batch = [&](int i0) {
+    const int i = i0 + lane;
+    const int ph = i < npw ? ptab[w0 + i] : 0;
+    bphys = settle(ph);                        // the page loads wait for these, in this rare branch
+    // the slots are gathered next to the page loads; with one page in
+    // flight they are read when the page is processed, so the first page's
+    // loads do not wait for them
+    const int sl = (i < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
+    bslot = kDepth == 1 ? sl : settle(sl);
+  };
+  auto fetch = [&](int i, KLoad& d, VLoad& e) {
+    if ((i & 63) == 0) batch(i);
+    const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
+    if (kDepth > 1) d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
+    if (SOFF)
+      load_page_soff<SCHEME, CMP, NO4, MV>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
+    else
+      load_page<SCHEME, CMP, NO4, MV>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
+  };
+  KLoad kA, kB;
+  VLoad vA, vB;
+  // (also with no page: the request for physical page 0 is in bounds and
+  // unused, and every path then waits for the query words here)
+  if (kDepth == 1) fetch(0, kA, vA);
   float qf[32];
   if (hv) {
     if (QF32) {
-      const float* qp = reinterpret_cast<const float*>(a.q) + ((int64_t)b * a.Hq + h) * 128 + 32 * kq;
 #pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        float4 v = *reinterpret_cast<const float4*>(qp + i);
-        qf[i] = v.x; qf[i + 1] = v.y; qf[i + 2] = v.z; qf[i + 3] = v.w;
+      for (int i = 0; i < 8; ++i) {
+        qf[4 * i] = __uint_as_float(qw[i].x); qf[4 * i + 1] = __uint_as_float(qw[i].y);
+        qf[4 * i + 2] = __uint_as_float(qw[i].z); qf[4 * i + 3] = __uint_as_float(qw[i].w);
       }
     } else {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h) * 128 + 32 * kq;
 #pragma unroll
-      for (int i = 0; i < 32; i += 8) {
-        uint4 v = *reinterpret_cast<const uint4*>(qp + i);
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {qw[i].x, qw[i].y, qw[i].z, qw[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[i + 2 * e] = __uint_as_float(w[e] << 16);
-          qf[i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          qf[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+          qf[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
         }
       }
     }
@@ -602,7 +675,10 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     beta[4 + jj] = (kq & 1) ? mine : other;
   }
   // Tier A operands of the two fp32 MFMAs: K slot k <-> bands 2k and 2k+1
-  const float bA0 = hv ? beta[2 * kq] : 0.0f, bA1 = hv ? beta[2 * kq + 1] : 0.0f;
+  // (selects, not an index by the lane's k: that would go through scratch)
+  const float b2k = kq == 0 ? beta[0] : kq == 1 ? beta[2] : kq == 2 ? beta[4] : beta[6];
+  const float b2k1 = kq == 0 ? beta[1] : kq == 1 ? beta[3] : kq == 2 ? beta[5] : beta[7];
+  const float bA0 = hv ? b2k : 0.0f, bA1 = hv ? b2k1 : 0.0f;
   const float qs2 = a.sm_scale * kLog2e * ldexpf(1.0f, -qe);     // log2-unit logit per raw unit
   // the dither bytes enter the key MFMAs as -(4 + hb 2^-8) and
   // -(2^-6 + lb 2^-16); with xi = hb 2^-8 + lb 2^-16 - 1/2 the chain's start
@@ -618,13 +694,6 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   const uint32_t st_lane = (key + (uint32_t)(64 * n + 16 * kq)) * kPcgMul + kPcgInc;
   // compacted softmax: lane (n, k) evaluates head n & 7, tokens 4k + r0, +1
   constexpr int NV = CMP ? 2 : 4;
-  const int r0 = CMP ? 2 * (n >> 3) : 0;
-  LaneOff lo;
-  lo.k = (uint32_t)(16 * lane);
-  lo.s = (uint32_t)(4 * (4 * kq + r0));
-  lo.w = meterA ? (uint32_t)(4 * (8 * n + 2 * kq)) : lo.k;
-  lo.v = (uint32_t)(16 * lane);
-  lo.o = (uint32_t)(2 * NO4 * (4 * n + kq));
   const float qs2c = CMP ? dpp_shr8_hi(qs2, qs2) : qs2;
   const float kappac = CMP ? dpp_shr8_hi(kappa, kappa) : kappa;
   // Per-wave LDS tile of the page's dither high bytes as fp16 operands
@@ -654,55 +723,15 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   // one page of this wave; the loop below alternates two prefetch buffers
   const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
   float vsum = 0.0f;                           // sum of the value weights p s fed to the MFMA
-  // Each wave takes a contiguous quarter of the split's pages: page i of
-  // this wave is page w0 + i.  Its physical page and exact-pool slot come
-  // from lane i % 64 of a batch read once per 64 pages, so the loop never
-  // waits on a page-table read.
-  const int per = (p1 - p0 + kNW - 1) / kNW;
-  const int w0 = p0 + wave * per;
-  const int npw = max(0, min(p1, w0 + per) - w0);
-  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
-  const int64_t pg_base = (int64_t)a.layer * c.num_pages;
-  LayerBufs lb;
-  if (SOFF) {
-    const int64_t lph = c.num_pages * c.num_kv_heads;     // page-head blocks per layer
-    const int64_t l0 = (int64_t)a.layer * lph;
-    constexpr int64_t PB = page_bytes<SCHEME>();
-    lb.k = layer_rsrc(c.k_codes, l0 * PB, (uint64_t)lph * PB);
-    lb.v = layer_rsrc(c.v_codes, l0 * PB, (uint64_t)lph * PB);
-    lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
-    lb.o = lb.ks = lb.vs = lb.wv = lb.k;       // (unused unless set below)
-    if (MV) lb.wv = layer_rsrc(c.v_witness, l0 * 64, (uint64_t)lph * 64);
-    if (NO4 > 0) lb.o = layer_rsrc(c.k_outlier, l0 * (128 * NO4), (uint64_t)lph * (128 * NO4));
-    if (int8_codes<SCHEME>()) {
-      lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
-      lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
-    }
-  }
-  int bphys = 0, bslot = -1;
-  auto batch = [&](int i0) {
-    const int i = i0 + lane;
-    const int ph = i < npw ? ptab[w0 + i] : 0;
-    const int sl = (i < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
-    bphys = settle(ph);                        // the wait for these stays in this rare branch
-    bslot = settle(sl);
-  };
-  auto fetch = [&](int i, KLoad& d, VLoad& e) {
-    if ((i & 63) == 0) batch(i);
-    const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
-    d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
-    if (SOFF)
-      load_page_soff<SCHEME, CMP, NO4, MV>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
-    else
-      load_page<SCHEME, CMP, NO4, MV>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, d, e);
-  };
   auto page = [&](const KLoad& cur, const VLoad& vl, KLoad& nxt, VLoad& vnxt, const int i) {
     // the page kDepth ahead; past the end the last page loads itself again
     // so that every iteration issues the same loads
+    // (its exact-pool slot first: the prefetch below may start the next batch)
+    const int slot = kDepth == 1 ? __builtin_amdgcn_readlane(bslot, i & 63) : cur.slot;
     fetch(min(i + kDepth, npw - 1), nxt, vnxt);
     const int jj = w0 + i;
     const int tok0 = jj * 16;
-    const bool exact = cur.slot >= 0;          // wave-uniform
+    const bool exact = slot >= 0;              // wave-uniform
     const bool full = tok0 + 16 <= S;          // wave-uniform: only the last page is ragged
 
     // ---------------- Tier A: a^T = W . beta^T on two fp32 MFMAs, issued first
@@ -788,7 +817,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       // values still need the draws.  The pool loads are issued before the
       // hashing so that their latency overlaps it.
       // (a wave-uniform base, the slot's 4 KB, plus the lane offset 256 n + 64 k)
-      const uint8_t* pb = reinterpret_cast<const uint8_t*>(c.exact_pool) + (int64_t)cur.slot * 4096;
+      const uint8_t* pb = reinterpret_cast<const uint8_t*>(c.exact_pool) + (int64_t)slot * 4096;
       const uint32_t po = (uint32_t)(256 * n + 64 * kq);
       uint4 xv[4];
 #pragma unroll
@@ -920,32 +949,47 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < NV; ++r) nvv = fmaf(p[r], wvv[r], nvv);
     }
-    // meter terms p (e^c - 1) = 2^(l2 - m + c log2 e) - p: one exp per token, and
-    // a bound large enough to overflow saturates the meter at +inf.  A bound in
-    // (0, 2^-6) would lose relative precision to the subtraction: then the
-    // page takes the series path (wave-uniform).
+    // meter terms p (e^c - 1).  When every bound of the wave's page is below
+    // 1/4 (the common case): a short series, no exp.  Otherwise
+    // 2^(l2 - m + c log2 e) - p, one exp per token, where a bound large
+    // enough to overflow saturates the meter at +inf; a bound in (0, 2^-6)
+    // would lose relative precision to that subtraction, so then the page
+    // takes the series path with the exp for the larger bounds (both choices
+    // wave-uniform).
     float ea = 0.0f, eb = 0.0f;
     if (meterA && !exact) {
-      // some bound in (0, 2^-6)?  As unsigned bits, c - 1 < 2^-6 - 1 exactly then
-      uint32_t cmin = 0xFFFFFFFFu;
+      // (as unsigned bits: the bounds are >= 0, and a NaN compares above 1/4)
+      uint32_t cbig = 0u;
 #pragma unroll
-      for (int r = 0; r < NV; ++r)
-        cmin = min(cmin, min(__float_as_uint(cA[r]) - 1u, __float_as_uint(cB[r]) - 1u));
-      const bool tiny = cmin < 0x3C7FFFFFu;
+      for (int r = 0; r < NV; ++r) cbig = max(cbig, max(__float_as_uint(cA[r]), __float_as_uint(cB[r])));
       // (the sums start from the first token's term: a 0.0f start value
       // would cost an add, since 0 + (-0) is not -0)
       float ta[NV], tb[NV];
-      if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
+      if (__builtin_amdgcn_ballot_w64(cbig >= 0x3E800000u) == 0) {
 #pragma unroll
         for (int r = 0; r < NV; ++r) {
-          ta[r] = __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
-          tb[r] = meterB ? __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r] : 0.0f;
+          ta[r] = p_expm1_small(p[r], cA[r]);
+          tb[r] = meterB ? p_expm1_small(p[r], cB[r]) : 0.0f;
         }
       } else {
+        // some bound in (0, 2^-6)?  As unsigned bits, c - 1 < 2^-6 - 1 exactly then
+        uint32_t cmin = 0xFFFFFFFFu;
 #pragma unroll
-        for (int r = 0; r < NV; ++r) {
-          ta[r] = fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
-          tb[r] = meterB ? fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f) : 0.0f;
+        for (int r = 0; r < NV; ++r)
+          cmin = min(cmin, min(__float_as_uint(cA[r]) - 1u, __float_as_uint(cB[r]) - 1u));
+        const bool tiny = cmin < 0x3C7FFFFFu;
+        if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
+#pragma unroll
+          for (int r = 0; r < NV; ++r) {
+            ta[r] = __builtin_amdgcn_exp2f(fmaf(cA[r], kLog2e, dl[r])) - p[r];
+            tb[r] = meterB ? __builtin_amdgcn_exp2f(fmaf(cB[r], kLog2e, dl[r])) - p[r] : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NV; ++r) {
+            ta[r] = fmaxf(p[r] * expm1_fast(cA[r]), cA[r] >= 88.0f ? INFINITY : 0.0f);
+            tb[r] = meterB ? fmaxf(p[r] * expm1_fast(cB[r]), cB[r] >= 88.0f ? INFINITY : 0.0f) : 0.0f;
+          }
         }
       }
       ea = ta[0];
@@ -1080,9 +1124,6 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     }
   };
   if constexpr (kDepth == 1) {
-    KLoad kA, kB;
-    VLoad vA, vB;
-    if (npw > 0) fetch(0, kA, vA);
     for (int i = 0; i < npw; i += 2) {
       page(kA, vA, kB, vB, i);
       if (i + 1 >= npw) break;
@@ -1190,6 +1231,92 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v += shfl_xor(v, m);
   return v;
+}
+
+// ---------------------------------------------------------------- load floor
+// What HBM delivers for the decode's own access pattern: the same grid, page
+// assignment, page-table batches, buffer resources, cache policies and page
+// loads as decode_kernel (kDepth = 1: one page in flight ahead of the one in
+// hand), with no arithmetic.  Each lane folds every loaded word into one
+// xor, stored only if it equals a fixed pattern, so that no load is dropped.
+// Dynamic LDS (the decode instance's static size) gives it the decode's
+// residency per CU.  The query, the outlier side store and the value
+// witnesses are not read.
+struct FloorArgs {
+  const int32_t* page_table;
+  const int32_t* ctx_len;
+  uint32_t* sink;
+  int max_pages, n_split, layer, meterA;
+};
+
+__device__ __forceinline__ uint32_t fold4(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+__device__ __forceinline__ uint32_t fold4(float4 v) { return fold4(__builtin_bit_cast(uint4, v)); }
+
+template <int SCHEME, bool PAIR>
+__global__ void __launch_bounds__(kThreads) decode_floor_kernel(wc_cache c, FloorArgs a) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, kq = lane >> 4;
+  const int S = a.ctx_len[b];
+  const int P = (S + 15) >> 4;
+  const int p0 = (int)((int64_t)split * P / a.n_split), p1 = (int)((int64_t)(split + 1) * P / a.n_split);
+  const bool meterA = a.meterA != 0;
+  const int r0 = PAIR ? 2 * (n >> 3) : 0;
+  LaneOff lo;
+  lo.k = (uint32_t)(16 * lane);
+  lo.s = (uint32_t)(4 * (4 * kq + r0));
+  lo.w = meterA ? (uint32_t)(4 * (8 * n + 2 * kq)) : lo.k;
+  lo.v = (uint32_t)(16 * lane);
+  lo.o = 0;
+  const int per = (p1 - p0 + kNW - 1) / kNW;
+  const int w0 = p0 + wave * per;
+  const int npw = max(0, min(p1, w0 + per) - w0);
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int64_t pg_base = (int64_t)a.layer * c.num_pages;
+  const int64_t lph = c.num_pages * c.num_kv_heads;
+  const int64_t l0 = (int64_t)a.layer * lph;
+  constexpr int64_t PB = page_bytes<SCHEME>();
+  LayerBufs lb;
+  lb.k = layer_rsrc(c.k_codes, l0 * PB, (uint64_t)lph * PB);
+  lb.v = layer_rsrc(c.v_codes, l0 * PB, (uint64_t)lph * PB);
+  lb.w = meterA ? layer_rsrc(c.witness, l0 * 512, (uint64_t)lph * 512) : lb.k;
+  lb.o = lb.ks = lb.vs = lb.wv = lb.k;
+  if (int8_codes<SCHEME>()) {
+    lb.ks = layer_rsrc(c.k_scale, l0 * 64, (uint64_t)lph * 64);
+    lb.vs = layer_rsrc(c.v_scale, l0 * 64, (uint64_t)lph * 64);
+  }
+  uint32_t acc = 0;
+  int bphys = 0, bslot = -1;
+  auto fetch = [&](int i, KLoad& d, VLoad& e) {
+    if ((i & 63) == 0) {
+      const int j = i + lane;
+      const int ph = j < npw ? ptab[w0 + j] : 0;
+      const int sl = (j < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
+      bphys = settle(ph);
+      bslot = settle(sl);
+    }
+    const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
+    d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
+    load_page_soff<SCHEME, PAIR, 0, false>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
+  };
+  auto fold = [&](const KLoad& d, const VLoad& e) {
+    uint32_t x = fold4(d.k0) ^ fold4(d.k1) ^ fold4(e.v0) ^ fold4(e.v1) ^ (uint32_t)d.slot;
+    if (SCHEME == WC_BF16_STORE) x ^= fold4(d.k2) ^ fold4(d.k3) ^ fold4(e.v2) ^ fold4(e.v3);
+    if (meterA) x ^= __float_as_uint(d.w.x) ^ __float_as_uint(d.w.y);
+    if (int8_codes<SCHEME>()) x ^= fold4(d.ks) ^ fold4(e.vs);
+    acc = (acc << 1 | acc >> 31) ^ x;
+  };
+  KLoad kA, kB;
+  VLoad vA, vB;
+  if (npw > 0) fetch(0, kA, vA);
+  for (int i = 0; i < npw; i += 2) {
+    fetch(min(i + 1, npw - 1), kB, vB);
+    fold(kA, vA);
+    if (i + 1 >= npw) break;
+    fetch(min(i + 2, npw - 1), kA, vA);
+    fold(kB, vB);
+  }
+  if (acc == 0x9E3779B9u) a.sink[0] = acc;
 }
 
 __global__ void __launch_bounds__(64) merge_kernel(const float* __restrict__ part, int n_split, float* o,
@@ -1469,6 +1596,81 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
   else
     launch_scheme<true>(c.scheme, cmp, soff, no4, mv, mode, grid, st, c, a);
   return check_launch("wc_decode_attn_meter");
+}
+
+template <int SCHEME>
+static void launch_floor(bool pair, bool match, dim3 grid, hipStream_t st, const wc_cache& c, const FloorArgs& a) {
+  // the residency of the decode's instance for the same cache and query
+  // group (meter on, bf16 query): its static LDS, given here as dynamic LDS
+  size_t lds = 0;
+  if (match) {
+    hipFuncAttributes fa{};
+    const void* fn = pair ? reinterpret_cast<const void*>(&decode_kernel<SCHEME, false, true, true, 0, false, kModeOn>)
+                          : reinterpret_cast<const void*>(&decode_kernel<SCHEME, false, false, true, 0, false, kModeOn>);
+    if (hipFuncGetAttributes(&fa, fn) == hipSuccess) lds = fa.sharedSizeBytes;
+  }
+  if (pair)
+    hipLaunchKernelGGL((decode_floor_kernel<SCHEME, true>), grid, dim3(kThreads), lds, st, c, a);
+  else
+    hipLaunchKernelGGL((decode_floor_kernel<SCHEME, false>), grid, dim3(kThreads), lds, st, c, a);
+}
+
+extern "C" int wc_decode_load_floor(const wc_cache* cache, int layer, int B, int Hq, const int32_t* page_table,
+                                    int max_pages, const int32_t* ctx_len, int n_split, unsigned meter_mask,
+                                    int match_residency, uint32_t* sink, void* stream) {
+  if (!cache || (B != 0 && (!page_table || !ctx_len || !sink))) {
+    set_error("wc_decode_load_floor: null pointer");
+    return WC_EINVAL;
+  }
+  const wc_cache& c = *cache;
+  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1) {
+    set_error("wc_decode_load_floor: need head_dim 128, 8 bands, 16-token pages");
+    return WC_EUNSUPPORTED;
+  }
+  if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3 && c.scheme != WC_RTN_INT8 &&
+      c.scheme != WC_BF16_STORE) {
+    set_error("wc_decode_load_floor: scheme %d has no decode path", c.scheme);
+    return WC_EUNSUPPORTED;
+  }
+  if (B < 0 || Hq < 1 || Hq % c.num_kv_heads != 0 || Hq / c.num_kv_heads > 16 || max_pages < 1 ||
+      n_split < 1 || n_split > 1024 || layer < 0 || layer >= c.num_layers) {
+    set_error("wc_decode_load_floor: bad B/Hq/max_pages/n_split/layer");
+    return WC_EINVAL;
+  }
+  if (meter_mask & ~(WC_METER_A | WC_METER_B | WC_BLOCK_CMAX | WC_METER_V)) {
+    set_error("wc_decode_load_floor: unknown meter_mask bits");
+    return WC_EINVAL;
+  }
+  if ((meter_mask & WC_METER_A) && !c.witness) {
+    set_error("wc_decode_load_floor: Tier A needs the witness");
+    return WC_EINVAL;
+  }
+  if ((c.scheme == WC_DITHER_INT8 || c.scheme == WC_RTN_INT8) && (!c.k_scale || !c.v_scale)) {
+    set_error("wc_decode_load_floor: INT8 cache needs scales");
+    return WC_EINVAL;
+  }
+  if (!c.k_codes || !c.v_codes) {
+    set_error("wc_decode_load_floor: cache codes not set");
+    return WC_EINVAL;
+  }
+  const uint64_t page_b = c.scheme == WC_BF16_STORE ? 4096u : 2048u;
+  if ((uint64_t)c.num_pages * (uint64_t)c.num_kv_heads * page_b > 0xFFFFFFFFull) {
+    set_error("wc_decode_load_floor: a layer's code array must be under 4 GB");
+    return WC_EUNSUPPORTED;
+  }
+  if (B == 0) return WC_OK;
+  FloorArgs a{page_table, ctx_len, sink, max_pages, n_split, layer, (meter_mask & WC_METER_A) ? 1 : 0};
+  dim3 grid((unsigned)n_split, (unsigned)c.num_kv_heads, (unsigned)B);
+  hipStream_t st = (hipStream_t)stream;
+  const bool pair = Hq / c.num_kv_heads <= 8;
+  const bool match = match_residency != 0;
+  switch (c.scheme) {
+    case WC_DITHER_INT8: launch_floor<WC_DITHER_INT8>(pair, match, grid, st, c, a); break;
+    case WC_FP8_E4M3: launch_floor<WC_FP8_E4M3>(pair, match, grid, st, c, a); break;
+    case WC_RTN_INT8: launch_floor<WC_RTN_INT8>(pair, match, grid, st, c, a); break;
+    default: launch_floor<WC_BF16_STORE>(pair, match, grid, st, c, a); break;
+  }
+  return check_launch("wc_decode_load_floor");
 }
 
 extern "C" int wc_lse_merge(const float* partials, int B, int Hq, int n_split, float* o, float* lse,

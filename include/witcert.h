@@ -84,7 +84,11 @@
  * witness above, and E_V = sum_t p~_t w^V_t, which bounds the value part of
  * the output error, ||sum_t p~_t (v^_t - v_t)||, by the triangle inequality
  * for any value quantizer; with the key side's TV,
- * ||o~ - o|| <= E_V + 2 TV max_t ||v_t||.
+ * ||o~ - o|| <= E_V + 2 TV max_t ||v_t||.  E_V is taken on the stored v^.  For
+ * dithered INT8 the returned output uses each value draw's low byte at its
+ * mean (every dequantized value within 2^-9 of its code step of v^), so the
+ * bound on the output this library returns adds 2^-9 sqrt(128) sum_t p~_t s_t
+ * <= 2^-9 sqrt(128) max_t s_t (s_t the value row scale); other schemes add 0.
  *
  * Outlier bypass (dithered INT8 keys, m = 8 or 16).  The summary reports the
  * capacity of the certified INT8 cache with an outlier bypass too, and
@@ -303,6 +307,31 @@ int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_
 
 /* Bytes of the decode workspace: B * Hq * n_split * 136 * 4. */
 size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
+
+/*
+ * wc_decode_load_floor -- a measurement of the decode's memory bound, not a
+ * step of the method.  The summary's cost paragraph puts the certified
+ * decode's cost in the bytes it reads (codes, scales, witness); this call
+ * issues exactly the page loads wc_decode_attn_meter issues for the same
+ * arguments (same grid, page assignment, page-table and exact-slot reads,
+ * cache policies, one page in flight per wave) and does no arithmetic, so
+ * its time is what HBM delivers for that access pattern.  The query, the
+ * outlier side store and the value witnesses are not read.
+ *
+ *  meter_mask       WC_METER_A adds the witness loads (other bits as in the
+ *                   decode; they add no loads).
+ *  match_residency  non-zero: each workgroup reserves the LDS of the
+ *                   decode's instance for this cache (meter on, bf16 query),
+ *                   so as many workgroups share a CU as in the decode; zero:
+ *                   no LDS (the loads alone set the residency).
+ *  sink             device uint32 [1]: written only when a lane's fold of
+ *                   the loaded words hits a fixed pattern; its contents mean
+ *                   nothing.
+ * Returns WC_EUNSUPPORTED when a layer's code array is 4 GB or more.
+ */
+int wc_decode_load_floor(const wc_cache* cache, int layer, int B, int Hq, const int32_t* page_table,
+                         int max_pages, const int32_t* ctx_len, int n_split, unsigned meter_mask,
+                         int match_residency, uint32_t* sink, void* stream);
 
 
 /*

@@ -279,3 +279,25 @@ def test_noalloc_gate_limit_and_refusal():
     assert rc == L.WC_EWORKSPACE and b"scratch" in L.lib.wc_last_error()
     assert L.lib.wc_gate_pagein_noalloc(None, 0, p, p, None, 2, 28, p, 8, p, 0.2, -1, p, p, p, None, None,
                                         None) == L.WC_EINVAL
+
+
+def test_load_floor_rejects_bad_arguments():
+    L = _lib()
+    f = L.lib.wc_decode_load_floor
+    p = ctypes.c_void_p(16)
+    ok = ctypes.byref(_cache(L))
+    assert f(None, 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL
+    assert f(ok, 0, 1, 8, None, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL                # page table
+    assert f(ok, 0, 1, 8, p, 4, p, 1, 3, 1, None, None) == L.WC_EINVAL                # sink
+    assert f(ctypes.byref(_cache(L, head_dim=64)), 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, scheme=2)), 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
+    assert f(ok, 2, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL                   # layer range
+    assert f(ok, 0, 1, 7, p, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL                   # Hq % Hkv
+    assert f(ok, 0, 1, 8, p, 4, p, 0, 3, 1, p, None) == L.WC_EINVAL                   # n_split
+    assert f(ok, 0, 1, 8, p, 4, p, 1, 1 << 9, 1, p, None) == L.WC_EINVAL              # mask bits
+    assert f(ctypes.byref(_cache(L, witness=None)), 0, 1, 8, p, 4, p, 1, 1, 1, p, None) == L.WC_EINVAL
+    assert f(ctypes.byref(_cache(L, k_scale=None)), 0, 1, 8, p, 4, p, 1, 0, 1, p, None) == L.WC_EINVAL
+    big = ctypes.byref(_cache(L, num_pages=1 << 20, num_kv_heads=4))                  # 8 GB per layer
+    assert f(big, 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
+    assert b"4 GB" in L.lib.wc_last_error()
+    assert f(ok, 0, 0, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_OK                       # nothing to do

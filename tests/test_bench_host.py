@@ -40,3 +40,38 @@ def test_more_than_one_gpu_exits_with_a_message():
                            text=True, timeout=120, env={**os.environ, **env})
         assert r.returncode == 2, (args, env, r.returncode)
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    head = ("Correlation_Id,Dispatch_Id,Agent_Id,Queue_Id,Process_Id,Thread_Id,Grid_Size,Kernel_Id,Kernel_Name,"
+            "Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,Accum_VGPR_Count,SGPR_Count,Counter_Name,"
+            "Counter_Value,Start_Timestamp,End_Timestamp\n")
+    with open(path, "w") as fh:
+        fh.write(head)
+        for i, (name, grid, counter, value) in enumerate(rows):
+            fh.write(f'{i},{i + 1},1,1,1,1,{grid},7,"{name}",256,0,0,64,0,32,{counter},{value},0,1\n')
+
+
+def test_counter_reducer(tmp_path):
+    # two passes as rocprofv3 writes them: the decode's step dispatches come
+    # first, timing loops after; the 1 GiB copies calibrate each counter
+    dec = "void wc::" + bench.HEADLINE_KERNEL + "(wc_cache, wc::DecodeArgs)"
+    other = "void wc::decode_kernel<0, false, true, true, 0, false, 1>(wc_cache, wc::DecodeArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    flo = "void wc::" + bench.FLOOR_KERNEL + "(wc_cache, wc::FloorArgs)"
+    fetch = [(dec, 100, "FETCH_SIZE", 600000 + i) for i in range(4)] + [(dec, 100, "FETCH_SIZE", 9e9),
+                                                                         (other, 100, "FETCH_SIZE", 1.0),
+                                                                         (copy, 64, "FETCH_SIZE", 5.0),
+                                                                         (flo, 100, "FETCH_SIZE", 610000)]
+    fetch += [(copy, 1 << 26, "FETCH_SIZE", 524288)] * 3
+    write = [(dec, 100, "WRITE_SIZE", 30000)] * 4 + [(copy, 1 << 26, "WRITE_SIZE", 1048576)] * 3
+    _counter_csv(str(tmp_path / "f" / "host" / "1_counter_collection.csv"), fetch)
+    _counter_csv(str(tmp_path / "w" / "host" / "1_counter_collection.csv"), write)
+    r = bench.reduce_counters(str(tmp_path / "f"), str(tmp_path / "w"), 4, 32, 32768)
+    assert r["fetch_factor"] == 2.0 and r["write_factor"] == 1.0
+    assert r["fetch_bytes_per_launch"] == round(600001.5 * 1024 * 2)
+    assert r["write_bytes_per_launch"] == 30000 * 1024
+    assert r["hbm_bytes_per_launch"] == r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
+    assert r["floor_fetch_bytes_per_launch"] == 610000 * 1024 * 2
+    assert r["source_sha"] == bench.decode_source_sha() and r["algorithmic_bytes_per_launch"] == 1242005888
