@@ -694,26 +694,28 @@ def _counter_rows(d):
     return rows
 
 
-def reduce_counters(fetch_dir, write_dir, launches, B, S):
+def reduce_counters(fetch_dir, write_dir, launches, B, S, floor_launches=0):
     """HBM bytes per launch of the headline decode from two rocprofv3 --pmc
     runs of bench.py (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
-    scaled by what the same counter reads for the 1 GiB device copies that
-    --copy-ref adds (1 GiB read and 1 GiB written per copy).  The decode's
+    scaled by what the same counter reads for the three 1 GiB device copies
+    that --copy-ref adds at the end of the run (1 GiB read and 1 GiB written
+    per copy).  The decode's
     figure is the mean over its first `launches` dispatches (the warm-up and
-    timed steps); the load floor's over all its dispatches."""
+    timed steps); the load floor's over its first `floor_launches`
+    dispatches (the loops taken with the decode's, meter on)."""
     import numpy as np
     out = {"source_sha": decode_source_sha(), "batch": B, "ctx": S, "launches": launches}
     total = 0.0
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r[3] == name]
-        copies = [r for r in rows if "copyBuffer" in r[0]]
-        if not copies:
+        # the 1 GiB copies of --copy-ref are the run's last three device copies
+        copies = sorted((r for r in rows if "copyBuffer" in r[0]), key=lambda r: r[2])[-3:]
+        if len(copies) < 3:
             raise SystemExit(f"{name}: no device copy dispatches (run bench.py with --copy-ref)")
-        gmax = max(r[1] for r in copies)
-        ref_kib = float(np.median([r[4] for r in copies if r[1] == gmax]))
+        ref_kib = float(np.median([r[4] for r in copies]))
         factor = (1 << 20) / ref_kib                    # KiB that 1 GiB moves
         dec = sorted((r for r in rows if HEADLINE_KERNEL in r[0]), key=lambda r: r[2])[:launches]
-        flo = [r for r in rows if FLOOR_KERNEL in r[0]]
+        flo = sorted((r for r in rows if FLOOR_KERNEL in r[0]), key=lambda r: r[2])[:floor_launches]
         if len(dec) < launches:
             raise SystemExit(f"{name}: {len(dec)} headline decode dispatches, expected {launches}")
         kib = float(np.mean([r[4] for r in dec]))
@@ -727,6 +729,70 @@ def reduce_counters(fetch_dir, write_dir, launches, B, S):
         total += kib * 1024 * factor
     out["hbm_bytes_per_launch"] = int(round(total))
     out["algorithmic_bytes_per_launch"] = decode_bytes(B, S, True)
+    return out
+
+
+def trace_phases(kt_dir, warmup, steps, loops=10, iters=20):
+    """Per-phase durations of the headline decode from a rocprofv3
+    --kernel-trace run of the default bench line (same --warmup and
+    --steps): its dispatches in order are the warm-up and timed steps, then
+    `loops` rounds of one untimed and `iters` timed launches with block
+    risks and the same without (the meter-off launches are another
+    instance).  Returns the step mean and, per mode, the median of the loop
+    means (us), next to the rocprofv3 statistics of every kernel."""
+    import csv
+    import glob
+    import numpy as np
+    rows = []
+    for f in sorted(glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    if not rows:
+        raise SystemExit(f"no kernel_trace.csv under {kt_dir}")
+    dec = sorted((r for r in rows if HEADLINE_KERNEL in r[0]), key=lambda r: r[1])
+    us = [(r[2] - r[1]) / 1e3 for r in dec]
+    n0 = warmup + steps
+    out = {"headline_dispatches": len(dec), "steps_mean_us": round(float(np.mean(us[warmup:n0])), 2)}
+    per = 2 * (iters + 1)
+    risk = [float(np.mean(us[n0 + k * per + 1:n0 + k * per + 1 + iters])) for k in range(loops)]
+    on = [float(np.mean(us[n0 + k * per + iters + 2:n0 + (k + 1) * per])) for k in range(loops)]
+    out["risk_loops_median_us"] = round(float(np.median(risk)), 2)
+    out["on_loops_median_us"] = round(float(np.median(on)), 2)
+    flo = sorted((r for r in rows if FLOOR_KERNEL in r[0]), key=lambda r: r[1])
+    if flo:
+        fus = [(r[2] - r[1]) / 1e3 for r in flo]
+        out["floor_first_loops_median_us"] = round(float(np.median(
+            [np.mean(fus[k * (iters + 1) + 1:(k + 1) * (iters + 1)]) for k in range(loops)])), 2)
+    stats = {}
+    for f in sorted(glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                try:
+                    stats[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": round(float(r["AverageNs"]) / 1e3, 2),
+                                        "min_us": round(float(r["MinNs"]) / 1e3, 2),
+                                        "max_us": round(float(r["MaxNs"]) / 1e3, 2),
+                                        "pct": round(float(r["Percentage"]), 2)}
+                except (KeyError, ValueError):
+                    continue
+    out["kernel_stats"] = stats
+    return out
+
+
+def counter_means(dirs, launches):
+    """Mean per dispatch of every counter in rocprofv3 --pmc runs (the
+    directories given) over the first `launches` dispatches of each decode
+    instance of the dithered INT8 and fp8 headline configurations."""
+    import numpy as np
+    out = {}
+    for name in (HEADLINE_KERNEL, HEADLINE_KERNEL.replace("<0,", "<1,")):
+        acc = {}
+        for d in dirs:
+            rows = [r for r in _counter_rows(d) if name in r[0]]
+            ids = sorted({r[2] for r in rows})[:launches]
+            for c in sorted({r[3] for r in rows}):
+                acc[c] = float(np.mean([sum(r[4] for r in rows if r[2] == i and r[3] == c) for i in ids]))
+        out[name] = acc
     return out
 
 
@@ -753,9 +819,22 @@ def main():
                     help="no GPU: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of "
                          "`bench.py --steps K --warmup W --no-cpu --copy-ref` (same K, W, --batch, --ctx given here) "
                          "into the headline decode's HBM bytes per launch, written to " + COUNTERS)
+    ap.add_argument("--trace-phases", metavar="KT_DIR",
+                    help="no GPU: the headline decode's per-phase durations from a rocprofv3 --kernel-trace --stats "
+                         "run of the default line (same --steps, --warmup)")
+    ap.add_argument("--counter-means", nargs="+", metavar="DIR",
+                    help="no GPU: per-dispatch means of the counters of rocprofv3 --pmc runs of "
+                         "`bench.py --steps K --warmup W --no-cpu` for the INT8 and fp8 decode instances")
     args = ap.parse_args()
+    if args.trace_phases:
+        print(json.dumps(trace_phases(args.trace_phases, args.warmup, args.steps)), flush=True)
+        return
+    if args.counter_means:
+        print(json.dumps(counter_means(args.counter_means, args.warmup + args.steps)), flush=True)
+        return
     if args.reduce_counters:
-        res = reduce_counters(*args.reduce_counters, args.warmup + args.steps, args.batch, args.ctx)
+        res = reduce_counters(*args.reduce_counters, args.warmup + args.steps, args.batch, args.ctx,
+                              floor_launches=10 * (max(args.steps, 10) + 1))
         with open(COUNTERS, "w") as fh:
             json.dump(res, fh, indent=1)
         print(json.dumps(res), flush=True)

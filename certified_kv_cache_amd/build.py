@@ -1,6 +1,7 @@
 """Build libwitcert.so (HIP, gfx950) in-tree with hipcc.
 
     python -m certified_kv_cache_amd.build [--verbose]
+    python -m certified_kv_cache_amd.build --sanitized OUT.so   (host ASan/UBSan)
 
 The library is compiled with -ffp-contract=off (the write path must agree bit
 for bit with a float32 replay; every intended fused multiply-add is an
@@ -49,5 +50,51 @@ def build(verbose=False, out=LIB, extra=()):
     return out
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (device
+# code unoptimized and uninstrumented), for the argument checks and host
+# glue on machines without a GPU.  The library expects the ASan runtime to be
+# preloaded into the process (asan_runtime()).
+SAN_FLAGS = ["-O1", "-g",
+             "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_device", "-O0", "-Xarch_device", "-g0"]
+
+
+def asan_runtime():
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return path
+
+
+def build_sanitized(out):
+    """Compile the sources in parallel with SAN_FLAGS and link `out`."""
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(os.path.dirname(out), src + ".o")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-ffp-contract=off",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *SAN_FLAGS,
+               "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, os.path.join(HERE, "csrc", src)]
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+        objs.append(obj)
+    failed = [p.communicate()[0] for p in procs if p.wait() != 0]
+    if failed:
+        sys.stderr.write("\n".join(failed))
+        raise RuntimeError("hipcc failed")
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-shared-libsan",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-o", out, *objs]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link failed")
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(sys.argv[sys.argv.index("--sanitized") + 1]))
+    else:
+        print(build(verbose="--verbose" in sys.argv))

@@ -60,18 +60,43 @@ def test_counter_reducer(tmp_path):
     other = "void wc::decode_kernel<0, false, true, true, 0, false, 1>(wc_cache, wc::DecodeArgs)"
     copy = "__amd_rocclr_copyBuffer"
     flo = "void wc::" + bench.FLOOR_KERNEL + "(wc_cache, wc::FloorArgs)"
-    fetch = [(dec, 100, "FETCH_SIZE", 600000 + i) for i in range(4)] + [(dec, 100, "FETCH_SIZE", 9e9),
-                                                                         (other, 100, "FETCH_SIZE", 1.0),
-                                                                         (copy, 64, "FETCH_SIZE", 5.0),
-                                                                         (flo, 100, "FETCH_SIZE", 610000)]
-    fetch += [(copy, 1 << 26, "FETCH_SIZE", 524288)] * 3
-    write = [(dec, 100, "WRITE_SIZE", 30000)] * 4 + [(copy, 1 << 26, "WRITE_SIZE", 1048576)] * 3
+    fetch = [(copy, 1 << 26, "FETCH_SIZE", 4108.0)]           # an earlier copy (a larger grid)
+    fetch += [(dec, 100, "FETCH_SIZE", 600000 + i) for i in range(4)] + [(dec, 100, "FETCH_SIZE", 9e9),
+                                                                          (other, 100, "FETCH_SIZE", 1.0),
+                                                                          (copy, 64, "FETCH_SIZE", 5.0),
+                                                                          (flo, 100, "FETCH_SIZE", 610000)]
+    fetch += [(copy, 4096, "FETCH_SIZE", 524288)] * 3
+    write = [(dec, 100, "WRITE_SIZE", 30000)] * 4 + [(copy, 4096, "WRITE_SIZE", 1048576)] * 3
     _counter_csv(str(tmp_path / "f" / "host" / "1_counter_collection.csv"), fetch)
     _counter_csv(str(tmp_path / "w" / "host" / "1_counter_collection.csv"), write)
-    r = bench.reduce_counters(str(tmp_path / "f"), str(tmp_path / "w"), 4, 32, 32768)
+    r = bench.reduce_counters(str(tmp_path / "f"), str(tmp_path / "w"), 4, 32, 32768, floor_launches=1)
     assert r["fetch_factor"] == 2.0 and r["write_factor"] == 1.0
     assert r["fetch_bytes_per_launch"] == round(600001.5 * 1024 * 2)
     assert r["write_bytes_per_launch"] == 30000 * 1024
     assert r["hbm_bytes_per_launch"] == r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
     assert r["floor_fetch_bytes_per_launch"] == 610000 * 1024 * 2
     assert r["source_sha"] == bench.decode_source_sha() and r["algorithmic_bytes_per_launch"] == 1242005888
+
+
+def test_trace_phases(tmp_path):
+    # the headline instance's dispatches in bench order: 3 warm-up and 2 timed
+    # steps, then rounds of (1 + 4) block-risk and (1 + 4) meter-on launches
+    dec = "void wc::" + bench.HEADLINE_KERNEL + "(wc_cache, wc::DecodeArgs)"
+    durs = [900, 900, 900, 250, 252]
+    for k in range(3):
+        durs += [999] + [240 + k] * 4 + [999] + [230 + k] * 4
+    os.makedirs(tmp_path / "kt" / "host")
+    with open(tmp_path / "kt" / "host" / "kt_kernel_trace.csv", "w") as fh:
+        fh.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        t = 0
+        for d in durs:
+            fh.write(f'"{dec}",{t},{t + d * 1000}\n')
+            fh.write(f'"other",{t + 1},{t + 2}\n')
+            t += 10 ** 7
+    with open(tmp_path / "kt" / "host" / "kt_kernel_stats.csv", "w") as fh:
+        fh.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        fh.write(f'"{dec}",35,0,300000.0,90.5,230000,999000,1\n')
+    r = bench.trace_phases(str(tmp_path / "kt"), 3, 2, loops=3, iters=4)
+    assert r["headline_dispatches"] == 35 and r["steps_mean_us"] == 251.0
+    assert r["risk_loops_median_us"] == 241.0 and r["on_loops_median_us"] == 231.0
+    assert r["kernel_stats"][dec]["avg_us"] == 300.0 and r["kernel_stats"][dec]["calls"] == 35
