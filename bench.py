@@ -814,7 +814,7 @@ def main():
                          "gate-compare: the same on the dithered INT8 cache, certificate gates against the tanh gate; "
                          "latency: decode + merge latency at the two parity sizes; "
                          "decode-bounds: the decode with its cache in HBM and L2-resident (compute alone)")
-    ap.add_argument("--layers", type=int, default=4, help="gate-flow: resident layers")
+    ap.add_argument("--layers", type=int, default=28, help="gate-flow, gate-compare: resident layers")
     ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of "
                          "`bench.py --steps K --warmup W --no-cpu --copy-ref` (same K, W, --batch, --ctx given here) "

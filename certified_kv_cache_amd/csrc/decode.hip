@@ -28,9 +28,11 @@
 //   PV   O^T[channel][head] += Vhat^T[channel][token] . P^T[token][head]
 //        (MFMA 16x16x16 f16, 8 channel tiles); B = P^T is exactly the D layout
 //        above (lane (n, k): tokens 4k..4k+3 of head n), so no shuffles; A = the
-//        value codes of channel 8n + tile, tokens 4k..4k+3, one 32-bit word of
-//        the value page layout.  Lane (n, k) ends with channels 32k..32k+31 of
-//        head n.
+//        value codes of channel 32 (n / 4) + 4 tile + n % 4, tokens 4k..4k+3,
+//        one 32-bit word of the value page layout (dithered INT8: with the
+//        draws of the same tokens and channel, read from the key side's LDS
+//        tile by 16-bit transpose reads).  Lane (n, k) ends with channels
+//        32k..32k+31 of head n.
 //   Tier A  a^T[token][head] = W[token][band] . beta[head][band] on two fp32
 //        MFMAs 16x16x4.
 //   RTN INT8  the code chain alone (no dither); values through 16x16x16 f16
@@ -68,6 +70,14 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i's
+// element e is element i % 4 of the four 16-bit values at the address of
+// lane 4 e + i / 4.  p: an 8-byte-aligned LDS address.
+typedef short s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr16_read(const void* p) {
+  const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
 __device__ __forceinline__ h2 make_h2(_Float16 a, _Float16 b) { return h2{a, b}; }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -217,7 +227,7 @@ struct LaneOff {
   uint32_t k;             // key codes: token n, channels 32k..32k+15 (+1 KB: 32k+16..32k+31)
   uint32_t s;             // scales: tokens 4k (+ r0) onward
   uint32_t w;             // witness bands 2k, 2k+1 of token n (meter off: the key codes again)
-  uint32_t v;             // value codes: channels 8n..8n+3 (+1 KB: 8n+4..8n+7), tokens 4k..4k+3
+  uint32_t v;             // value codes: tiles 0..3 (+1 KB: 4..7) of the lane, tokens 4k..4k+3
   uint32_t o;             // outlier side store: entries k m/4 .. of token n
 };
 
@@ -840,16 +850,14 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       Da = zero4;
       Do = zero4;
     }
-    // the value side's draws (tokens 4k..4k+3, channels 8n..8n+7), read back
-    // now so that the LDS latency hides behind the softmax
-    uint4 H0, H1, H2, H3;
-    if (SCHEME == WC_DITHER_INT8) {
-      __builtin_amdgcn_wave_barrier();
-      H0 = sH[4 * kq][n];
-      H1 = sH[4 * kq + 1][n];
-      H2 = sH[4 * kq + 2][n];
-      H3 = sH[4 * kq + 3][n];
-    }
+    // the value side's draws: tile t of lane (n, k) is channel
+    // 32 (n / 4) + 4 t + n % 4 (the value page layout), tokens 4k..4k+3.  The
+    // 16-bit transpose read gives lane n of each 16-lane group element n % 4
+    // of the four halves addressed by lane 4 e + n / 4, as its element e; so
+    // lane n addresses token 4k + n / 4, channels 32 (n % 4) + 4 t onward, and
+    // receives the four tokens' operands of its channel, in token order.
+    const uint8_t* hrow = reinterpret_cast<const uint8_t*>(sH[4 * kq + (n >> 2)]) + 64 * (n & 3);
+    if (SCHEME == WC_DITHER_INT8) __builtin_amdgcn_wave_barrier();
     // raw = sum q' (code - xi) (a repaired block: sum q' k of the exact keys)
     float raw[4] = {Dc[0], Dc[1], Dc[2], Dc[3]};
     float cA[4] = {Da[0], Da[1], Da[2], Da[3]};
@@ -1067,16 +1075,12 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       vsum = __builtin_amdgcn_fdot2(make_h2(Bc[2], Bc[3]), ones, vsum, false);
       const h8 B2 = make_h8(as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])),
                             as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])));
-      const uint32_t h0w[4] = {H0.x, H0.y, H0.z, H0.w}, h1w[4] = {H1.x, H1.y, H1.z, H1.w};
-      const uint32_t h2w[4] = {H2.x, H2.y, H2.z, H2.w}, h3w[4] = {H3.x, H3.y, H3.z, H3.w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        // channel 8n + t: half (t % 2) of word t / 2 of each token's group
-        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-        const int w = t >> 1;
         uint32_t c0, c1;
         codes_to_h(vw[t], c0, c1);
-        O[t] = mfma32(make_h8(c0, c1, perm(h1w[w], h0w[w], sel), perm(h3w[w], h2w[w], sel)), B2, O[t]);
+        const uint2 hb = tr16_read(hrow + 8 * t);
+        O[t] = mfma32(make_h8(c0, c1, hb.x, hb.y), B2, O[t]);
       }
     } else if (SCHEME == WC_BF16_STORE) {
       // [V|V] . [P_hi|P_lo]: tokens 4k..4k+3 of channel 8n + t twice, against
@@ -1173,7 +1177,8 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sO[wave][n][32 * kq + 8 * r + t] = O[t][r];
+    for (int r = 0; r < 4; ++r)                // row 4k + r of tile t: channel 32k + 4t + r (16-bit store: 32k + 8r + t)
+      sO[wave][n][SCHEME == WC_BF16_STORE ? 32 * kq + 8 * r + t : 32 * kq + 4 * t + r] = O[t][r];
   if (kq == 0) {
     sM[wave][n][0] = m_run;
     sM[wave][n][1] = l_run;

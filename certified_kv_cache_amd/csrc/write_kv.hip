@@ -262,12 +262,14 @@ __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __
   if (SC && lane16 == 0) c.k_scale[pg * 16 + off] = o.ks;
   if (OUTL && ochan >= 0)
     c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] = reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
-  // values: channel 8 lane16 + k of token off: half k / 4, token group off / 4,
-  // channel group lane16, word k % 4, byte off % 4
+  // values: channel c = 8 lane16 + k of token off goes to half (c % 32) / 16,
+  // token group off / 4, lane row 4 (c / 32) + c % 4, word (c % 16) / 4, byte
+  // off % 4 (the decode's value tiles)
   if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = o.wv;
-  uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + (off >> 2) * 256 + lane16 * 16 + (off & 3);
+  uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + ((lane16 >> 1) & 1) * 1024 + (off >> 2) * 256 +
+                (lane16 >> 2) * 64 + (lane16 & 1) * 8 + (off & 3);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) vc[(k >> 2) * 1024 + (k & 3) * 4] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+  for (int k = 0; k < 8; ++k) vc[(k & 3) * 16 + (k >> 2) * 4] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
   if (SC && lane16 == 0) c.v_scale[pg * 16 + off] = o.vs;
 }
 
@@ -314,7 +316,8 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
       make_uint2(o.kp[0], o.kp[1]);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    sV[(k >> 2) * 1024 + (j >> 2) * 256 + lane16 * 16 + (k & 3) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+    sV[((lane16 >> 1) & 1) * 1024 + (j >> 2) * 256 + (lane16 >> 2) * 64 + (k & 3) * 16 + (lane16 & 1) * 8 +
+       (k >> 2) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
   const bool rep = repaired_row<T>(c, pg, j, kin + in_off, lane16);
   if (lane16 < 8) c.witness[(pg * 16 + j) * 8 + lane16] = rep ? 0.0f : o.w;
   if (SC && lane16 == 0) {

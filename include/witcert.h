@@ -44,8 +44,8 @@
  *            2-bit:    [L][P][Hkv][128][8] bytes (32 tokens of one channel,
  *                      4 codes per byte, token i in bits 2(i%4)).
  *  v_codes   INT8/fp8: [L][P][Hkv][2][4][16][4][4] bytes: token t, channel c
- *                      at [(c%8)/4][t/4][c/8][c%4][t%4] (four tokens of one
- *                      channel are one 32-bit word).
+ *                      at [(c%32)/16][t/4][4(c/32) + c%4][(c%16)/4][t%4]
+ *                      (four tokens of one channel are one 32-bit word).
  *            2-bit:    [L][P][Hkv][32][32] bytes (token-major, 4 codes/byte).
  *            16-bit store: bf16 [L][P][Hkv][4][4][16][2][4]: token t,
  *                      channel c at [(c%8)/2][t/4][c/8][c%2][t%4].

@@ -54,10 +54,10 @@ def gather_k_codes(kc, layer, pt_row, S, g):
 
 def gather_v_codes(vc, layer, pt_row, S, g):
     """[S, 128] value codes from [L][P][Hkv][2][4][16][4][4]: token t, channel c
-    at [(c % 8) // 4][(t % 16) // 4][c // 8][c % 4][t % 4]."""
+    at [(c % 32) // 16][(t % 16) // 4][4 (c // 32) + c % 4][(c % 16) // 4][t % 4]."""
     t = np.arange(S)[:, None]
     c = np.arange(128)[None, :]
-    return vc[layer, pt_row[t // 16], g, (c % 8) // 4, (t % 16) // 4, c // 8, c % 4, t % 4]
+    return vc[layer, pt_row[t // 16], g, (c % 32) // 16, (t % 16) // 4, 4 * (c // 32) + c % 4, (c % 16) // 4, t % 4]
 
 
 def gather_k_bf16(kc, layer, pt_row, S, g):
