@@ -856,7 +856,6 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     // of the four halves addressed by lane 4 e + n / 4, as its element e; so
     // lane n addresses token 4k + n / 4, channels 32 (n % 4) + 4 t onward, and
     // receives the four tokens' operands of its channel, in token order.
-    const uint8_t* hrow = reinterpret_cast<const uint8_t*>(sH[4 * kq + (n >> 2)]) + 64 * (n & 3);
     if (SCHEME == WC_DITHER_INT8) __builtin_amdgcn_wave_barrier();
     // raw = sum q' (code - xi) (a repaired block: sum q' k of the exact keys)
     float raw[4] = {Dc[0], Dc[1], Dc[2], Dc[3]};
@@ -1075,6 +1074,12 @@ decode_kernel(wc_cache c, DecodeArgs a) {
       vsum = __builtin_amdgcn_fdot2(make_h2(Bc[2], Bc[3]), ones, vsum, false);
       const h8 B2 = make_h8(as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])),
                             as_u32(make_h2(Bc[0], Bc[1])), as_u32(make_h2(Bc[2], Bc[3])));
+      // (with the outlier bypass the address is formed here from a laundered
+      // lane index, so that it holds no register through the rest of the
+      // page: those instances are the ones at the register limit)
+      int ln = lane;
+      if (NO4 > 0) asm volatile("" : "+v"(ln));
+      const uint8_t* hrow = reinterpret_cast<const uint8_t*>(sH[4 * (ln >> 4) + ((ln >> 2) & 3)]) + 64 * (ln & 3);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         uint32_t c0, c1;
