@@ -779,19 +779,31 @@ def trace_phases(kt_dir, warmup, steps, loops=10, iters=20):
     return out
 
 
-def counter_means(dirs, launches):
+def counter_means(dirs, launches, kernels=None):
     """Mean per dispatch of every counter in rocprofv3 --pmc runs (the
-    directories given) over the first `launches` dispatches of each decode
-    instance of the dithered INT8 and fp8 headline configurations."""
+    directories given): over the first `launches` dispatches of the dithered
+    INT8 and fp8 headline decode instances, or, with `kernels` (name
+    substrings), over every dispatch of each kernel whose name holds one."""
     import numpy as np
     out = {}
-    for name in (HEADLINE_KERNEL, HEADLINE_KERNEL.replace("<0,", "<1,")):
+    rows_all = [row for d in dirs for row in _counter_rows(d)]
+    if kernels:
+        names = sorted({r[0].split("(")[0] for r in rows_all if any(k in r[0] for k in kernels)})
+    else:
+        names = [HEADLINE_KERNEL, HEADLINE_KERNEL.replace("<0,", "<1,")]
+    for name in names:
         acc = {}
         for d in dirs:
             rows = [r for r in _counter_rows(d) if name in r[0]]
-            ids = sorted({r[2] for r in rows})[:launches]
+            ids = sorted({r[2] for r in rows})
+            if not kernels:
+                ids = ids[:launches]
             for c in sorted({r[3] for r in rows}):
-                acc[c] = float(np.mean([sum(r[4] for r in rows if r[2] == i and r[3] == c) for i in ids]))
+                per = {}
+                for r in rows:
+                    if r[3] == c:
+                        per[r[2]] = per.get(r[2], 0.0) + r[4]
+                acc[c] = float(np.mean([per[i] for i in ids if i in per]))
         out[name] = acc
     return out
 
@@ -825,12 +837,15 @@ def main():
     ap.add_argument("--counter-means", nargs="+", metavar="DIR",
                     help="no GPU: per-dispatch means of the counters of rocprofv3 --pmc runs of "
                          "`bench.py --steps K --warmup W --no-cpu` for the INT8 and fp8 decode instances")
+    ap.add_argument("--kernels", default=None,
+                    help="--counter-means: comma-separated kernel name substrings (every dispatch of each)")
     args = ap.parse_args()
     if args.trace_phases:
         print(json.dumps(trace_phases(args.trace_phases, args.warmup, args.steps)), flush=True)
         return
     if args.counter_means:
-        print(json.dumps(counter_means(args.counter_means, args.warmup + args.steps)), flush=True)
+        print(json.dumps(counter_means(args.counter_means, args.warmup + args.steps,
+                                       args.kernels.split(",") if args.kernels else None)), flush=True)
         return
     if args.reduce_counters:
         res = reduce_counters(*args.reduce_counters, args.warmup + args.steps, args.batch, args.ctx,

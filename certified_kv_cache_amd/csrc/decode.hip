@@ -906,7 +906,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     // (a value scale above the largest seen so far also rescales: the
     // weights p s_v fed to the fp16 PV operand are kept in range by taking
     // m_ref = the running max minus sig, with the wave-uniform sig chosen so
-    // that s_max 2^sig lies in (64, 128]: then p s_v <= 2^8 2^7 and the
+    // that s_max 2^sig lies in [64, 128): then p s_v < 2^8 2^7 and the
     // weights of the largest scales stay far above fp16's subnormals.  Every
     // sum is taken relative to m_ref, so sig cancels in o, LSE and the meters.)
     const bool need_m = lmax > m_lim;

@@ -100,3 +100,16 @@ def test_trace_phases(tmp_path):
     assert r["headline_dispatches"] == 35 and r["steps_mean_us"] == 251.0
     assert r["risk_loops_median_us"] == 241.0 and r["on_loops_median_us"] == 231.0
     assert r["kernel_stats"][dec]["avg_us"] == 300.0 and r["kernel_stats"][dec]["calls"] == 35
+
+
+def test_counter_means(tmp_path):
+    dec = "void wc::" + bench.HEADLINE_KERNEL + "(wc_cache, wc::DecodeArgs)"
+    wr = "void wc::write_rows_kernel<unsigned short, 0, false>(wc_cache, unsigned short const*)"
+    rows = [(dec, 100, "SQ_INSTS_VALU", 10.0 * (i + 1)) for i in range(6)] + \
+           [(wr, 100, "FETCH_SIZE", 5.0), (wr, 100, "FETCH_SIZE", 7.0)]
+    _counter_csv(str(tmp_path / "s" / "h" / "1_counter_collection.csv"), rows)
+    r = bench.counter_means([str(tmp_path / "s")], 4)
+    assert r[bench.HEADLINE_KERNEL]["SQ_INSTS_VALU"] == 25.0      # the first four dispatches
+    r = bench.counter_means([str(tmp_path / "s")], 4, kernels=["wc::write"])
+    assert list(r) == ["void wc::write_rows_kernel<unsigned short, 0, false>"]
+    assert r["void wc::write_rows_kernel<unsigned short, 0, false>"]["FETCH_SIZE"] == 6.0
