@@ -509,10 +509,15 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     const int sl = (i < npw && c.exact_slot) ? c.exact_slot[(pg_base + ph) * c.num_kv_heads + g] : -1;
     bslot = kDepth == 1 ? sl : settle(sl);
   };
+  // Past the wave's last page the prefetch requests physical page 0 of the
+  // layer: the loads (and so every wait) are the same as for a real page, the
+  // data is never used, and the block, requested by every wave, stays in L2
+  // instead of a last page being read from HBM a second time.
   auto fetch = [&](int i, KLoad& d, VLoad& e) {
-    if ((i & 63) == 0) batch(i);
-    const int phys = __builtin_amdgcn_readlane(bphys, i & 63);
-    if (kDepth > 1) d.slot = __builtin_amdgcn_readlane(bslot, i & 63);
+    const bool past = i >= npw;
+    if (!past && (i & 63) == 0) batch(i);
+    const int phys = past ? 0 : __builtin_amdgcn_readlane(bphys, i & 63);
+    if (kDepth > 1) d.slot = past ? -1 : __builtin_amdgcn_readlane(bslot, i & 63);
     if (SOFF)
       load_page_soff<SCHEME, CMP, NO4, MV>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, d, e);
     else
@@ -520,9 +525,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   };
   KLoad kA, kB;
   VLoad vA, vB;
-  // (also with no page: the request for physical page 0 is in bounds and
-  // unused, and every path then waits for the query words here)
-  if (kDepth == 1) fetch(0, kA, vA);
+  // (also with no page: the batch of a wave without pages reads no table and
+  // requests physical page 0, in bounds and unused, and every path then
+  // waits for the query words here)
+  if (kDepth == 1) {
+    batch(0);
+    const int phys = __builtin_amdgcn_readlane(bphys, 0);
+    if (SOFF)
+      load_page_soff<SCHEME, CMP, NO4, MV>(lb, (uint32_t)(phys * c.num_kv_heads + g), lo, meterA, kA, vA);
+    else
+      load_page<SCHEME, CMP, NO4, MV>(c, (pg_base + phys) * c.num_kv_heads + g, lo, meterA, kA, vA);
+  }
   float qf[32];
   if (hv) {
     if (QF32) {
@@ -738,7 +751,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     // so that every iteration issues the same loads
     // (its exact-pool slot first: the prefetch below may start the next batch)
     const int slot = kDepth == 1 ? __builtin_amdgcn_readlane(bslot, i & 63) : cur.slot;
-    fetch(min(i + kDepth, npw - 1), nxt, vnxt);
+    fetch(i + kDepth, nxt, vnxt);
     const int jj = w0 + i;
     const int tok0 = jj * 16;
     const bool exact = slot >= 0;              // wave-uniform
@@ -1298,6 +1311,11 @@ __global__ void __launch_bounds__(kThreads) decode_floor_kernel(wc_cache c, Floo
   uint32_t acc = 0;
   int bphys = 0, bslot = -1;
   auto fetch = [&](int i, KLoad& d, VLoad& e) {
+    if (i >= npw) {                            // past the last page: physical page 0, as the decode
+      d.slot = -1;
+      load_page_soff<SCHEME, PAIR, 0, false>(lb, (uint32_t)g, lo, meterA, d, e);
+      return;
+    }
     if ((i & 63) == 0) {
       const int j = i + lane;
       const int ph = j < npw ? ptab[w0 + j] : 0;
@@ -1320,10 +1338,10 @@ __global__ void __launch_bounds__(kThreads) decode_floor_kernel(wc_cache c, Floo
   VLoad vA, vB;
   if (npw > 0) fetch(0, kA, vA);
   for (int i = 0; i < npw; i += 2) {
-    fetch(min(i + 1, npw - 1), kB, vB);
+    fetch(i + 1, kB, vB);
     fold(kA, vA);
     if (i + 1 >= npw) break;
-    fetch(min(i + 2, npw - 1), kA, vA);
+    fetch(i + 2, kA, vA);
     fold(kB, vB);
   }
   if (acc == 0x9E3779B9u) a.sink[0] = acc;
