@@ -567,10 +567,14 @@ def decode_bounds(B, S, iters=20):
 
         t = time_modes(decode, iters, {n: dict(name=n) for n in modes}, warm=60)
         res[tname] = {n: round(v, 2) for n, v in t.items()}
-        if tname == "hbm":
-            # board power and shader clock while each mode runs back to back
-            # for about four seconds (amd-smi sampled once in the middle)
-            res["power_clock"] = {n: power_clock(lambda: decode(n)) for n in modes}
+        # board power and shader clock while each mode runs back to back for
+        # about four seconds (amd-smi sampled once in the middle): the clock
+        # the power limit leaves differs between the two tables
+        res.setdefault("power_clock", {})[tname] = {n: power_clock(lambda: decode(n)) for n in modes}
+    # the decode's loads alone (INT8 cache, meter on, same grid and residency)
+    floor = make_floor(w, B, w["cache"])
+    res["hbm"]["int8_load_floor"] = round(time_modes(lambda: floor(), iters, {"f": {}}, warm=60)["f"], 2)
+    res["power_clock"]["hbm"]["int8_load_floor"] = power_clock(lambda: floor())
     return res
 
 

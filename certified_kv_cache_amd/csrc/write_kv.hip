@@ -12,6 +12,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "wc_common.h"
 
 namespace wc {
@@ -34,31 +36,68 @@ int check_launch(const char* what) {
   return WC_OK;
 }
 
+// The same maximum for values that are >= 0 and not NaN: their order is that
+// of their bit patterns, one integer max with a DPP operand per step.
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kRowRor8, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kRowRor4, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQuadSwap2, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQuadSwap1, 0xF, 0xF, false));
+  return __uint_as_float(u);
+}
+// Lane N of each 16-lane row, to every lane of that row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row16_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
 // Inputs are read once and code blocks written once: their accesses carry
 // the non-temporal cache policy (native vector types, which the builtins take).
 typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
 typedef float nt_f4 __attribute__((ext_vector_type(4)));
 
+// One lane's 8 input channels as loaded (16 B of bf16 or 32 B of fp32), kept
+// raw so that the loads can be issued ahead of the work that waits on them.
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
-
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-  const nt_f4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p));
-  const nt_f4 b = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p + 4));
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+struct Raw8<uint16_t> {
+  nt_u4 a;
+};
+template <>
+struct Raw8<float> {
+  nt_f4 a, b;
+};
+
+template <typename T>
+__device__ __forceinline__ Raw8<T> load_raw8(const T* p);
+template <>
+__device__ __forceinline__ Raw8<float> load_raw8<float>(const float* p) {
+  return Raw8<float>{__builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p)),
+                     __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p + 4))};
+}
+template <>
+__device__ __forceinline__ Raw8<uint16_t> load_raw8<uint16_t>(const uint16_t* p) {
+  return Raw8<uint16_t>{__builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p))};
 }
 
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
-  const nt_u4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
-  uint32_t w[4] = {a.x, a.y, a.z, a.w};
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&x)[8]) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+__device__ __forceinline__ void unpack8(const Raw8<uint16_t>& r, float (&x)[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = __uint_as_float(w[i] << 16);
     x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
+  unpack8(load_raw8<T>(p), x);
 }
 
 struct RowArgs {
@@ -149,46 +188,58 @@ struct RowQ {
 // OUTL: dithered INT8 keys with the outlier bypass (bf16 input): the
 // channels in omask are excluded from the key absmax, coded 0 with a zero
 // residual (their exact keys go to the side store, written by the caller).
+//
+// The row-level steps are shared out over the row's 16 lanes instead of being
+// repeated on each: the four scale quotients (s and 1/s of K and of V) are one
+// correctly rounded division, lanes 4j..4j+3 taking quotient j, and the key's
+// band norms (lanes 0..7) and the value's row norm (lanes 8..15) one square
+// root; each result is then broadcast within the row.
 template <typename T, int SCHEME>
-__device__ __forceinline__ RowQ quant_row(const T* kin, const T* vin, int64_t in_off, const uint32_t (&words)[4],
+__device__ __forceinline__ RowQ quant_row(const Raw8<T>& krow, const Raw8<T>& vrow, const uint32_t (&words)[4],
                                           uint32_t omask) {
-  RowQ o;
+  constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
+  const int lane16 = threadIdx.x & 15;
+  float xk[8], xv[8];
+  unpack8(krow, xk);
+  unpack8(vrow, xv);
+  float sk = 0.0f, ik = 0.0f, sv = 0.0f, iv = 0.0f;
+  if (SC) {
+    // absmax from 0 up: a NaN input never wins, so both maxima are finite or
+    // +inf and their 16-lane maxima can be taken on the bit patterns
+    float amk = 0.0f, amv = 0.0f;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const bool isv = which == 1;
-    float x[8];
-    load8<T>((isv ? vin : kin) + in_off, x);
-    const uint32_t ex = isv ? 0u : omask;
-    float am = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) am = fmaxf(am, ((ex >> k) & 1u) ? 0.0f : fabsf(x[k]));
-    am = row16_max(am);
-    float s = 0.0f, inv = 0.0f;
-    if ((SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8) && am > 0.0f) {
-      s = div_rn(am, 127.0f);
-      inv = div_rn(127.0f, am);
+    for (int k = 0; k < 8; ++k) {
+      amk = fmaxf(amk, ((omask >> k) & 1u) ? 0.0f : fabsf(xk[k]));
+      amv = fmaxf(amv, fabsf(xv[k]));
     }
-    uint32_t packed[2];
-    float r[8];
-    quant8<SCHEME>(x, s, inv, words, ex, packed, r);
-    float ss = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ss = fmaf(r[k], r[k], ss);
-    if (!isv) {
-      const float tot = ss + dpp_f<kRowRor8>(ss);   // lanes l, l + 8: the two halves of band l % 8
-      o.w = sqrtf(tot) * kWitnessGuard;
-      o.kp[0] = packed[0];
-      o.kp[1] = packed[1];
-      o.ks = s;
-    } else {
-      // value witness ||v^ - v|| over the row's 128 channels (16-lane sum)
-      ss = row16_sum(ss);
-      o.wv = sqrtf(ss) * kWitnessGuard;
-      o.vp[0] = packed[0];
-      o.vp[1] = packed[1];
-      o.vs = s;
-    }
+    amk = row16_max_nonneg(amk);
+    amv = row16_max_nonneg(amv);
+    const int role = lane16 >> 2;              // 0: amk / 127, 1: 127 / amk, 2, 3: the same of amv
+    const float am = role < 2 ? amk : amv;
+    const float qt = (role & 1) ? div_rn(127.0f, am) : div_rn(am, 127.0f);
+    // (an all-zero row keeps s = 1/s = 0)
+    sk = amk > 0.0f ? row16_bcast<0>(qt) : 0.0f;
+    ik = amk > 0.0f ? row16_bcast<4>(qt) : 0.0f;
+    sv = amv > 0.0f ? row16_bcast<8>(qt) : 0.0f;
+    iv = amv > 0.0f ? row16_bcast<12>(qt) : 0.0f;
   }
+  RowQ o;
+  float rk[8], rv[8];
+  quant8<SCHEME>(xk, sk, ik, words, omask, o.kp, rk);
+  quant8<SCHEME>(xv, sv, iv, words, 0u, o.vp, rv);
+  o.ks = sk;
+  o.vs = sv;
+  float ssk = 0.0f, ssv = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ssk = fmaf(rk[k], rk[k], ssk);
+    ssv = fmaf(rv[k], rv[k], ssv);
+  }
+  ssk += dpp_f<kRowRor8>(ssk);                 // lanes l, l + 8: the two halves of band l % 8
+  ssv = row16_sum(ssv);                        // value witness ||v^ - v|| over the row's 128 channels
+  const float nrm = sqrtf(lane16 < 8 ? ssk : ssv) * kWitnessGuard;
+  o.w = nrm;                                   // (lanes 0..7: band lane16)
+  o.wv = row16_bcast<8>(nrm);
   return o;
 }
 
@@ -210,11 +261,13 @@ __device__ __forceinline__ void bypass_lanes(const wc_cache& c, int layer, int h
 // also stores its exact key (bf16, 8 channels per lane) in the block's pool
 // row, and its witness is 0 (the decode takes c = 0 there).  The host refuses
 // float32 keys for a cache with exact_slot set, so only the bf16 instance
-// copies.  Returns whether the row's block is repaired.
+// copies.  es: the block's exact_slot entry (null: no pool).  Returns whether
+// the row's block is repaired.
 template <typename T>
-__device__ __forceinline__ bool repaired_row(const wc_cache& c, int64_t pg, int64_t off, const T* krow, int lane16) {
-  if (!c.exact_slot) return false;
-  const int32_t s = c.exact_slot[pg];
+__device__ __forceinline__ bool repaired_row(const wc_cache& c, const int32_t* es, int64_t off, const T* krow,
+                                             int lane16) {
+  if (!es) return false;
+  const int32_t s = *es;
   if (s < 0) return false;
   if constexpr (sizeof(T) == 2) {
     const uint4 x = *reinterpret_cast<const uint4*>(krow);
@@ -223,54 +276,116 @@ __device__ __forceinline__ bool repaired_row(const wc_cache& c, int64_t pg, int6
   return true;
 }
 
+// Element base + e of p.  W32: the launch's every in-layer offset e (in
+// bytes) fits in 32 bits, which the host checks; then each access takes the
+// wave-uniform p + base and one 32-bit lane offset, not a 64-bit address
+// computed per lane.
+template <bool W32, typename P>
+__device__ __forceinline__ P* at(P* p, int64_t base, typename std::conditional<W32, uint32_t, int64_t>::type e) {
+  if (!W32) return p + base + e;
+  using B = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+  return reinterpret_cast<P*>(reinterpret_cast<B*>(p + base) + (uint32_t)(e * (uint32_t)sizeof(P)));
+}
+
 // Grid (ceil(n_tok / 16), Hkv, n_layers): 16 consecutive tokens of one KV
-// head per workgroup (no index division).
-template <typename T, int SCHEME, bool OUTL>
+// head per workgroup (no index division).  When the workgroup's 16 rows are
+// the 16 tokens of one page in order (a prefill written through this call),
+// the page's code blocks are assembled in LDS and leave as whole 16-byte
+// lines, as in the page path; otherwise each row stores its own bytes (a
+// token's value codes are every fourth byte of its block).
+template <typename T, int SCHEME, bool OUTL, bool W32>
 __global__ void __launch_bounds__(256) write_rows_kernel(wc_cache c, const T* __restrict__ kin,
                                                          const T* __restrict__ vin, RowArgs a) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  __shared__ __align__(16) uint8_t sK[2048];
+  __shared__ __align__(16) uint8_t sV[2048];
+  using IX = typename std::conditional<W32, uint32_t, int64_t>::type;   // in-layer offsets
+  const int lane16 = threadIdx.x & 15, j = threadIdx.x >> 4;
+  const int64_t tok0 = (int64_t)blockIdx.x * 16;                      // < n_tok
+  const int64_t tok = tok0 + j;
   const bool live = tok < a.n_tok;
-  const int64_t i = live ? tok : 0;
+  const IX i = live ? (IX)tok : (IX)0;        // (n_tok <= 2^26)
   const int g = blockIdx.y, l = blockIdx.z;
   const int layer = a.layer0 + l;
-  const int64_t slot = a.slot[i];
-  const int64_t page = slot / 16, off = slot % 16;
-  const int32_t p = a.pos[i];
-  const int64_t in_off = (int64_t)l * a.layer_stride + (i * a.hkv + g) * 128 + 8 * lane16;
-  const int64_t pg = ((int64_t)layer * a.num_pages + page) * a.hkv + g;   // page-head block
+  const int64_t slot = *at<W32>(a.slot, 0, i);
+  const IX page = (IX)(slot / 16), off = (IX)(slot % 16);
+  const int32_t p = *at<W32>(a.pos, 0, i);
+  const IX in_e = (i * (IX)a.hkv + (IX)g) * 128 + (IX)(8 * lane16);
+  const int64_t in_base = (int64_t)l * a.layer_stride;
+  const T* krow = at<W32>(kin, in_base, in_e);
+  const T* vrow = at<W32>(vin, in_base, in_e);
+  // the input rows and the first row's slot are requested before anything
+  // waits on the index loads above
+  const Raw8<T> rk = load_raw8<T>(krow), rv = load_raw8<T>(vrow);
+  const int64_t s0 = *at<W32>(a.slot, 0, (IX)tok0);
+  const int64_t lpg = (int64_t)layer * a.num_pages * a.hkv;         // the layer's first page-head block
+  const IX pgl = page * (IX)a.hkv + (IX)g;                           // the row's block within the layer
 
   uint32_t omask = 0;
   int ochan = -1;
   if (OUTL) bypass_lanes(c, layer, a.hkv, g, lane16, omask, ochan);
   uint32_t words[4] = {0u, 0u, 0u, 0u};
   if (SCHEME == WC_DITHER_INT8) {
-    const uint32_t key = stream_key(a.seed[i], (uint32_t)layer, (uint32_t)g);
+    // the wave's four rows usually belong to one sequence: then its key is
+    // chained once, in scalar registers
+    const uint64_t sd = *at<W32>(a.seed, 0, i);
+    const uint32_t lo = (uint32_t)sd, hi = (uint32_t)(sd >> 32);
+    const uint32_t lo0 = __builtin_amdgcn_readfirstlane(lo), hi0 = __builtin_amdgcn_readfirstlane(hi);
+    uint32_t key;
+    if (__builtin_amdgcn_ballot_w64(lo != lo0 || hi != hi0) == 0)
+      key = stream_key(((uint64_t)hi0 << 32) | lo0, (uint32_t)layer, (uint32_t)g);
+    else
+      key = stream_key(sd, (uint32_t)layer, (uint32_t)g);
 #pragma unroll
     for (int w = 0; w < 4; ++w) words[w] = pcg_out_sdwa((key + (uint32_t)(64 * p + 4 * lane16 + w)) * kPcgMul + kPcgInc);
   }
-  const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
-  if (!live) return;
+  const RowQ o = quant_row<T, SCHEME>(rk, rv, words, omask);
+  // whole page: row j is token j of the page that holds the first row's slot
+  const bool whole = __syncthreads_and(live && slot == s0 + j && (s0 & 15) == 0);   // workgroup-uniform
   constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
   // keys: channels 8 lane16 .. +7 of token off: half (lane16 % 4) / 2, 32-channel
-  // group lane16 / 4, bytes 8 (lane16 % 2) .. of the token's 16-byte chunk
-  uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + pg * 2048 + ((lane16 & 3) >> 1) * 1024 +
-                (lane16 >> 2) * 256 + off * 16 + 8 * (lane16 & 1);
-  *reinterpret_cast<uint2*>(kc) = make_uint2(o.kp[0], o.kp[1]);
-  const bool rep = repaired_row<T>(c, pg, off, kin + in_off, lane16);
-  if (lane16 < 8) c.witness[(pg * 16 + off) * 8 + lane16] = rep ? 0.0f : o.w;
-  if (SC && lane16 == 0) c.k_scale[pg * 16 + off] = o.ks;
-  if (OUTL && ochan >= 0)
-    c.k_outlier[(pg * 16 + off) * c.num_outliers + lane16] = reinterpret_cast<const uint16_t*>(kin)[in_off - 8 * lane16 + ochan];
+  // group lane16 / 4, bytes 8 (lane16 % 2) .. of the token's 16-byte chunk;
   // values: channel c = 8 lane16 + k of token off goes to half (c % 32) / 16,
   // token group off / 4, lane row 4 (c / 32) + c % 4, word (c % 16) / 4, byte
   // off % 4 (the decode's value tiles)
-  if (c.v_witness && lane16 == 0) c.v_witness[pg * 16 + off] = o.wv;
-  uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + pg * 2048 + ((lane16 >> 1) & 1) * 1024 + (off >> 2) * 256 +
-                (lane16 >> 2) * 64 + (lane16 & 1) * 8 + (off & 3);
+  const int kin_blk = ((lane16 & 3) >> 1) * 1024 + (lane16 >> 2) * 256 + 8 * (lane16 & 1);
+  const int vin_blk = ((lane16 >> 1) & 1) * 1024 + (lane16 >> 2) * 64 + (lane16 & 1) * 8;
+  if (whole) {
+    *reinterpret_cast<uint2*>(sK + kin_blk + j * 16) = make_uint2(o.kp[0], o.kp[1]);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) vc[(k & 3) * 16 + (k >> 2) * 4] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
-  if (SC && lane16 == 0) c.v_scale[pg * 16 + off] = o.vs;
+    for (int k = 0; k < 8; ++k)
+      sV[vin_blk + (j >> 2) * 256 + (k & 3) * 16 + (k >> 2) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+  } else if (live) {
+    uint8_t* kc = at<W32>(reinterpret_cast<uint8_t*>(c.k_codes), lpg * 2048, pgl * 2048 + (IX)kin_blk + off * 16);
+    *reinterpret_cast<uint2*>(kc) = make_uint2(o.kp[0], o.kp[1]);
+    uint8_t* vc = at<W32>(reinterpret_cast<uint8_t*>(c.v_codes), lpg * 2048,
+                          pgl * 2048 + (IX)vin_blk + (off >> 2) * 256 + (off & 3));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vc[(k & 3) * 16 + (k >> 2) * 4] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
+  }
+  if (live) {
+    const int32_t* es = c.exact_slot ? at<W32>((const int32_t*)c.exact_slot, lpg, pgl) : nullptr;
+    const bool rep = repaired_row<T>(c, es, (int64_t)off, krow, lane16);
+    const IX row = pgl * 16 + off;                                   // (block, token) within the layer
+    if (lane16 < 8) *at<W32>(c.witness, lpg * 128, row * 8 + (IX)lane16) = rep ? 0.0f : o.w;
+    if (SC && lane16 == 0) {
+      *at<W32>(c.k_scale, lpg * 16, row) = o.ks;
+      *at<W32>(c.v_scale, lpg * 16, row) = o.vs;
+    }
+    if (c.v_witness && lane16 == 0) *at<W32>(c.v_witness, lpg * 16, row) = o.wv;
+    if (OUTL && ochan >= 0)
+      *at<W32>(c.k_outlier, lpg * 16 * c.num_outliers, row * (IX)c.num_outliers + (IX)lane16) =
+          reinterpret_cast<const uint16_t*>(krow - 8 * lane16)[ochan];
+  }
+  if (whole) {
+    __syncthreads();
+    // threads 0..127 the key block, 128..255 the value block, 16 bytes each
+    const int t = threadIdx.x & 127;
+    const IX pg0 = (IX)(s0 / 16) * (IX)a.hkv + (IX)g;
+    uint8_t* dst = at<W32>(reinterpret_cast<uint8_t*>(threadIdx.x < 128 ? c.k_codes : c.v_codes), lpg * 2048,
+                           pg0 * 2048 + (IX)(16 * t));
+    __builtin_nontemporal_store(*reinterpret_cast<const nt_u4*>((threadIdx.x < 128 ? sK : sV) + 16 * t),
+                                reinterpret_cast<nt_u4*>(dst));
+  }
 }
 
 // Whole pages (prefill): one workgroup per (layer, page, KV head) block, row
@@ -310,7 +425,7 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
 #pragma unroll
     for (int w = 0; w < 4; ++w) words[w] = pcg_out_sdwa((key + (uint32_t)(64 * p + 4 * lane16 + w)) * kPcgMul + kPcgInc);
   }
-  const RowQ o = quant_row<T, SCHEME>(kin, vin, in_off, words, omask);
+  const RowQ o = quant_row<T, SCHEME>(load_raw8<T>(kin + in_off), load_raw8<T>(vin + in_off), words, omask);
   constexpr bool SC = SCHEME == WC_DITHER_INT8 || SCHEME == WC_RTN_INT8;
   *reinterpret_cast<uint2*>(sK + ((lane16 & 3) >> 1) * 1024 + (lane16 >> 2) * 256 + j * 16 + 8 * (lane16 & 1)) =
       make_uint2(o.kp[0], o.kp[1]);
@@ -318,7 +433,7 @@ __global__ void __launch_bounds__(256) write_pages_kernel(wc_cache c, const T* _
   for (int k = 0; k < 8; ++k)
     sV[((lane16 >> 1) & 1) * 1024 + (j >> 2) * 256 + (lane16 >> 2) * 64 + (k & 3) * 16 + (lane16 & 1) * 8 +
        (k >> 2) * 4 + (j & 3)] = (uint8_t)(o.vp[k >> 2] >> (8 * (k & 3)));
-  const bool rep = repaired_row<T>(c, pg, j, kin + in_off, lane16);
+  const bool rep = repaired_row<T>(c, c.exact_slot ? c.exact_slot + pg : nullptr, j, kin + in_off, lane16);
   if (lane16 < 8) c.witness[(pg * 16 + j) * 8 + lane16] = rep ? 0.0f : o.w;
   if (SC && lane16 == 0) {
     c.k_scale[pg * 16 + j] = o.ks;
@@ -397,7 +512,7 @@ __global__ void __launch_bounds__(256) witness_kernel(wc_cache c, const T* __res
   const int64_t slot = a.slot[i];
   const int64_t pg = ((int64_t)(a.layer0 + l) * a.num_pages + slot / 16) * a.hkv + g;
   // a repaired block: the exact key x to the pool row, witness 0
-  const bool rep = repaired_row<T>(c, pg, slot % 16, x + in_off, lane16);
+  const bool rep = repaired_row<T>(c, c.exact_slot ? c.exact_slot + pg : nullptr, slot % 16, x + in_off, lane16);
   if (lane16 < 8) c.witness[(pg * 16 + slot % 16) * 8 + lane16] = rep ? 0.0f : sqrtf(tot) * kWitnessGuard;
 }
 
@@ -664,31 +779,31 @@ extern "C" int wc_write_kv(const wc_cache* cache, int layer0, int n_layers, cons
       }
     }
     dim3 grid((unsigned)((n_tok + 15) / 16), (unsigned)c.num_kv_heads, (unsigned)n_layers);
+    // 32-bit in-layer offsets when one layer's code array and one layer of
+    // input fit in 4 GB (the index arrays do: n_tok <= 2^26)
+    const int64_t esize = in_dtype == WC_BF16 ? 2 : 4;
+    const bool w32 = c.num_pages * c.num_kv_heads * 2048 <= (int64_t(1) << 32) &&
+                     n_tok * c.num_kv_heads * 128 * esize <= (int64_t(1) << 32);
+#define WC_ROWS(T, SCH, OU)                                                                                    \
+  do {                                                                                                         \
+    if (w32)                                                                                                   \
+      hipLaunchKernelGGL((write_rows_kernel<T, SCH, OU, true>), grid, dim3(256), 0, st, c, (const T*)k,      \
+                         (const T*)v, a);                                                                      \
+    else                                                                                                       \
+      hipLaunchKernelGGL((write_rows_kernel<T, SCH, OU, false>), grid, dim3(256), 0, st, c, (const T*)k,     \
+                         (const T*)v, a);                                                                      \
+  } while (0)
+    const bool bf = in_dtype == WC_BF16;
     if (c.scheme == WC_DITHER_INT8) {
-      if (c.num_outliers != 0)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8, true>), grid, dim3(256), 0, st, c,
-                           (const uint16_t*)k, (const uint16_t*)v, a);
-      else if (in_dtype == WC_BF16)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c,
-                           (const uint16_t*)k, (const uint16_t*)v, a);
-      else
-        hipLaunchKernelGGL((write_rows_kernel<float, WC_DITHER_INT8, false>), grid, dim3(256), 0, st, c,
-                           (const float*)k, (const float*)v, a);
+      if (c.num_outliers != 0) WC_ROWS(uint16_t, WC_DITHER_INT8, true);
+      else if (bf) WC_ROWS(uint16_t, WC_DITHER_INT8, false);
+      else WC_ROWS(float, WC_DITHER_INT8, false);
     } else if (c.scheme == WC_RTN_INT8) {
-      if (in_dtype == WC_BF16)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_RTN_INT8, false>), grid, dim3(256), 0, st, c,
-                           (const uint16_t*)k, (const uint16_t*)v, a);
-      else
-        hipLaunchKernelGGL((write_rows_kernel<float, WC_RTN_INT8, false>), grid, dim3(256), 0, st, c,
-                           (const float*)k, (const float*)v, a);
+      if (bf) WC_ROWS(uint16_t, WC_RTN_INT8, false); else WC_ROWS(float, WC_RTN_INT8, false);
     } else {
-      if (in_dtype == WC_BF16)
-        hipLaunchKernelGGL((write_rows_kernel<uint16_t, WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c,
-                           (const uint16_t*)k, (const uint16_t*)v, a);
-      else
-        hipLaunchKernelGGL((write_rows_kernel<float, WC_FP8_E4M3, false>), grid, dim3(256), 0, st, c,
-                           (const float*)k, (const float*)v, a);
+      if (bf) WC_ROWS(uint16_t, WC_FP8_E4M3, false); else WC_ROWS(float, WC_FP8_E4M3, false);
     }
+#undef WC_ROWS
     return check_launch("wc_write_kv");
   }
   if (c.scheme == WC_KIVI2) {

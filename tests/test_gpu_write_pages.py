@@ -1,5 +1,8 @@
 """GPU parity of the whole-page write (wc_write_kv_pages): against the oracle
-on every page, and bit-identical to the per-token write of the same tokens."""
+on every page, and bit-identical to the per-token write of the same tokens,
+both in page order (each workgroup of the per-token write then holds one whole
+page and stores it as whole lines) and shuffled (each row stores its own
+bytes)."""
 import numpy as np
 import pytest
 import torch
@@ -43,7 +46,7 @@ def test_write_pages_matches_oracle_and_row_write(scheme, dtype, m):
     pages = rng.permutation(P)[:NP].astype(np.int32)
     pos0 = (16 * rng.integers(0, 1000, NP)).astype(np.int32)
     seeds = rng.integers(0, 2 ** 62, NP).astype(np.int64)
-    caches = [L.KVCache(sch, NL + 1, P, HKV, num_outliers=m, v_witness=True) for _ in range(2)]
+    caches = [L.KVCache(sch, NL + 1, P, HKV, num_outliers=m, v_witness=True) for _ in range(3)]
     O = None
     if m:
         O = np.stack([np.stack([outlier.top_energy_channels(k32[l, :, g], m) for g in range(HKV)])
@@ -58,12 +61,16 @@ def test_write_pages_matches_oracle_and_row_write(scheme, dtype, m):
     pos = torch.from_numpy((pos0[t // 16] + t % 16).astype(np.int32)).cuda()
     tseed = torch.from_numpy(seeds[t // 16]).cuda()
     L.wc_write_kv(caches[1], kd, vd, slot, pos, tseed, layer0=1)
+    sh = torch.from_numpy(rng.permutation(NP * 16)).cuda()              # no workgroup holds a whole page
+    L.wc_write_kv(caches[2], kd[:, sh].contiguous(), vd[:, sh].contiguous(), slot[sh], pos[sh], tseed[sh], layer0=1)
     torch.cuda.synchronize()
     names = ["k_codes", "v_codes", "witness", "v_witness"] + (["k_scale", "v_scale"] if scheme != "fp8" else []) + \
             (["k_outlier"] if m else [])
-    for nm in names:                                 # the two writes agree bit for bit
-        a, b = getattr(caches[0], nm).cpu().numpy(), getattr(caches[1], nm).cpu().numpy()
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), nm
+    for nm in names:                                 # the three writes agree bit for bit
+        a = getattr(caches[0], nm).cpu().numpy()
+        for j in (1, 2):
+            b = getattr(caches[j], nm).cpu().numpy()
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (nm, j)
     c = caches[0]
     kc, vc, wt, wv = (getattr(c, nm).cpu().numpy() for nm in ("k_codes", "v_codes", "witness", "v_witness"))
     for l in range(NL):
