@@ -399,9 +399,10 @@ def prefill_write(iters, seed=4, NL=28, NT=4096):
             psd = torch.full((NT // 16,), 777, dtype=torch.int64, device="cuda")
             calls.append(("_pages", lambda: L.wc_write_kv_pages(cache, k, v, pg, p0, psd)))
         for suffix, call in calls:
-            # 100 untimed calls first: the clocks settle after a few hundred
-            # microseconds of back-to-back work
-            us = time_decode(call, iters, warm=100)
+            # 400 untimed calls first (the shader clock that the power limit
+            # leaves takes tens of milliseconds of back-to-back work to
+            # settle), then the median of three timed loops
+            us = float(np.median([time_decode(call, iters, warm=400 if r == 0 else 0) for r in range(3)]))
             tot = in_bytes + written
             out["schemes"][name + suffix] = {"us": round(us, 2), "bytes_written": written, "bytes_total": tot,
                                              "written_GBps": round(written / (us * 1e-6) / 1e9, 1),

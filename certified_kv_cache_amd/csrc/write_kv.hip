@@ -216,7 +216,10 @@ __device__ __forceinline__ RowQ quant_row(const Raw8<T>& krow, const Raw8<T>& vr
     amv = row16_max_nonneg(amv);
     const int role = lane16 >> 2;              // 0: amk / 127, 1: 127 / amk, 2, 3: the same of amv
     const float am = role < 2 ? amk : amv;
-    const float qt = (role & 1) ? div_rn(127.0f, am) : div_rn(am, 127.0f);
+    // (operands selected first: one division sequence for the wave, not two
+    // divergent ones)
+    const float num = (role & 1) ? 127.0f : am, den = (role & 1) ? am : 127.0f;
+    const float qt = div_rn(num, den);
     // (an all-zero row keeps s = 1/s = 0)
     sk = amk > 0.0f ? row16_bcast<0>(qt) : 0.0f;
     ik = amk > 0.0f ? row16_bcast<4>(qt) : 0.0f;
