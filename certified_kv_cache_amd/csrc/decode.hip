@@ -1526,8 +1526,10 @@ extern "C" int wc_decode_attn_meter(const wc_cache* cache, int layer, const void
     return WC_EINVAL;
   }
   const wc_cache& c = *cache;
-  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1) {
-    set_error("wc_decode_attn_meter: need head_dim 128, 8 bands, 16-token pages");
+  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1 || c.num_pages < 1) {
+    // (a wave's prefetch past its last page, or of a wave with no page,
+    // requests physical page 0, so the layer needs one)
+    set_error("wc_decode_attn_meter: need head_dim 128, 8 bands, 16-token pages, >= 1 physical page");
     return WC_EUNSUPPORTED;
   }
   if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3 && c.scheme != WC_RTN_INT8 &&
@@ -1651,8 +1653,10 @@ extern "C" int wc_decode_load_floor(const wc_cache* cache, int layer, int B, int
     return WC_EINVAL;
   }
   const wc_cache& c = *cache;
-  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1) {
-    set_error("wc_decode_load_floor: need head_dim 128, 8 bands, 16-token pages");
+  if (c.head_dim != 128 || c.num_bands != 8 || c.page_size != 16 || c.num_kv_heads < 1 || c.num_pages < 1) {
+    // (a wave's prefetch past its last page, or of a wave with no page,
+    // requests physical page 0, so the layer needs one)
+    set_error("wc_decode_load_floor: need head_dim 128, 8 bands, 16-token pages, >= 1 physical page");
     return WC_EUNSUPPORTED;
   }
   if (c.scheme != WC_DITHER_INT8 && c.scheme != WC_FP8_E4M3 && c.scheme != WC_RTN_INT8 &&

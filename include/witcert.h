@@ -270,7 +270,10 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *
  *  q          device [B][Hq][128], q_dtype WC_F32 | WC_BF16; Hq multiple of Hkv,
  *             Hq/Hkv <= 16.
- *  page_table device int32 [B][max_pages] physical page of each logical block.
+ *  page_table device int32 [B][max_pages] physical page of each logical block
+ *             (< num_pages).  The cache needs num_pages >= 1 (WC_EUNSUPPORTED
+ *             otherwise): a wave's prefetch past its last block requests
+ *             physical page 0.
  *  ctx_len    device int32 [B]: tokens cached per sequence (<= max_pages*16).
  *  seed       device uint64 [B]: dither seed of each sequence.
  *  Repaired blocks (exact_slot >= 0) take their keys from the bf16 pool,
@@ -327,7 +330,8 @@ size_t wc_decode_workspace_bytes(int B, int Hq, int n_split);
  *  sink             device uint32 [1]: written only when a lane's fold of
  *                   the loaded words hits a fixed pattern; its contents mean
  *                   nothing.
- * Returns WC_EUNSUPPORTED when a layer's code array is 4 GB or more.
+ * Returns WC_EUNSUPPORTED when a layer's code array is 4 GB or more, or the
+ * cache has no physical page.
  */
 int wc_decode_load_floor(const wc_cache* cache, int layer, int B, int Hq, const int32_t* page_table,
                          int max_pages, const int32_t* ctx_len, int n_split, unsigned meter_mask,

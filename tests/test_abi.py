@@ -98,6 +98,7 @@ def test_decode_rejects_bad_arguments():
     assert call(seed=None) == L.WC_EINVAL
     assert call(cache=ctypes.byref(_cache(L, scheme=1)), mask=3) == L.WC_EINVAL   # Tier B needs INT8
     assert call(cache=ctypes.byref(_cache(L, scheme=2))) == L.WC_EUNSUPPORTED
+    assert call(cache=ctypes.byref(_cache(L, num_pages=0))) == L.WC_EUNSUPPORTED   # no physical page
     assert call(B=0) == L.WC_OK
 
 
@@ -291,6 +292,7 @@ def test_load_floor_rejects_bad_arguments():
     assert f(ok, 0, 1, 8, p, 4, p, 1, 3, 1, None, None) == L.WC_EINVAL                # sink
     assert f(ctypes.byref(_cache(L, head_dim=64)), 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
     assert f(ctypes.byref(_cache(L, scheme=2)), 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
+    assert f(ctypes.byref(_cache(L, num_pages=0)), 0, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EUNSUPPORTED
     assert f(ok, 2, 1, 8, p, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL                   # layer range
     assert f(ok, 0, 1, 7, p, 4, p, 1, 3, 1, p, None) == L.WC_EINVAL                   # Hq % Hkv
     assert f(ok, 0, 1, 8, p, 4, p, 0, 3, 1, p, None) == L.WC_EINVAL                   # n_split
