@@ -821,7 +821,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--ctx", type=int, default=32768)
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU baseline and the amd-smi power reading (the profiler runs)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--workload", default="decode",
@@ -951,6 +952,12 @@ def main():
         "decode_bytes": bytes_on, "step_bytes": step_bytes(B, S),
         "pages_paged_in": int(outs["paged"].item()) // 4096,
     }
+    if not args.no_cpu:
+        # board power and shader clock while the step's decode, then its load
+        # floor, run back to back (amd-smi read once in the middle of about
+        # four seconds of each): the INT8 decode runs at the board's power limit
+        out["power_clock"] = {"decode_block_risks": power_clock(lambda: decode(mask=3, with_risk=True)),
+                              "load_floor": power_clock(lambda: floor(mask=3, match=True))}
     out["fp8_variant"] = fp8_variant(w, B, S, iters)
     out["outlier_variant"] = [outlier_variant(w, B, S, iters, m) for m in (8, 16)]
     out["rtn_variant"] = scheme_variant(w, B, S, iters, "rtn")
