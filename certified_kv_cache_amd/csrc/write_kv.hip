@@ -551,12 +551,25 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
   const T* kb = kin + (int64_t)l * a.layer_stride;
   const T* vb = vin + (int64_t)l * a.layer_stride;
 
-  // keys: stage the 32 x 128 tile (8 channels per 16-byte load), per-channel
-  // min/max over the 32 tokens
-  for (int e = t; e < 32 * 16; e += 256) {
-    const int tok = e >> 4, c8 = (e & 15) * 8;
+  // every load of the workgroup first: this thread's 16 value channels (token
+  // t / 8, channels 16 (t % 8) ..) and its two pieces of the 32 x 128 key tile
+  // (8 channels per 16-byte load), so that the value rows' latency passes
+  // while the keys are processed
+  const int vtok = t >> 3, vpart = t & 7;
+  const T* vsrc = vb + ((i0 + vtok) * a.hkv + g) * 128 + 16 * vpart;
+  const Raw8<T> rv0 = load_raw8<T>(vsrc), rv1 = load_raw8<T>(vsrc + 8);
+  Raw8<T> rk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = t + 256 * u, tok = e >> 4, c8 = (e & 15) * 8;
+    rk[u] = load_raw8<T>(kb + ((i0 + tok) * a.hkv + g) * 128 + c8);
+  }
+  // keys: stage the tile, per-channel min/max over the 32 tokens
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = t + 256 * u, tok = e >> 4, c8 = (e & 15) * 8;
     float x8[8];
-    load8<T>(kb + ((i0 + tok) * a.hkv + g) * 128 + c8, x8);
+    unpack8(rk[u], x8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) xs[tok][c8 + j] = x8[j];
   }
@@ -609,11 +622,10 @@ __global__ void __launch_bounds__(256) write_kivi2_kernel(wc_cache c, const T* _
   }
   // values: groups of 32 channels of one token; thread = (token, 16-channel half-group)
   {
-    const int tok = t >> 3, part = t & 7;
+    const int tok = vtok, part = vpart;
     float x[16];
-    const T* src = vb + ((i0 + tok) * a.hkv + g) * 128 + 16 * part;
-    load8<T>(src, *reinterpret_cast<float(*)[8]>(&x[0]));
-    load8<T>(src + 8, *reinterpret_cast<float(*)[8]>(&x[8]));
+    unpack8(rv0, *reinterpret_cast<float(*)[8]>(&x[0]));
+    unpack8(rv1, *reinterpret_cast<float(*)[8]>(&x[8]));
     float vmn = x[0], vmx = x[0];
 #pragma unroll
     for (int k = 1; k < 16; ++k) {
