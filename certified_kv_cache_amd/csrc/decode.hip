@@ -178,6 +178,10 @@ __device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
 __device__ __forceinline__ f4 mfma_bf(uint4 a, uint4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
+// 16x16x16 bf16 (four bf16 per lane and operand)
+__device__ __forceinline__ f4 mfma_bf16k(uint2 a, uint2 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+}
 // Scheme traits: INT8 codes with row scales (dithered or RTN); the 16-bit store.
 template <int SCHEME>
 constexpr bool int8_codes() {
@@ -594,8 +598,16 @@ decode_kernel(wc_cache c, DecodeArgs a) {
   for (int i = 0; i < 32; ++i) bsum[i >> 3] = fmaf(qf[i], qf[i], bsum[i >> 3]);   // Tier A: the full query
   // Outlier bypass: the key chains see the query with the bypassed channels
   // zeroed; entry k m/4 + j of the side store (channel O[k m/4 + j]) meets
-  // head n's query there in MFMA j: bO[j] = q[O[k m/4 + j]] sm log2 e.
+  // head n's query there.  m = 16 with a bf16 query (BFO): bOq holds those
+  // four query entries as bf16, K slots 4k..4k+3 of one 16x16x16 bf16 MFMA,
+  // so every product is exact and the scale sm log2 e is applied once to the
+  // sum.  Otherwise fp32 MFMA j takes bO[j] = q[O[k m/4 + j]] sm log2 e (for
+  // m = 8 the bf16 form would need a zero register per page buffer, past the
+  // register limit).
+  constexpr bool BFO = NO4 == 4 && !QF32;
   float bO[4] = {0.f, 0.f, 0.f, 0.f};
+  uint2 bOq = make_uint2(0u, 0u);
+  const float osc = a.sm_scale * kLog2e;
   float qz2 = 0.0f;                            // sum of q^2 off the bypassed channels (Tier B)
   if (NO4 > 0) {
     const int32_t* oc = c.outlier_ch + ((int64_t)a.layer * c.num_kv_heads + g) * (4 * NO4);
@@ -617,9 +629,17 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < NO4; ++j) {
         const int ch = oc[kq * NO4 + j] & 127;
-        const float qv = QF32 ? reinterpret_cast<const float*>(a.q)[qrow + ch]
-                              : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qrow + ch]);
-        bO[j] = qv * (a.sm_scale * kLog2e);
+        if (BFO) {
+          const uint32_t qb = reinterpret_cast<const uint16_t*>(a.q)[qrow + ch];
+          if (j == 0) bOq.x |= qb;
+          if (j == 1) bOq.x |= qb << 16;
+          if (j == 2) bOq.y |= qb;
+          if (j == 3) bOq.y |= qb << 16;
+        } else {
+          const float qv = QF32 ? reinterpret_cast<const float*>(a.q)[qrow + ch]
+                                : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qrow + ch]);
+          bO[j] = qv * osc;
+        }
       }
     }
   }
@@ -762,10 +782,12 @@ decode_kernel(wc_cache c, DecodeArgs a) {
     // repaired block)
     f4 Da = zero4;
     if (meterA) Da = mfma_f32(cur.w.y, bA1, mfma_f32(cur.w.x, bA0, zero4));
-    // exact logits on the bypassed channels (log2 units), also for repaired
+    // exact logits on the bypassed channels (log2 units; BFO: the sum of the
+    // exact products, scaled where the logit is formed), also for repaired
     // blocks: their pool keys meet the zeroed query
     f4 Do = zero4;
-    if (NO4 > 0) {
+    if (BFO) Do = mfma_bf16k(cur.xo, bOq, Do);
+    if (NO4 > 0 && !BFO) {
       Do = mfma_f32(__uint_as_float(cur.xo.x << 16), bO[0], Do);
       Do = mfma_f32(__uint_as_float(cur.xo.x & 0xFFFF0000u), bO[1], Do);
       if (NO4 == 4) {
@@ -891,7 +913,7 @@ decode_kernel(wc_cache c, DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
       l2[r] = qs2c * st[r] * raw[r];
-      if (NO4 > 0) l2[r] += lo2[r];
+      if (NO4 > 0) l2[r] = BFO ? fmaf(lo2[r], osc, l2[r]) : l2[r] + lo2[r];
       cB[r] = kapB * st[r];
     }
     if (!full) {                               // tokens past the end: no weight, no bound, finite scales
