@@ -263,9 +263,14 @@ def make_step(w, B, S):
         L.wc_decode_attn_meter(w["cache"], 0, w["q"], w["tab"], w["ctx"], w["seed"], part, sm, mask, DELTA[0],
                                *DELTA[1:], NSPLIT, block_logrisk=risk if with_risk else None)
 
-    def step():
+    def step(ev=None):
+        # ev: a pair of HIP events recorded around the decode on its stream
         L.wc_write_kv(w["cache"], n["k"], n["v"], n["slot"], n["pos"], n["seed"])
+        if ev is not None:
+            ev[0].record()
         decode()
+        if ev is not None:
+            ev[1].record()
         L.wc_lse_merge(part, B, HQ, NSPLIT, o, lse, ra, rb)
         L.wc_gate_pagein(w["cache"], 0, risk, lse, w["tab"], w["ctx"], TAU, w["host"], pool_used, paged, gws,
                          meter=rb)
@@ -888,12 +893,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # each timed step's decode between a pair of HIP events on its stream (the
+    # roofline's launch duration); recording them adds no synchronization
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step()
+        step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
+    in_step = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    t_in_step = float(np.mean(in_step))
     # the step's decode (meter on, block risks), the same kernel without block
     # risks, and with the meter off, each timed as 10 loops of back-to-back
     # launches taken in turn (risk, on, off, risk, ...) so that a drift of the
@@ -915,7 +925,8 @@ def main():
     fl = time_modes(floor, iters, {"free": dict(mask=3, match=False), "off": dict(mask=0, match=True)}, warm=20)
     dec_step_us = t_risk
     bytes_on = decode_bytes(B, S, True)
-    ach = bytes_on / (dec_step_us * 1e-6) / 1e9
+    ach = bytes_on / (dec_step_us * 1e-6) / 1e9             # back-to-back loops
+    ach_step = bytes_on / (t_in_step * 1e-6) / 1e9          # inside the timed steps
     traffic = None
     if os.path.exists(COUNTERS):
         cnt = json.load(open(COUNTERS))
@@ -930,8 +941,12 @@ def main():
         "config": {"workload": f"decode B={B} S={S} Hq={HQ} Hkv={HKV} d={D} dithered-int8 Tier A+B, "
                                f"{NSPLIT} KV splits, 16-token pages (random permutation), append+decode+merge+gate",
                    "batch": B, "ctx": S, "n_split": NSPLIT, "tau": TAU},
-        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {"bound": "hbm", "achieved": round(ach_step, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach_step / PEAK_GBS, 4), "traffic": traffic},
+        "decode_us_in_steps": round(t_in_step, 2),
+        "decode_in_steps": f"the decode of each of the {args.steps} timed steps between HIP events on its stream, "
+                           f"mean (the roofline's launch duration); decode_us and pct_peak time the same kernel "
+                           f"back to back, where the board stays at its power limit throughout",
         "decode_us": round(dec_step_us, 2), "decode_us_p10": round(loops[1], 2), "decode_us_p90": round(loops[8], 2),
         "decode_loops": f"10 rounds of three loops of {iters} back-to-back launches (block risks, meter on, meter "
                         f"off, in turn); median, and p10, p90 of the loop means with block risks",
