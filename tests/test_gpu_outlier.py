@@ -105,7 +105,7 @@ def _check(sc, out, repaired=None):
                 assert np.all(got >= r["tv_true"] * (1 - 1e-6)), (key, b, g)
 
 
-@pytest.mark.parametrize("m,qdtype", [(8, "bf16"), (16, "bf16"), (8, "f32")])
+@pytest.mark.parametrize("m,qdtype", [(8, "bf16"), (16, "bf16"), (8, "f32"), (16, "f32")])
 def test_bypass_decode_parity(m, qdtype):
     L = H.need_gpu()
     _flush(f"bypass decode m={m} q={qdtype}")
@@ -132,13 +132,14 @@ def test_bypass_decode_parity(m, qdtype):
     assert np.all(out["R_B"].ravel()[live] < 0.5 * pout["R_B"].ravel()[live])
 
 
-def test_bypass_decode_large_group():
+@pytest.mark.parametrize("m", [8, 16])
+def test_bypass_decode_large_group(m):
     # 12 query heads per KV head: the uncompacted softmax path
     L = H.need_gpu()
-    _flush("bypass decode G=12")
+    _flush(f"bypass decode G=12 m={m}")
     lens = [300, 77]
     k, v, q = _layer(74, lens, Hq=24, Hkv=2, outliers=1)
-    sc = Scenario(L.WC_DITHER_INT8, k, v, q, lens, "bf16", Hkv=2, num_outliers=8)
+    sc = Scenario(L.WC_DITHER_INT8, k, v, q, lens, "bf16", Hkv=2, num_outliers=m)
     _check(sc, sc.decode(n_split=3, mask=3))
 
 
