@@ -300,7 +300,8 @@ int wc_outlier_select(const void* x, int in_dtype, int n_layers, int64_t n_tok, 
  *             requested, else A); -inf for blocks without risk.  With
  *             WC_BLOCK_CMAX in meter_mask it receives instead max_{t in block}
  *             c_t of the gate's tier (0 for repaired blocks), the input of
- *             wc_gate_pagein_tanh.
+ *             wc_gate_pagein_tanh.  Entries past a sequence's ceil(S/16)
+ *             pages are not written.
  */
 int wc_decode_attn_meter(const wc_cache* cache, int layer, const void* q, int q_dtype, int B, int Hq,
                          const int32_t* page_table, int max_pages, const int32_t* ctx_len,

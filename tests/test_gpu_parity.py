@@ -250,9 +250,11 @@ def test_block_risk_matches_oracle(scheme):
             assert np.all(np.abs(rho - ref) <= 1e-4 * ref + 1e-30), (b, g)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (9, 1), (8, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (9, 1), (8, 1), (4, 4), (8, 4), (16, 4), (15, 3), (12, 1)])
 def test_decode_group_sizes(Hq, Hkv):
-    # groups of more than 8 query heads take the uncompacted softmax path
+    # groups of more than 8 query heads take the uncompacted softmax path;
+    # the block outputs leave in runs of up to 4 heads x 16 pages, so groups
+    # of 1 to 16 heads take one to four rounds
     L = H.need_gpu()
     _flush(f"decode group {Hq}/{Hkv}")
     lens = [300, 77]
@@ -260,8 +262,20 @@ def test_decode_group_sizes(Hq, Hkv):
     d = inputs.layer(seed=12, S=n, Hq=Hq, Hkv=Hkv, outliers=1)
     q = inputs.layer(seed=13, S=1, Hq=Hq, Hkv=Hkv, batch=2)["q"]
     sc = Scenario(L.WC_DITHER_INT8, d["k"], d["v"], q, lens, "bf16", Hkv=Hkv)
-    out = sc.decode(n_split=3, mask=3)
+    out = sc.decode(n_split=3, mask=3, risk=True)
     _check_decode(sc, out)
+    cm = sc.decode(n_split=3, mask=3, cmax=True)["cmax"]
+    for b, S in enumerate(lens):
+        P = -(-S // 16)
+        for g in range(Hkv):
+            _, r = sc.oracle(b, g)
+            hs = slice(g * sc.G, (g + 1) * sc.G)
+            rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
+            assert np.all(np.abs(rho - r["block_risk"]) <= 1e-4 * r["block_risk"] + 1e-30), (b, g)
+            got = cm[b, hs, :P].astype(np.float64)
+            assert np.all(np.abs(got - r["block_cmax"]) <= 1e-4 * r["block_cmax"] + 1e-30), (b, g)
+            # entries past the sequence's pages are left as they were
+            assert np.all(np.isnan(out["logrisk"][b, hs, P:])) and np.all(np.isnan(cm[b, hs, P:])), (b, g)
 
 
 @pytest.mark.parametrize("scheme", ["int8", "rtn"])
