@@ -250,6 +250,35 @@ def test_block_risk_matches_oracle(scheme):
             assert np.all(np.abs(rho - ref) <= 1e-4 * ref + 1e-30), (b, g)
 
 
+@pytest.mark.parametrize("scheme", ["int8", "fp8", "rtn"])
+def test_decode_fp32_query_ragged(scheme):
+    """fp32 keys, values and queries (the query's hi/lo operand split on a
+    ragged grouped batch, 2 waves per SIMD) with block risks, one to many
+    splits."""
+    L = H.need_gpu()
+    _flush(f"decode fp32 query {scheme}")
+    lens = [1, 17, 700, 0, 129]
+    n = sum(lens)
+    rng = np.random.default_rng(31)
+    k = (rng.standard_normal((n, 4, 128)) * rng.uniform(0.05, 5.0, (n, 4, 1))).astype(np.float32)
+    v = (rng.standard_normal((n, 4, 128)) * rng.uniform(0.1, 3.0, (n, 4, 1))).astype(np.float32)
+    q = rng.standard_normal((len(lens), 28, 128)).astype(np.float32)
+    sch = {"int8": L.WC_DITHER_INT8, "fp8": L.WC_FP8_E4M3, "rtn": L.WC_RTN_INT8}[scheme]
+    sc = Scenario(sch, k, v, q, lens, "f32", Hkv=4)
+    for n_split in (1, 4, 9):
+        out = sc.decode(n_split=n_split, mask=3 if scheme == "int8" else 1, risk=True)
+        _check_decode(sc, out)
+        for b, S in enumerate(lens):
+            P = -(-S // 16)
+            for g in range(4):
+                if S == 0:
+                    continue
+                _, r = sc.oracle(b, g)
+                hs = slice(g * 7, (g + 1) * 7)
+                rho = np.exp(out["logrisk"][b, hs, :P].astype(np.float64) - out["lse"][b, hs, None])
+                assert np.all(np.abs(rho - r["block_risk"]) <= 1e-4 * r["block_risk"] + 1e-30), (n_split, b, g)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(32, 2), (9, 1), (8, 1), (4, 4), (8, 4), (16, 4), (15, 3), (12, 1)])
 def test_decode_group_sizes(Hq, Hkv):
     # groups of more than 8 query heads take the uncompacted softmax path;
