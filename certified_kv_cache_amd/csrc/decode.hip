@@ -1489,11 +1489,12 @@ extern "C" size_t wc_decode_workspace_bytes(int B, int Hq, int n_split) {
 }
 
 // Host dispatch from the run-time shape to the template instance.  The meter
-// configurations of the common shape (bf16 query, group <= 8, 32-bit layer
-// offsets, no bypass, no value certificate) have instances of their own.
+// configurations of the common shapes (bf16 query, group <= 8, 32-bit layer
+// offsets, no value certificate; with or without the outlier bypass) have
+// instances of their own.
 template <int SCH, bool QF, bool CM, bool SO, int NO>
 static void launch_mv(bool mv, int mode, dim3 grid, hipStream_t st, const wc_cache& c, const DecodeArgs& a) {
-  if constexpr (!QF && CM && SO && NO == 0) {
+  if constexpr (!QF && CM && SO) {
     if (!mv && mode == kModeOff) {
       hipLaunchKernelGGL((decode_kernel<SCH, QF, CM, SO, NO, false, kModeOff>), grid, dim3(kThreads), 0, st, c, a);
       return;
